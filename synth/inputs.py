@@ -1,0 +1,157 @@
+"""Seeded synthetic workloads for the fused weight-gradient + optimizer step.
+
+The pages evaluate on Llama-3.1-8B and Qwen3 layers (FORGE explainer, section 4
+"Experimental results"); no dataset or trained weight is used here. Every tensor
+is drawn from numpy's PCG64 generator seeded by
+``SeedSequence([0xF06E, config, layer, step, tensor_id])`` with
+tensor_id 0 = W init, 1 = X, 2 = dY, 3 = X outlier rows, 4 = dY outlier rows.
+"N(0, s)" means standard deviation s. bfloat16 tensors are the round-to-nearest-
+even bfloat16 of the float32 sample, done on the bit patterns.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+ROOT_TAG = 0xF06E
+TID_W, TID_X, TID_DY, TID_X_OUT, TID_DY_OUT = 0, 1, 2, 3, 4
+
+
+def layer_seed(config: int, layer: int, step: int, tensor_id: int) -> np.random.Generator:
+    """PCG64 generator for one tensor of one layer at one step."""
+    ss = np.random.SeedSequence([ROOT_TAG, int(config), int(layer), int(step), int(tensor_id)])
+    return np.random.Generator(np.random.PCG64(ss))
+
+
+def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round float32 samples to bfloat16 (nearest, ties to even); returns uint16 bits.
+
+    Only finite samples occur in these workloads; NaN inputs are rejected.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("synthetic inputs must be finite")
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def draw_normal(gen: np.random.Generator, shape: Tuple[int, ...], std: float) -> np.ndarray:
+    """float32 N(0, std) samples."""
+    x = gen.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return x
+
+
+def outlier_rows(config: int, layer: int, step: int, tensor_id: int, T: int, frac: float) -> np.ndarray:
+    """Sorted, distinct token rows chosen as outliers: round(frac * T) of them."""
+    n = int(round(frac * T))
+    gen = layer_seed(config, layer, step, tensor_id)
+    return np.sort(gen.choice(T, size=n, replace=False))
+
+
+def sample_rows(config: int, layer: int, out: int, n: int) -> np.ndarray:
+    """Seeded subset of output rows for row-sampled parity checks (sorted, distinct)."""
+    n = min(n, out)
+    gen = layer_seed(config, layer, 0, 99)
+    return np.sort(gen.choice(out, size=n, replace=False))
+
+
+@dataclass(frozen=True)
+class LayerSpec:
+    """One linear layer: W is [out, in]; X is [T, in]; dY is [T, out]."""
+    name: str
+    out: int
+    inn: int
+    T: int
+    io: str = "bf16"              # "bf16" or "f32" for X, dY and W
+    w_std: float = 0.02
+    x_std: float = 1.0
+    dy_std: float = 1e-3
+    outlier_frac: float = 0.0     # fraction of token rows scaled by outlier_scale
+    outlier_scale: float = 100.0
+
+    @property
+    def P(self) -> int:
+        return self.out * self.inn
+
+
+def _to_io(x32: np.ndarray, io: str) -> np.ndarray:
+    return bf16_bits_from_f32(x32) if io == "bf16" else np.ascontiguousarray(x32, dtype=np.float32)
+
+
+def draw_layer_init(config: int, layer: int, spec: LayerSpec) -> np.ndarray:
+    """Initial W (uint16 bf16 bits or float32)."""
+    w = draw_normal(layer_seed(config, layer, 0, TID_W), (spec.out, spec.inn), spec.w_std)
+    return _to_io(w, spec.io)
+
+
+def draw_layer_batch(config: int, layer: int, step: int, spec: LayerSpec) -> Tuple[np.ndarray, np.ndarray]:
+    """Fresh (X, dY) for one step (step is 1-based); bf16 bits or float32."""
+    x = draw_normal(layer_seed(config, layer, step, TID_X), (spec.T, spec.inn), spec.x_std)
+    dy = draw_normal(layer_seed(config, layer, step, TID_DY), (spec.T, spec.out), spec.dy_std)
+    if spec.outlier_frac > 0.0:
+        rx = outlier_rows(config, layer, step, TID_X_OUT, spec.T, spec.outlier_frac)
+        rd = outlier_rows(config, layer, step, TID_DY_OUT, spec.T, spec.outlier_frac)
+        x[rx, :] *= np.float32(spec.outlier_scale)
+        dy[rd, :] *= np.float32(spec.outlier_scale)
+    return _to_io(x, spec.io), _to_io(dy, spec.io)
+
+
+def _llama8b_layers(T: int) -> List[LayerSpec]:
+    h, kv, ff = 4096, 1024, 14336
+    return [
+        LayerSpec("q_proj", h, h, T), LayerSpec("k_proj", kv, h, T), LayerSpec("v_proj", kv, h, T),
+        LayerSpec("o_proj", h, h, T), LayerSpec("gate_proj", ff, h, T), LayerSpec("up_proj", ff, h, T),
+        LayerSpec("down_proj", h, ff, T),
+    ]
+
+
+@dataclass
+class Workload:
+    """A named workload: its layers, optimizer(s), step count and state format."""
+    config: int
+    name: str
+    layers: List[LayerSpec]
+    steps: int
+    optimizers: Tuple[str, ...] = ("adamw",)
+    state: str = "f32"                 # "f32" or "q8" (int8 m, uint8 sqrt-v, block 64)
+    stochastic_round: bool = True
+    extra: Dict[str, object] = field(default_factory=dict)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    # fp32 everything, 256x256, 512 tokens, AdamW, 3 steps, no stochastic rounding
+    "fp32_256": Workload(0, "fp32_256", [LayerSpec("linear", 256, 256, 512, io="f32", dy_std=1e-2)],
+                         steps=3, stochastic_round=False),
+    # q_proj-shaped: 4096x4096 bf16, 8192 tokens, AdamW + SR, 10 steps
+    "q_proj_8192": Workload(1, "q_proj_8192", [LayerSpec("q_proj", 4096, 4096, 8192)], steps=10),
+    # the seven linears of a Llama-3.1-8B-shaped decoder layer, 8192 tokens
+    "llama8b_layer_8192": Workload(2, "llama8b_layer_8192", _llama8b_layers(8192), steps=1),
+    # INT8 block-64 states on down_proj, 16384 tokens, 1% outlier rows x100, 20 steps
+    "down_q8_16384": Workload(3, "down_q8_16384",
+                              [LayerSpec("down_proj", 4096, 14336, 16384, outlier_frac=0.01)],
+                              steps=20, state="q8"),
+    # eight optimizers on a Qwen3-14B-shaped MLP weight 17408x5120, 4096 tokens, 10 steps
+    "qwen14b_mlp_4096": Workload(4, "qwen14b_mlp_4096", [LayerSpec("mlp_up", 17408, 5120, 4096)], steps=10,
+                                 optimizers=("adamw", "nadam", "radam", "lion", "rmsprop", "adagrad",
+                                             "sgd", "sgd_momentum")),
+}
+
+
+def llama8b_stack(T: int = 8192, n_layers: int = 32) -> List[LayerSpec]:
+    """All 7*n_layers linear layers of an n_layers-deep Llama-8B-shaped stack."""
+    out: List[LayerSpec] = []
+    for _ in range(n_layers):
+        out.extend(_llama8b_layers(T))
+    return out
