@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused weight-gradient + optimizer step (FORGE) on one MI355X.
+
+A step is one pass of the hot path for each layer of the workload, on inputs
+already resident in device memory: the input gradient dX = dY W (old weights),
+then the fused dW = dY^T X + optimizer update of W and its moments. The default
+workload is the q_proj-shaped layer (W 4096x4096 bf16, fp32 AdamW moments,
+8192 tokens, stochastic rounding). `value` counts the algorithmic FLOPs of both
+GEMMs of every step (4 * T * out * in per layer) over the timed wall time.
+
+Besides the JSON line's contract fields it reports:
+  roofline      the fused kernel's achieved TFLOP/s (2*T*out*in per launch over its
+                mean launch time, HIP events on the launch stream) against the MI355X
+                dense peak of its input dtype;
+  cpu_baseline  the float64 oracle timed on the host on a bounded sample;
+  unfused       the two-phase baseline (dW stored as fp32, separate optimizer pass),
+                its time, the fused speedup and the transient memory each needs.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused wgrad+AdamW TFLOP/s & ms/layer (Llama-8B shapes), % MFMA peak, dW HBM bytes"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA peaks
+HBM_GBS = 8000.0
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("forge_internal.h", "forge_wgrad.hip"):
+        with open(os.path.join(ROOT, "optimizer_gemm_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="q_proj_8192",
+                   help="q_proj_8192 | llama8b_layer_8192 | down_q8_16384 | qwen14b_mlp_4096 | fp32_256 | stack")
+    p.add_argument("--opt", default="adamw")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-unfused", action="store_true")
+    return p.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
+              "(tensor-parallel shards run the same kernel on each GPU's share)", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import optimizer_gemm_amd as forge
+    from synth import WORKLOADS, draw_layer_batch, draw_layer_init, llama8b_stack
+
+    if args.workload == "stack":
+        layers = llama8b_stack(8192, 32)
+        wl_config, state, sr = 5, "f32", True
+    else:
+        wl = WORKLOADS[args.workload]
+        layers, wl_config, state, sr = wl.layers, wl.config, wl.state, wl.stochastic_round
+    opt = args.opt
+    dev = torch.device("cuda:0")
+    io = layers[0].io
+    tdt = torch.bfloat16 if io == "bf16" else torch.float32
+
+    def to_dev(a):
+        if io == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # one (X, dY, dX) buffer set per distinct shape; W and its moments per layer
+    shape_bufs = {}
+    per_layer = []
+    t0 = time.perf_counter()
+    for li, spec in enumerate(layers):
+        key = (spec.out, spec.inn, spec.T)
+        if key not in shape_bufs:
+            X, dY = draw_layer_batch(wl_config, li, 1, spec)
+            shape_bufs[key] = (to_dev(X), to_dev(dY), torch.empty((spec.T, spec.inn), dtype=tdt, device=dev))
+        W = to_dev(draw_layer_init(wl_config, li if args.workload != "stack" else li % 7, spec))
+        m, v, ms, vs = forge.new_states(W, opt, state)
+        per_layer.append((spec, W, m, v, ms, vs, ((0x5EED0000 + wl_config) ^ li)))
+    print(f"[bench] setup {time.perf_counter() - t0:.1f}s: {len(layers)} layer(s), workload {args.workload}, "
+          f"opt {opt}, states {state}", file=sys.stderr, flush=True)
+    hyper = forge.make_hyper(opt, stochastic_round=int(sr))
+
+    step_counter = [0]
+
+    def one_step(fused_events=None):
+        step_counter[0] += 1
+        t = step_counter[0]
+        for k, (spec, W, m, v, ms, vs, seed) in enumerate(per_layer):
+            X, dY, dX = shape_bufs[(spec.out, spec.inn, spec.T)]
+            forge.dgrad(dY, W, dX)
+            if fused_events is not None:
+                fused_events[k][0].record()
+            forge.wgrad_step(X, dY, W, m, v, opt, hyper, t, seed, ms, vs)
+            if fused_events is not None:
+                fused_events[k][1].record()
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    flops_gemm = [2.0 * s.T * s.out * s.inn for (s, *_rest) in per_layer]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in per_layer]
+          for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for k in range(args.steps):
+        one_step(ev[k])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    elapsed_ms = start.elapsed_time(end)
+    ms_per_step = elapsed_ms / args.steps
+    total_flops = 2.0 * sum(flops_gemm) * args.steps  # dgrad + wgrad per layer per step
+    value = total_flops / (elapsed_ms * 1e-3) / 1e12
+    fused_ms = [[ev[k][j][0].elapsed_time(ev[k][j][1]) for j in range(len(per_layer))] for k in range(args.steps)]
+    fused_ms_layer = np.mean(np.array(fused_ms), axis=0)           # mean per layer
+    fused_total = float(np.sum(fused_ms_layer))
+    fused_tflops = sum(flops_gemm) / (fused_total * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[io]
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step, fused {fused_total:.3f} ms/step "
+          f"({fused_tflops:.1f} TFLOP/s), wall {wall:.2f}s", file=sys.stderr, flush=True)
+
+    # --- traffic from committed rocprofv3 counters (only if taken on this kernel source) ---
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("opt", "adamw") == opt:
+            traffic = tr.get("bytes_per_launch")
+
+    # --- unfused baseline (separate timed region) ---
+    unfused = None
+    if not args.no_unfused and args.workload != "stack":
+        spec, W, m, v, ms, vs, seed = per_layer[0]
+        X, dY, dX = shape_bufs[(spec.out, spec.inn, spec.T)]
+        n_rep = max(3, min(args.steps, 20))
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        forge.wgrad_step(X, dY, W, m, v, opt, hyper, 10_000, seed, ms, vs)
+        torch.cuda.synchronize()
+        fused_transient = torch.cuda.max_memory_allocated() - base
+        torch.cuda.reset_peak_memory_stats()
+        dW = torch.empty((spec.out, spec.inn), dtype=torch.float32, device=dev)
+        forge.wgrad_unfused(X, dY, W, m, v, opt, hyper, 10_001, seed, ms, vs, dW_workspace=dW)
+        torch.cuda.synchronize()
+        unfused_transient = torch.cuda.max_memory_allocated() - base
+        e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+              torch.cuda.Event(enable_timing=True)) for _ in range(n_rep)]
+        f_e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_rep)]
+        for r in range(n_rep):
+            f_e[r][0].record()
+            forge.wgrad_step(X, dY, W, m, v, opt, hyper, 10_002 + r, seed, ms, vs)
+            f_e[r][1].record()
+            e[r][0].record()
+            forge.wgrad(X, dY, dW)
+            e[r][1].record()
+            forge.optimizer_step(dW, W, m, v, opt, hyper, 10_002 + r, seed, ms, vs)
+            e[r][2].record()
+        torch.cuda.synchronize()
+        gemm_ms = float(np.median([a.elapsed_time(b) for a, b, _ in e]))
+        opt_ms = float(np.median([b.elapsed_time(c) for _, b, c in e]))
+        fused_med = float(np.median([a.elapsed_time(b) for a, b in f_e]))
+        del dW
+        unfused = {"gemm_store_ms": round(gemm_ms, 4), "optimizer_ms": round(opt_ms, 4),
+                   "total_ms": round(gemm_ms + opt_ms, 4), "fused_ms": round(fused_med, 4),
+                   "speedup_vs_unfused": round((gemm_ms + opt_ms) / fused_med, 3),
+                   "dW_hbm_bytes_algorithmic": {"fused": 0, "unfused": 8 * spec.out * spec.inn},
+                   "peak_transient_bytes": {"fused": int(fused_transient), "unfused": int(unfused_transient)},
+                   "layer": f"{spec.name} {spec.out}x{spec.inn} T={spec.T}"}
+
+    # --- CPU baseline: the float64 oracle on a bounded sample (first layer) ---
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import gemm, optim, step as ostep
+        from synth import f32_from_bf16_bits
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+        except Exception:
+            cores = os.cpu_count() or 1
+        spec = layers[0]
+        X, dY = draw_layer_batch(wl_config, 0, 1, spec)
+        W0 = draw_layer_init(wl_config, 0, spec)
+        n_rows = spec.out if spec.P <= 32 * 1024 * 1024 else 1024
+        rows = np.arange(n_rows)
+        hp = optim.hyper(opt)
+        slots = optim.SLOTS[opt]
+        z = np.zeros((n_rows, spec.inn), np.float32)
+        Xw = f32_from_bf16_bits(X) if io == "bf16" else X
+        dYw = f32_from_bf16_bits(dY) if io == "bf16" else dY
+        Ww = f32_from_bf16_bits(W0[rows]) if io == "bf16" else W0[rows]
+        reps, times = 2, []
+        for _ in range(reps):
+            c0 = time.perf_counter()
+            gemm.dgrad(dYw[:, rows], Ww)  # dX contribution of the sampled rows of W
+            ostep.wgrad_step(opt, X, dY, W0[rows], z if "m" in slots else None, z if "v" in slots else None,
+                             hp, 1, 1, io=io, sr=sr, rows=rows)
+            times.append(time.perf_counter() - c0)
+        tcpu = float(np.median(times))
+        flops = 4.0 * spec.T * n_rows * spec.inn
+        cpu = {"value": round(flops / tcpu / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+               "sample": f"{spec.name} {n_rows} of {spec.out} output rows x {spec.inn}, T={spec.T}: float64 "
+                         f"dgrad + fused-step oracle, median of {reps} ({tcpu:.2f} s each)"}
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": io,
+        "data": "synthetic (seeded Gaussian inputs of the layer shapes; random-init weights)",
+        "config": {"workload": args.workload, "layers": len(layers),
+                   "shapes": sorted({f"{s.out}x{s.inn}" for s in layers}), "tokens": layers[0].T,
+                   "optimizer": opt, "states": state, "stochastic_round": bool(sr),
+                   "step": "dgrad(old W) then fused wgrad+optimizer, per layer"},
+        "fused_ms_per_layer": [round(float(x), 4) for x in fused_ms_layer][:8],
+        "fused_tflops": round(fused_tflops, 2),
+        "pct_mfma_peak": round(100.0 * fused_tflops / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(fused_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(fused_tflops / peak, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+        "unfused": unfused,
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(rec))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

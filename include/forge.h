@@ -1,0 +1,182 @@
+/*
+ * forge.h - C ABI of the MI355X (gfx950) fused weight-gradient + optimizer step.
+ *
+ * Method: FORGE, "Fused On-Register Gradient Elimination for Memory-Efficient
+ * LLM Training" (explainer pages, technical summary). For a linear layer
+ * Y = X W^T the weight gradient dW = dY^T X (summed over the T tokens) is
+ * computed one weight tile at a time in FP32 accumulators; the element-wise
+ * optimizer update is applied to the tile while it is still in registers and
+ * only the updated weight tile and its moment tiles are written back, so the
+ * gradient never reaches device memory (§2 Method, "Core mechanism", steps
+ * 1-4). The input gradient dX = dY W must be computed from the old weights,
+ * i.e. before the update (§5, limitations paragraph).
+ *
+ * Conventions for every entry point
+ *   - All tensors are row-major and live in device memory owned by the caller;
+ *     the library never allocates, frees or keeps a pointer after returning.
+ *   - W and the moments are [out, in]; X is [T, in]; dY is [T, out]; dX is [T, in].
+ *   - `ld` is the row pitch in elements (ld >= cols). Data pointers must be
+ *     16-byte aligned; cols and ld must be multiples of 8 (bf16) or 4 (fp32).
+ *     A tensor with no elements may have a NULL data pointer.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     null stream). No entry point synchronises the host.
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     error nothing is launched and a negative status is returned. No entry
+ *     point keeps global mutable state; calls are thread-safe.
+ *   - Results are deterministic: fixed reduction order, no atomics.
+ */
+#ifndef FORGE_H
+#define FORGE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* forge_stream_t; /* hipStream_t */
+
+/* Element types. */
+typedef enum {
+  FORGE_F32 = 0,  /* IEEE float32 */
+  FORGE_BF16 = 1, /* bfloat16 */
+  FORGE_I8 = 2,   /* int8 codes of a signed moment (block-64 absmax, scale/127) */
+  FORGE_U8 = 3    /* uint8 codes of sqrt(second moment) (block-64 absmax, scale/255) */
+} forge_dtype;
+
+/* The eight element-wise optimizers the pages list (§3 Contributions, generality). */
+typedef enum {
+  FORGE_ADAMW = 0,
+  FORGE_SGD = 1,
+  FORGE_SGD_MOMENTUM = 2,
+  FORGE_LION = 3,
+  FORGE_RMSPROP = 4,
+  FORGE_ADAGRAD = 5,
+  FORGE_NADAM = 6,
+  FORGE_RADAM = 7
+} forge_opt;
+
+/* A 2-D row-major device tensor. `scale` is used only for FORGE_I8 / FORGE_U8
+ * moments: float32 block scales, [rows, cols/64] with row pitch cols/64, one per
+ * 64 consecutive elements of a row (§2 "Precision and fidelity": INT8 states
+ * with blocks of 64). */
+typedef struct {
+  void* data;
+  int32_t dtype; /* forge_dtype */
+  int32_t reserved;
+  int64_t rows;
+  int64_t cols;
+  int64_t ld;
+  float* scale;
+} forge_tensor;
+
+/* Optimizer hyper-parameters in double (torch.optim conventions; unused fields ignored).
+ *   AdamW, Lion: decoupled decay theta *= (1 - lr*weight_decay).
+ *   SGD, SGD-momentum, RMSprop, AdaGrad, NAdam, RAdam: coupled L2, g += weight_decay*theta.
+ *   Lion: beta1 interpolates the sign argument, beta2 tracks the state.
+ *   RMSprop: alpha is the smoothing constant. AdaGrad: lr_decay. NAdam: momentum_decay.
+ *   SGD-momentum: momentum, dampening, nesterov. */
+typedef struct {
+  double lr, beta1, beta2, eps, weight_decay;
+  double momentum, dampening, alpha, lr_decay, momentum_decay;
+  int32_t nesterov;
+  int32_t stochastic_round; /* bf16 W only: 1 = stochastic rounding (default), 0 = nearest-even */
+} forge_hyper;
+
+/* Per-step scalars the kernels use, computed on the host in double precision
+ * from (opt, hyper, step) and rounded once to float (bias corrections, NAdam
+ * momentum products, RAdam rectification). Exposed for inspection and tests. */
+typedef struct {
+  float lr;           /* lr (AdaGrad: lr / (1 + (t-1) lr_decay)) */
+  float decay;        /* 1 - lr*weight_decay (AdamW, Lion) */
+  float wd;           /* weight_decay for coupled L2 */
+  float b1, omb1;     /* beta1 and 1-beta1 (SGD-m: momentum-buffer coefficients) */
+  float b2, omb2;     /* beta2 and 1-beta2 (RMSprop: alpha, 1-alpha) */
+  float step_size;    /* AdamW: lr/bc1; RAdam: lr*r_t*sqrt(bc2)/bc1 or lr/bc1 */
+  float inv_sqrt_bc2; /* 1/sqrt(1-beta2^t) */
+  float eps;
+  float c_g, c_m;     /* NAdam gradient / momentum coefficients; SGD-m: momentum */
+  int32_t flag;       /* RAdam: 1 = rectified branch; SGD-m: nesterov */
+  int32_t opt;
+} forge_scalars;
+
+/* Status codes. */
+#define FORGE_OK 0
+#define FORGE_ERR_NULL (-1)        /* a required pointer is NULL */
+#define FORGE_ERR_SHAPE (-2)       /* dimensions inconsistent between tensors */
+#define FORGE_ERR_DTYPE (-3)       /* unsupported dtype combination */
+#define FORGE_ERR_ALIGN (-4)       /* pointer not 16-B aligned, or cols/ld not a multiple of 8 (bf16) / 4 (fp32) */
+#define FORGE_ERR_UNSUPPORTED (-5) /* size outside what the kernels handle (e.g. INT8 needs in % 64 == 0) */
+#define FORGE_ERR_HYPER (-6)       /* step < 1, unknown optimizer, non-finite or out-of-range hyper-parameter */
+#define FORGE_ERR_HIP (-7)         /* kernel launch failed (HIP error) */
+#define FORGE_ERR_ALIAS (-8)       /* output tensors overlap each other or an input */
+
+/*
+ * Fused weight-gradient + optimizer step (§2 Method, "Core mechanism"):
+ *   dW = dY^T X (FP32 accumulation over T tokens, tile by tile, never stored),
+ *   then the `opt` update of W, m, v in place, with step t = `step` (1-based).
+ * X [T, in] and dY [T, out] are read only; W [out, in] is updated in place.
+ * dtypes: X, dY, W all FORGE_F32, or all FORGE_BF16. m and v: FORGE_F32, or
+ * FORGE_I8 (m) and FORGE_U8 (v) with block scales (requires in % 64 == 0).
+ * Slots an optimizer does not use may be NULL and are never touched:
+ *   SGD: none; SGD-momentum, Lion: m; RMSprop, AdaGrad: v; others: m and v.
+ * bfloat16 W is written with stochastic rounding (hyper->stochastic_round)
+ * driven by a counter hash: r16 = top 16 bits of the SplitMix64 output number
+ * ((step << 32) | (o*in + i)) + 1 from state `seed`; bf16 = (bits(w32) + r16) >> 16
+ * (NaN -> quiet NaN). T == 0 is allowed (zero gradient). Requires out*in < 2^32.
+ * Must be enqueued after forge_linear_dgrad of the same layer (which reads the old W).
+ */
+int forge_linear_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge_tensor* W,
+                            forge_tensor* m, forge_tensor* v, int32_t opt, const forge_hyper* hyper,
+                            int64_t step, uint64_t seed, forge_stream_t stream);
+
+/*
+ * Input gradient dX = dY W (§5, limitations: read before the weight update).
+ * dY [T, out], W [out, in], dX [T, in]; all FORGE_F32, or all FORGE_BF16
+ * (bf16 output rounded to nearest-even from the FP32 accumulator).
+ */
+int forge_linear_dgrad(const forge_tensor* dY, const forge_tensor* W, forge_tensor* dX,
+                       forge_stream_t stream);
+
+/*
+ * Unfused baseline, first half: the two-phase schedule the pages describe as
+ * the standard one (§1, "the gradient floor"): the same GEMM, but dW [out, in]
+ * is written to device memory as float32 (row pitch ld_dw >= in, multiple of 4).
+ */
+int forge_linear_wgrad(const forge_tensor* X, const forge_tensor* dY, float* dW, int64_t ld_dw,
+                       forge_stream_t stream);
+
+/*
+ * Unfused baseline, second half: a separate element-wise optimizer pass that
+ * reads the stored float32 dW back and updates W, m, v exactly as the fused
+ * step does (same per-element arithmetic, same rounding and RNG).
+ */
+int forge_optimizer_step(const float* dW, int64_t ld_dw, forge_tensor* W, forge_tensor* m,
+                         forge_tensor* v, int32_t opt, const forge_hyper* hyper, int64_t step,
+                         uint64_t seed, forge_stream_t stream);
+
+/* Host-only helpers (no GPU work). */
+
+/* Fills *out with the per-step scalars of (opt, hyper, step). Returns a status. */
+int forge_step_scalars(int32_t opt, const forge_hyper* hyper, int64_t step, forge_scalars* out);
+
+/* Defaults of the optimizer sweep for `opt` (lr, betas, eps, decay ...). Returns a status. */
+int forge_default_hyper(int32_t opt, forge_hyper* out);
+
+/* The stochastic-rounding random bits of element `idx` at `step` (same hash as the kernels). */
+uint32_t forge_rand16(uint64_t seed, int64_t step, uint32_t idx);
+
+/* Stochastic rounding of float32 x to bfloat16 bits with random bits r16 (same rule as the kernels). */
+uint16_t forge_sr_bf16(float x, uint32_t r16);
+
+/* Human-readable text of a status code (static storage). */
+const char* forge_status_str(int status);
+
+/* Library ABI version (major*100 + minor). */
+int forge_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FORGE_H */

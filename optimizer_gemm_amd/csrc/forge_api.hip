@@ -1,0 +1,363 @@
+// C ABI of the forge library: host-side validation, per-step scalars and
+// dispatch to the gfx950 kernels. Nothing here allocates device memory or
+// synchronises the host; every error is detected before anything is enqueued.
+#include <math.h>
+#include <stdint.h>
+
+#include "forge_internal.h"
+
+using namespace forge;
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+int elem_size(int dt) { return dt == FORGE_F32 ? 4 : dt == FORGE_BF16 ? 2 : 1; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Byte range a row-major tensor may touch.
+struct Range {
+  uintptr_t lo, hi;
+};
+Range range_of(const forge_tensor* t) {
+  const uintptr_t lo = (uintptr_t)t->data;
+  const int64_t n = t->rows == 0 ? 0 : ((t->rows - 1) * t->ld + t->cols) * elem_size(t->dtype);
+  return Range{lo, lo + (uintptr_t)n};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+int check_shape(const forge_tensor* t) {
+  if (t->rows < 0 || t->cols < 0 || t->rows >= kMaxDim || t->cols >= kMaxDim) return FORGE_ERR_SHAPE;
+  if (t->ld < t->cols) return FORGE_ERR_SHAPE;
+  return FORGE_OK;
+}
+
+// Dense io tensor (X, dY, W, dX): fp32 or bf16, 16-byte vectors along rows.
+int check_io(const forge_tensor* t, int dtype) {
+  if (!t) return FORGE_ERR_NULL;
+  if (!t->data && t->rows != 0 && t->cols != 0) return FORGE_ERR_NULL;  // empty tensors may be NULL
+  if (t->dtype != dtype) return FORGE_ERR_DTYPE;
+  int r = check_shape(t);
+  if (r) return r;
+  const int ve = dtype == FORGE_BF16 ? 8 : 4;
+  if (!aligned16(t->data) || t->cols % ve || t->ld % ve) return FORGE_ERR_ALIGN;
+  return FORGE_OK;
+}
+
+bool finite(double x) { return isfinite(x) != 0; }
+
+int check_hyper(int opt, const forge_hyper* h, int64_t step) {
+  if (!h) return FORGE_ERR_NULL;
+  if (opt < FORGE_ADAMW || opt > FORGE_RADAM) return FORGE_ERR_HYPER;
+  if (step < 1 || step >= ((int64_t)1 << 31)) return FORGE_ERR_HYPER;
+  const double f[] = {h->lr, h->beta1, h->beta2, h->eps, h->weight_decay, h->momentum, h->dampening, h->alpha,
+                      h->lr_decay, h->momentum_decay};
+  for (double x : f)
+    if (!finite(x)) return FORGE_ERR_HYPER;
+  if (h->lr < 0.0 || h->eps < 0.0 || h->lr_decay < 0.0) return FORGE_ERR_HYPER;
+  switch (opt) {
+    case FORGE_ADAMW:
+    case FORGE_NADAM:
+    case FORGE_RADAM:
+    case FORGE_LION:
+      if (h->beta1 < 0.0 || h->beta1 >= 1.0 || h->beta2 < 0.0 || h->beta2 >= 1.0) return FORGE_ERR_HYPER;
+      break;
+    case FORGE_SGD_MOMENTUM:
+      if (h->momentum < 0.0 || h->momentum >= 1.0 || h->dampening < 0.0 || h->dampening > 1.0) return FORGE_ERR_HYPER;
+      break;
+    case FORGE_RMSPROP:
+      if (h->alpha < 0.0 || h->alpha >= 1.0) return FORGE_ERR_HYPER;
+      break;
+    default:
+      break;
+  }
+  if (opt == FORGE_RADAM && h->beta2 <= 0.0) return FORGE_ERR_HYPER;
+  return FORGE_OK;
+}
+
+// Moment slots: returns the state format (ST_F32 / ST_Q8) or a negative status.
+int check_states(int opt, int io_dtype, const forge_tensor* W, const forge_tensor* m, const forge_tensor* v) {
+  const int sl = opt_slots(opt);
+  const forge_tensor* slot[2] = {m, v};
+  int fmt = -1;
+  for (int k = 0; k < 2; ++k) {
+    if (!(sl & (1 << k))) continue;
+    const forge_tensor* t = slot[k];
+    if (!t || !t->data) return FORGE_ERR_NULL;
+    int r = check_shape(t);
+    if (r) return r;
+    if (t->rows != W->rows || t->cols != W->cols) return FORGE_ERR_SHAPE;
+    int f;
+    if (t->dtype == FORGE_F32) {
+      f = ST_F32;
+      if (!aligned16(t->data) || t->ld % 4) return FORGE_ERR_ALIGN;
+    } else if ((k == 0 && t->dtype == FORGE_I8) || (k == 1 && t->dtype == FORGE_U8)) {
+      f = ST_Q8;
+      if (io_dtype != FORGE_BF16) return FORGE_ERR_DTYPE;
+      if (!t->scale) return FORGE_ERR_NULL;
+      if (!aligned16(t->data) || t->ld % 16 || ((uintptr_t)t->scale & 3u)) return FORGE_ERR_ALIGN;
+      if (t->cols % 64) return FORGE_ERR_UNSUPPORTED;
+    } else {
+      return FORGE_ERR_DTYPE;
+    }
+    if (fmt >= 0 && f != fmt) return FORGE_ERR_DTYPE;
+    fmt = f;
+  }
+  return fmt < 0 ? ST_F32 : fmt;
+}
+
+int check_alias(const forge_tensor* const* outs, int n_out, const forge_tensor* const* ins, int n_in) {
+  for (int a = 0; a < n_out; ++a) {
+    if (!outs[a]) continue;
+    const Range ra = range_of(outs[a]);
+    for (int b = a + 1; b < n_out; ++b)
+      if (outs[b] && overlap(ra, range_of(outs[b]))) return FORGE_ERR_ALIAS;
+    for (int b = 0; b < n_in; ++b)
+      if (ins[b] && overlap(ra, range_of(ins[b]))) return FORGE_ERR_ALIAS;
+    if (outs[a]->scale) {
+      const int64_t nb = outs[a]->rows * (outs[a]->cols / 64) * 4;
+      const Range rs{(uintptr_t)outs[a]->scale, (uintptr_t)outs[a]->scale + (uintptr_t)nb};
+      for (int b = 0; b < n_out; ++b)
+        if (outs[b] && overlap(rs, range_of(outs[b]))) return FORGE_ERR_ALIAS;
+    }
+  }
+  return FORGE_OK;
+}
+
+OptArgs make_args(forge_tensor* W, forge_tensor* m, forge_tensor* v, int opt, const forge_scalars& s,
+                  uint64_t seed, int64_t step) {
+  const int sl = opt_slots(opt);
+  OptArgs a{};
+  a.W = W->data;
+  a.ldw = W->ld;
+  if (sl & 1) {
+    a.m = m->data;
+    a.ldm = m->ld;
+    a.m_scale = m->scale;
+  }
+  if (sl & 2) {
+    a.v = v->data;
+    a.ldv = v->ld;
+    a.v_scale = v->scale;
+  }
+  a.out = (int32_t)W->rows;
+  a.in = (int32_t)W->cols;
+  a.rng_base = rng_base(seed, (uint64_t)step);
+  a.s = s;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int forge_version(void) { return 100; }
+
+const char* forge_status_str(int status) {
+  switch (status) {
+    case FORGE_OK: return "ok";
+    case FORGE_ERR_NULL: return "a required pointer is NULL";
+    case FORGE_ERR_SHAPE: return "tensor dimensions are inconsistent";
+    case FORGE_ERR_DTYPE: return "unsupported dtype combination";
+    case FORGE_ERR_ALIGN: return "pointer not 16-byte aligned or cols/ld not a multiple of the vector width";
+    case FORGE_ERR_UNSUPPORTED: return "size not supported by the kernels";
+    case FORGE_ERR_HYPER: return "invalid optimizer, step or hyper-parameter";
+    case FORGE_ERR_HIP: return "HIP kernel launch failed";
+    case FORGE_ERR_ALIAS: return "output tensors overlap each other or an input";
+    default: return "unknown status";
+  }
+}
+
+int forge_default_hyper(int32_t opt, forge_hyper* h) {
+  if (!h) return FORGE_ERR_NULL;
+  if (opt < FORGE_ADAMW || opt > FORGE_RADAM) return FORGE_ERR_HYPER;
+  *h = forge_hyper{};
+  h->lr = 1e-3;
+  h->beta1 = 0.9;
+  h->beta2 = 0.999;
+  h->eps = 1e-8;
+  h->alpha = 0.99;
+  h->momentum_decay = 4e-3;
+  h->stochastic_round = 1;
+  switch (opt) {
+    case FORGE_ADAMW: h->weight_decay = 0.01; break;
+    case FORGE_SGD_MOMENTUM: h->momentum = 0.9; break;
+    case FORGE_LION:
+      h->lr = 1e-4;
+      h->beta2 = 0.99;
+      h->weight_decay = 0.1;
+      break;
+    case FORGE_ADAGRAD: h->eps = 1e-10; break;
+    default: break;
+  }
+  return FORGE_OK;
+}
+
+int forge_step_scalars(int32_t opt, const forge_hyper* h, int64_t step, forge_scalars* out) {
+  if (!out) return FORGE_ERR_NULL;
+  int r = check_hyper(opt, h, step);
+  if (r) return r;
+  const double t = (double)step;
+  const double lr = h->lr, b1 = h->beta1, b2 = h->beta2, wd = h->weight_decay;
+  forge_scalars s{};
+  s.opt = opt;
+  s.lr = (float)lr;
+  s.wd = (float)wd;
+  s.eps = (float)h->eps;
+  s.decay = (float)(1.0 - lr * wd);
+  s.b1 = (float)b1;
+  s.omb1 = (float)(1.0 - b1);
+  s.b2 = (float)b2;
+  s.omb2 = (float)(1.0 - b2);
+  const double bc1 = 1.0 - pow(b1, t), bc2 = 1.0 - pow(b2, t);
+  switch (opt) {
+    case FORGE_ADAMW:
+      s.step_size = (float)(lr / bc1);
+      s.inv_sqrt_bc2 = (float)(1.0 / sqrt(bc2));
+      break;
+    case FORGE_SGD_MOMENTUM: {
+      const double mu = h->momentum;
+      // The momentum buffer starts as the first (decayed) gradient itself.
+      s.b1 = step == 1 ? 0.f : (float)mu;
+      s.omb1 = step == 1 ? 1.f : (float)(1.0 - h->dampening);
+      s.c_m = (float)mu;
+      s.flag = h->nesterov ? 1 : 0;
+      break;
+    }
+    case FORGE_RMSPROP:
+      s.b2 = (float)h->alpha;
+      s.omb2 = (float)(1.0 - h->alpha);
+      break;
+    case FORGE_ADAGRAD:
+      s.lr = (float)(lr / (1.0 + (t - 1.0) * h->lr_decay));
+      break;
+    case FORGE_NADAM: {
+      const double psi = h->momentum_decay;
+      auto mu = [&](double k) { return b1 * (1.0 - 0.5 * pow(0.96, k * psi)); };
+      double prod = 1.0;
+      for (int64_t k = 1; k <= step; ++k) prod *= mu((double)k);
+      const double mu_t = mu(t), mu_n = mu(t + 1.0);
+      s.inv_sqrt_bc2 = (float)(1.0 / sqrt(bc2));
+      s.c_g = (float)(lr * (1.0 - mu_t) / (1.0 - prod));
+      s.c_m = (float)(lr * mu_n / (1.0 - prod * mu_n));
+      break;
+    }
+    case FORGE_RADAM: {
+      const double rho_inf = 2.0 / (1.0 - b2) - 1.0;
+      const double rho_t = rho_inf - 2.0 * t * pow(b2, t) / bc2;
+      if (rho_t > 5.0) {
+        const double rect = sqrt((rho_t - 4.0) * (rho_t - 2.0) * rho_inf / ((rho_inf - 4.0) * (rho_inf - 2.0) * rho_t));
+        s.flag = 1;
+        s.step_size = (float)(lr * rect * sqrt(bc2) / bc1);
+      } else {
+        s.flag = 0;
+        s.step_size = (float)(lr / bc1);
+      }
+      break;
+    }
+    default:
+      break;
+  }
+  *out = s;
+  return FORGE_OK;
+}
+
+uint32_t forge_rand16(uint64_t seed, int64_t step, uint32_t idx) {
+  return rand16_from_base(rng_base(seed, (uint64_t)step), idx);
+}
+
+uint16_t forge_sr_bf16(float x, uint32_t r16) { return (uint16_t)sr_bf16_bits(x, r16 & 0xFFFFu); }
+
+int forge_linear_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge_tensor* W, forge_tensor* m,
+                            forge_tensor* v, int32_t opt, const forge_hyper* hyper, int64_t step, uint64_t seed,
+                            forge_stream_t stream) {
+  if (!X || !dY || !W) return FORGE_ERR_NULL;
+  int r = check_hyper(opt, hyper, step);
+  if (r) return r;
+  const int io = W->dtype;
+  if (io != FORGE_F32 && io != FORGE_BF16) return FORGE_ERR_DTYPE;
+  if ((r = check_io(X, io)) || (r = check_io(dY, io)) || (r = check_io(W, io))) return r;
+  if (X->rows != dY->rows || X->cols != W->cols || dY->cols != W->rows) return FORGE_ERR_SHAPE;
+  const int fmt = check_states(opt, io, W, m, v);
+  if (fmt < 0) return fmt;
+  if (W->rows * W->cols >= ((int64_t)1 << 32)) return FORGE_ERR_UNSUPPORTED;
+  const int sl = opt_slots(opt);
+  const forge_tensor* outs[3] = {W, (sl & 1) ? m : nullptr, (sl & 2) ? v : nullptr};
+  const forge_tensor* ins[2] = {X, dY};
+  if ((r = check_alias(outs, 3, ins, 2))) return r;
+  forge_scalars s;
+  if ((r = forge_step_scalars(opt, hyper, step, &s))) return r;
+  if (W->rows == 0 || W->cols == 0) return FORGE_OK;
+  const OptArgs a = make_args(W, m, v, opt, s, seed, step);
+  const GemmDims d{(int32_t)X->rows, (int32_t)W->rows, (int32_t)W->cols, X->ld, dY->ld};
+  const int sr = (io == FORGE_BF16 && hyper->stochastic_round) ? 1 : 0;
+  hipError_t e = launch_wgrad_fused(io == FORGE_BF16, fmt == ST_Q8, opt, sr, X->data, dY->data, d, a,
+                                    (hipStream_t)stream);
+  return e == hipSuccess ? FORGE_OK : FORGE_ERR_HIP;
+}
+
+int forge_linear_dgrad(const forge_tensor* dY, const forge_tensor* W, forge_tensor* dX, forge_stream_t stream) {
+  if (!dY || !W || !dX) return FORGE_ERR_NULL;
+  const int io = W->dtype;
+  if (io != FORGE_F32 && io != FORGE_BF16) return FORGE_ERR_DTYPE;
+  int r;
+  if ((r = check_io(dY, io)) || (r = check_io(W, io)) || (r = check_io(dX, io))) return r;
+  if (dY->cols != W->rows || dX->rows != dY->rows || dX->cols != W->cols) return FORGE_ERR_SHAPE;
+  const forge_tensor* outs[1] = {dX};
+  const forge_tensor* ins[2] = {dY, W};
+  if ((r = check_alias(outs, 1, ins, 2))) return r;
+  if (dX->rows == 0 || dX->cols == 0) return FORGE_OK;
+  hipError_t e = launch_dgrad(io == FORGE_BF16, dY->data, dY->ld, W->data, W->ld, dX->data, dX->ld,
+                              (int32_t)dY->rows, (int32_t)W->rows, (int32_t)W->cols, (hipStream_t)stream);
+  return e == hipSuccess ? FORGE_OK : FORGE_ERR_HIP;
+}
+
+int forge_linear_wgrad(const forge_tensor* X, const forge_tensor* dY, float* dW, int64_t ld_dw,
+                       forge_stream_t stream) {
+  if (!X || !dY || !dW) return FORGE_ERR_NULL;
+  const int io = X->dtype;
+  if (io != FORGE_F32 && io != FORGE_BF16) return FORGE_ERR_DTYPE;
+  int r;
+  if ((r = check_io(X, io)) || (r = check_io(dY, io))) return r;
+  if (X->rows != dY->rows) return FORGE_ERR_SHAPE;
+  if (ld_dw < X->cols) return FORGE_ERR_SHAPE;
+  if (!aligned16(dW) || ld_dw % 4) return FORGE_ERR_ALIGN;
+  const forge_tensor dWt{dW, FORGE_F32, 0, dY->cols, X->cols, ld_dw, nullptr};
+  const forge_tensor* outs[1] = {&dWt};
+  const forge_tensor* ins[2] = {X, dY};
+  if ((r = check_alias(outs, 1, ins, 2))) return r;
+  if (dY->cols == 0 || X->cols == 0) return FORGE_OK;
+  const GemmDims d{(int32_t)X->rows, (int32_t)dY->cols, (int32_t)X->cols, X->ld, dY->ld};
+  hipError_t e = launch_wgrad_store(io == FORGE_BF16, X->data, dY->data, d, dW, ld_dw, (hipStream_t)stream);
+  return e == hipSuccess ? FORGE_OK : FORGE_ERR_HIP;
+}
+
+int forge_optimizer_step(const float* dW, int64_t ld_dw, forge_tensor* W, forge_tensor* m, forge_tensor* v,
+                         int32_t opt, const forge_hyper* hyper, int64_t step, uint64_t seed, forge_stream_t stream) {
+  if (!dW || !W) return FORGE_ERR_NULL;
+  int r = check_hyper(opt, hyper, step);
+  if (r) return r;
+  const int io = W->dtype;
+  if (io != FORGE_F32 && io != FORGE_BF16) return FORGE_ERR_DTYPE;
+  if ((r = check_io(W, io))) return r;
+  if (ld_dw < W->cols) return FORGE_ERR_SHAPE;
+  if (!aligned16(dW) || ld_dw % 4) return FORGE_ERR_ALIGN;
+  const int fmt = check_states(opt, io, W, m, v);
+  if (fmt < 0) return fmt;
+  if (W->rows * W->cols >= ((int64_t)1 << 32)) return FORGE_ERR_UNSUPPORTED;
+  const int sl = opt_slots(opt);
+  const forge_tensor dWt{const_cast<float*>(dW), FORGE_F32, 0, W->rows, W->cols, ld_dw, nullptr};
+  const forge_tensor* outs[3] = {W, (sl & 1) ? m : nullptr, (sl & 2) ? v : nullptr};
+  const forge_tensor* ins[1] = {&dWt};
+  if ((r = check_alias(outs, 3, ins, 1))) return r;
+  forge_scalars s;
+  if ((r = forge_step_scalars(opt, hyper, step, &s))) return r;
+  if (W->rows == 0 || W->cols == 0) return FORGE_OK;
+  const OptArgs a = make_args(W, m, v, opt, s, seed, step);
+  const int sr = (io == FORGE_BF16 && hyper->stochastic_round) ? 1 : 0;
+  hipError_t e = launch_optimizer(io == FORGE_BF16, fmt == ST_Q8, opt, sr, dW, ld_dw, a, (hipStream_t)stream);
+  return e == hipSuccess ? FORGE_OK : FORGE_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,314 @@
+// Input gradient dX = dY W of a linear layer (FORGE explainer, §5 limitations:
+// the input gradient must be read from the old weights, before the update), and
+// the stand-alone element-wise optimizer pass of the two-phase baseline (§1).
+//
+// dgrad mapping on gfx950: the MFMA computes C[m = i][n = t] = sum_o W[o][i] dY[t][o],
+// i.e. dX^T tiles, so a lane's four accumulator rows are four consecutive
+// columns of one dX row (one 8- or 16-byte store). W is staged in LDS as it
+// sits in memory (rows of `out`, contiguous along `in`) and read K-major with
+// the LDS transpose read; dY rows are already contiguous along the contraction
+// index and are read with plain 16-byte LDS reads from a padded layout.
+#include "forge_internal.h"
+
+namespace forge {
+
+__device__ __forceinline__ int dswz(int row) { return (row & 3) | ((row >> 1) & 4); }
+
+__device__ __forceinline__ bf16x4 lds_read_tr_d(const uint16_t* p) {
+  typedef __bf16 v4bf_t __attribute__((__vector_size__(8)));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wold-style-cast"
+  auto lp = (__attribute__((address_space(3))) v4bf_t*)(const_cast<uint16_t*>(p));
+#pragma clang diagnostic pop
+  v4bf_t r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp);
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// BM (in) x BN (tokens) output tile, BK (out) per stage, WM x WN waves.
+template <int BM_, int BN_, int BK_, int WM_, int WN_>
+struct DCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+  static constexpr int NT = 64 * WM * WN;
+  static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
+};
+
+template <class C, bool BF16>
+__global__ __launch_bounds__(C::NT) void dgrad_kernel(const void* __restrict__ dYp, int64_t lddy,
+                                                      const void* __restrict__ Wp, int64_t ldw,
+                                                      void* __restrict__ dXp, int64_t lddx, int T, int n_out,
+                                                      int n_in) {
+  constexpr int ES = BF16 ? 2 : 4;               // element size
+  constexpr int VE = 16 / ES;                    // elements per 16-byte chunk
+  constexpr int LA = BF16 ? C::BM : C::BM + 16;  // W stage row pitch (elements)
+  constexpr int LB = C::BK + (BF16 ? 8 : 4);     // dY stage row pitch (elements), padded
+  constexpr int STAGE = (C::BK * LA + C::BN * LB) * ES;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % C::WM, wn = wave / C::WM;
+  const int wave_m0 = wm * C::TM, wave_n0 = wn * C::TN;
+  const int g16 = lane >> 4, l16 = lane & 15;
+
+  const int tiles_i = (n_in + C::BM - 1) / C::BM;
+  const int bi = blockIdx.x % tiles_i, bt = blockIdx.x / tiles_i;
+  const int i0 = bi * C::BM, t0 = bt * C::BN;
+
+  f32x4 acc[C::FM][C::FN];
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int CA = C::BK * C::BM / VE;  // chunks of W per stage
+  constexpr int CB = C::BN * C::BK / VE;  // chunks of dY per stage
+  constexpr int PA = (CA + C::NT - 1) / C::NT, PB = (CB + C::NT - 1) / C::NT;
+  u32x4 ra[PA], rb[PB];
+  const char* Wb = reinterpret_cast<const char*>(Wp);
+  const char* dYb = reinterpret_cast<const char*>(dYp);
+  auto As = [&](int buf) { return smem + buf * STAGE; };
+  auto Bs = [&](int buf) { return smem + buf * STAGE + C::BK * LA * ES; };
+
+  auto gload = [&](int s) {
+    const int k0 = s * C::BK;
+#pragma unroll
+    for (int j = 0; j < PA; ++j) {
+      const int c = tid + j * C::NT;
+      const int row = c / (C::BM / VE), col = (c % (C::BM / VE)) * VE;
+      const int o = k0 + row, i = i0 + col;
+      ra[j] = u32x4{0u, 0u, 0u, 0u};
+      if ((CA % C::NT == 0 || c < CA) && o < n_out && i < n_in)
+        ra[j] = *reinterpret_cast<const u32x4*>(Wb + ((int64_t)o * ldw + i) * ES);
+    }
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+      const int c = tid + j * C::NT;
+      const int row = c / (C::BK / VE), col = (c % (C::BK / VE)) * VE;
+      const int t = t0 + row, o = k0 + col;
+      rb[j] = u32x4{0u, 0u, 0u, 0u};
+      if ((CB % C::NT == 0 || c < CB) && t < T && o < n_out)
+        rb[j] = *reinterpret_cast<const u32x4*>(dYb + ((int64_t)t * lddy + o) * ES);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < PA; ++j) {
+      const int c = tid + j * C::NT;
+      if (CA % C::NT == 0 || c < CA) {
+        const int row = c / (C::BM / VE), cc = c % (C::BM / VE);
+        int off;
+        if constexpr (BF16) {
+          const int grp = (cc >> 1) ^ (dswz(row) & (C::BM / 16 - 1));
+          off = row * LA + grp * 16 + (cc & 1) * 8;
+        } else {
+          off = row * LA + cc * 4;
+        }
+        *reinterpret_cast<u32x4*>(As(buf) + off * ES) = ra[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+      const int c = tid + j * C::NT;
+      if (CB % C::NT == 0 || c < CB) {
+        const int row = c / (C::BK / VE), cc = c % (C::BK / VE);
+        *reinterpret_cast<u32x4*>(Bs(buf) + (row * LB + cc * VE) * ES) = rb[j];
+      }
+    }
+  };
+
+  const int nstages = (n_out + C::BK - 1) / C::BK;
+  if (nstages > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+  const int r4 = l16 >> 2, c4 = l16 & 3;
+  for (int s = 0; s < nstages; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nstages) gload(s + 1);
+    if constexpr (BF16) {
+      const uint16_t* A = reinterpret_cast<const uint16_t*>(As(buf));
+      const uint16_t* B = reinterpret_cast<const uint16_t*>(Bs(buf));
+#pragma unroll
+      for (int kk = 0; kk < C::BK / 32; ++kk) {
+        const int k0 = kk * 32 + 8 * g16 + r4, k1 = k0 + 4;
+        bf16x8 af[C::FM], bfr[C::FN];
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+          const int grp = (wave_m0 >> 4) + fm;
+          bf16x4 lo = lds_read_tr_d(A + k0 * LA + ((grp ^ (dswz(k0) & (C::BM / 16 - 1))) << 4) + 4 * c4);
+          bf16x4 hi = lds_read_tr_d(A + k1 * LA + ((grp ^ (dswz(k1) & (C::BM / 16 - 1))) << 4) + 4 * c4);
+          af[fm] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) {
+          const int row = wave_n0 + 16 * fn + l16;
+          bfr[fn] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(B + row * LB + kk * 32 + 8 * g16));
+        }
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < C::FN; ++fn)
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+      }
+    } else {
+      const float* A = reinterpret_cast<const float*>(As(buf));
+      const float* B = reinterpret_cast<const float*>(Bs(buf));
+#pragma unroll
+      for (int kk = 0; kk < C::BK / 4; ++kk) {
+        const int k = kk * 4 + g16;
+        float af[C::FM], bfr[C::FN];
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) af[fm] = A[k * LA + wave_m0 + 16 * fm + l16];
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) bfr[fn] = B[(wave_n0 + 16 * fn + l16) * LB + k];
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < C::FN; ++fn)
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+      }
+    }
+    if (s + 1 < nstages) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // C[m = i][n = t]: lane holds dX[t][i..i+3].
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn) {
+    const int t = t0 + wave_n0 + 16 * fn + l16;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const int i = i0 + wave_m0 + 16 * fm + 4 * g16;
+      if (t < T && i < n_in) {
+        const f32x4 c = acc[fm][fn];
+        if constexpr (BF16) {
+          u32x2 r;
+          r.x = rne_bf16_bits(c.x) | (rne_bf16_bits(c.y) << 16);
+          r.y = rne_bf16_bits(c.z) | (rne_bf16_bits(c.w) << 16);
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(dXp) + (int64_t)t * lddx + i) = r;
+        } else {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dXp) + (int64_t)t * lddx + i) = c;
+        }
+      }
+    }
+  }
+}
+
+using DCfgBF16 = DCfg<128, 128, 64, 2, 2>;
+using DCfgF32 = DCfg<64, 64, 16, 2, 2>;
+
+hipError_t launch_dgrad(int io_bf16, const void* dY, int64_t lddy, const void* W, int64_t ldw, void* dX,
+                        int64_t lddx, int32_t T, int32_t n_out, int32_t n_in, hipStream_t stream) {
+  if (io_bf16) {
+    using C = DCfgBF16;
+    const int tiles = ((n_in + C::BM - 1) / C::BM) * ((T + C::BN - 1) / C::BN);
+    if (tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL((dgrad_kernel<C, true>), dim3(tiles), dim3(C::NT), 0, stream, dY, lddy, W, ldw, dX, lddx, T,
+                       n_out, n_in);
+  } else {
+    using C = DCfgF32;
+    const int tiles = ((n_in + C::BM - 1) / C::BM) * ((T + C::BN - 1) / C::BN);
+    if (tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL((dgrad_kernel<C, false>), dim3(tiles), dim3(C::NT), 0, stream, dY, lddy, W, ldw, dX, lddx, T,
+                       n_out, n_in);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Element-wise optimizer pass of the unfused baseline: each thread owns four
+// consecutive elements of one row; 16 consecutive threads cover one INT8 block
+// of 64 (rows are multiples of 64 long in that mode).
+// ---------------------------------------------------------------------------
+template <bool W_BF16, int OPT, bool Q8, bool SR>
+__global__ __launch_bounds__(256) void optimizer_kernel(const float* __restrict__ dW, int64_t ld_dw, OptArgs a) {
+  constexpr int SL = opt_slots(OPT);
+  constexpr bool HAS_M = SL & 1, HAS_V = SL & 2;
+  const int64_t vec_per_row = a.in >> 2;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)a.out * vec_per_row;
+  const bool valid = gid < total;
+  const int o = valid ? (int)(gid / vec_per_row) : 0;
+  const int i = valid ? (int)(gid % vec_per_row) * 4 : 0;
+  float w[4] = {0.f, 0.f, 0.f, 0.f}, m[4] = {0.f, 0.f, 0.f, 0.f}, v[4] = {0.f, 0.f, 0.f, 0.f}, g[4];
+  if (valid) {
+    load_f4(dW, ld_dw, o, i, g);
+    load_w4<W_BF16>(a, o, i, w);
+    if constexpr (Q8) {
+      if constexpr (HAS_M) dequant_m4(a, o, i, m);
+      if constexpr (HAS_V) dequant_v4(a, o, i, v);
+    } else {
+      if constexpr (HAS_M) load_f4(a.m, a.ldm, o, i, m);
+      if constexpr (HAS_V) load_f4(a.v, a.ldv, o, i, v);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) opt_apply<OPT>(g[j], w[j], m[j], v[j], a.s);
+    store_w4<W_BF16, SR>(a, o, i, w);
+  }
+  if constexpr (Q8) {
+    float r[4], mmax = 0.f, vmax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r[j] = sqrtf(v[j]);
+      mmax = fmaxf(mmax, fabsf(m[j]));
+      vmax = fmaxf(vmax, r[j]);
+    }
+#pragma unroll
+    for (int sh = 1; sh < 16; sh <<= 1) {
+      mmax = fmaxf(mmax, __shfl_xor(mmax, sh));
+      vmax = fmaxf(vmax, __shfl_xor(vmax, sh));
+    }
+    const float sm = mmax / 127.f, sv = vmax / 255.f;
+    if (valid) {
+      if constexpr (HAS_M)
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<int8_t*>(a.m) + (int64_t)o * a.ldm + i) = quant_m4(m, sm);
+      if constexpr (HAS_V)
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.v) + (int64_t)o * a.ldv + i) = quant_v4(r, sv);
+      if ((i & 63) == 0) {
+        const int64_t si = (int64_t)o * (a.in >> 6) + (i >> 6);
+        if constexpr (HAS_M) a.m_scale[si] = sm;
+        if constexpr (HAS_V) a.v_scale[si] = sv;
+      }
+    }
+  } else {
+    if (valid) {
+      if constexpr (HAS_M) store_f4(a.m, a.ldm, o, i, m);
+      if constexpr (HAS_V) store_f4(a.v, a.ldv, o, i, v);
+    }
+  }
+}
+
+template <int OPT>
+static hipError_t launch_opt_t(int w_bf16, int q8, int sr, const float* dW, int64_t ld_dw, const OptArgs& a,
+                               hipStream_t st) {
+  const int64_t total = (int64_t)a.out * (a.in >> 2);
+  if (total == 0) return hipSuccess;
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  if (!w_bf16) {
+    hipLaunchKernelGGL((optimizer_kernel<false, OPT, false, false>), grid, block, 0, st, dW, ld_dw, a);
+  } else if (q8) {
+    if (sr) hipLaunchKernelGGL((optimizer_kernel<true, OPT, true, true>), grid, block, 0, st, dW, ld_dw, a);
+    else hipLaunchKernelGGL((optimizer_kernel<true, OPT, true, false>), grid, block, 0, st, dW, ld_dw, a);
+  } else {
+    if (sr) hipLaunchKernelGGL((optimizer_kernel<true, OPT, false, true>), grid, block, 0, st, dW, ld_dw, a);
+    else hipLaunchKernelGGL((optimizer_kernel<true, OPT, false, false>), grid, block, 0, st, dW, ld_dw, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_optimizer(int w_bf16, int state_q8, int opt, int sr, const float* dW, int64_t ld_dw,
+                            const OptArgs& a, hipStream_t stream) {
+  switch (opt) {
+    case FORGE_ADAMW: return launch_opt_t<FORGE_ADAMW>(w_bf16, state_q8, sr, dW, ld_dw, a, stream);
+    case FORGE_SGD: return launch_opt_t<FORGE_SGD>(w_bf16, state_q8, sr, dW, ld_dw, a, stream);
+    case FORGE_SGD_MOMENTUM: return launch_opt_t<FORGE_SGD_MOMENTUM>(w_bf16, state_q8, sr, dW, ld_dw, a, stream);
+    case FORGE_LION: return launch_opt_t<FORGE_LION>(w_bf16, state_q8, sr, dW, ld_dw, a, stream);
+    case FORGE_RMSPROP: return launch_opt_t<FORGE_RMSPROP>(w_bf16, state_q8, sr, dW, ld_dw, a, stream);
+    case FORGE_ADAGRAD: return launch_opt_t<FORGE_ADAGRAD>(w_bf16, state_q8, sr, dW, ld_dw, a, stream);
+    case FORGE_NADAM: return launch_opt_t<FORGE_NADAM>(w_bf16, state_q8, sr, dW, ld_dw, a, stream);
+    case FORGE_RADAM: return launch_opt_t<FORGE_RADAM>(w_bf16, state_q8, sr, dW, ld_dw, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace forge

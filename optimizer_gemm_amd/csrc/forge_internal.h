@@ -1,0 +1,253 @@
+// Internal device/host helpers of the forge library (not part of the C ABI).
+//
+// Everything here serves the fused weight-gradient + optimizer step of the
+// FORGE explainer pages (technical summary, §2 Method): the counter-hash RNG
+// and stochastic rounding for the bfloat16 weight write-back, the per-element
+// optimizer arithmetic that runs on the FP32 accumulator registers, and the
+// INT8 block-64 moment codec.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/forge.h"
+
+namespace forge {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// State formats of the moment slots.
+enum StateFmt { ST_F32 = 0, ST_Q8 = 1 };
+// Which slots an optimizer keeps (bit 0: m, bit 1: v).
+__host__ __device__ constexpr int opt_slots(int opt) {
+  return opt == FORGE_ADAMW ? 3 : opt == FORGE_SGD ? 0 : opt == FORGE_SGD_MOMENTUM ? 1
+       : opt == FORGE_LION ? 1 : opt == FORGE_RMSPROP ? 2 : opt == FORGE_ADAGRAD ? 2
+       : opt == FORGE_NADAM ? 3 : 3;
+}
+
+// ---------------------------------------------------------------------------
+// Counter-based random bits and stochastic rounding (§2 "Precision and
+// fidelity": stochastic rounding of the bfloat16 weight write-back so sub-ULP
+// updates accumulate without bias). The counter of element idx at step t is
+// (t << 32) | idx; its random word is SplitMix64 output number counter+1 from
+// state `seed` (Steele, Lea & Flood, OOPSLA 2014); the top 16 bits are used.
+// ---------------------------------------------------------------------------
+__host__ __device__ __forceinline__ uint64_t splitmix64_mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// seed + gamma*(counter+1) for counter = (step<<32)|idx, split so the step part
+// is computed once per launch: base = seed + gamma*(step<<32).
+__host__ __device__ __forceinline__ uint64_t rng_base(uint64_t seed, uint64_t step) {
+  return seed + 0x9E3779B97F4A7C15ull * (step << 32);
+}
+__host__ __device__ __forceinline__ uint32_t rand16_from_base(uint64_t base, uint32_t idx) {
+  uint64_t z = base + 0x9E3779B97F4A7C15ull * ((uint64_t)idx + 1ull);
+  return (uint32_t)(splitmix64_mix(z) >> 48);
+}
+
+__host__ __device__ __forceinline__ uint32_t f32_bits(float x) {
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  return u;
+}
+__host__ __device__ __forceinline__ float bits_f32(uint32_t u) {
+  float x;
+  memcpy(&x, &u, 4);
+  return x;
+}
+
+// bfloat16 bits of x rounded stochastically with random bits r16 < 2^16.
+__host__ __device__ __forceinline__ uint32_t sr_bf16_bits(float x, uint32_t r16) {
+  uint32_t u = f32_bits(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
+  return (u + r16) >> 16;
+}
+// bfloat16 bits of x rounded to nearest, ties to even.
+__host__ __device__ __forceinline__ uint32_t rne_bf16_bits(float x) {
+  uint32_t u = f32_bits(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__host__ __device__ __forceinline__ float bf16_bits_f32(uint32_t b) { return bits_f32(b << 16); }
+
+// ---------------------------------------------------------------------------
+// Per-element optimizer updates on FP32 registers (§2 "Core mechanism", step 2:
+// the update runs on the completed gradient tile inside the registers). g is
+// the gradient element, w the weight, m/v the moment slots. Scalars come from
+// the host (forge_step_scalars), so the same code serves every step.
+// ---------------------------------------------------------------------------
+template <int OPT>
+__device__ __forceinline__ void opt_apply(float g, float& w, float& m, float& v, const forge_scalars& s) {
+  if constexpr (OPT == FORGE_ADAMW) {
+    w = w * s.decay;
+    m = fmaf(s.b1, m, s.omb1 * g);
+    v = fmaf(s.b2, v, s.omb2 * (g * g));
+    float denom = fmaf(sqrtf(v), s.inv_sqrt_bc2, s.eps);
+    w = w - s.step_size * (m / denom);
+  } else if constexpr (OPT == FORGE_SGD) {
+    float d = fmaf(s.wd, w, g);
+    w = w - s.lr * d;
+  } else if constexpr (OPT == FORGE_SGD_MOMENTUM) {
+    float d = fmaf(s.wd, w, g);
+    m = fmaf(s.b1, m, s.omb1 * d);  // b1 = 0, omb1 = 1 on step 1 (buffer starts as d)
+    float dir = s.flag ? fmaf(s.c_m, m, d) : m;
+    w = w - s.lr * dir;
+  } else if constexpr (OPT == FORGE_LION) {
+    float c = fmaf(s.b1, m, s.omb1 * g);
+    float sg = c > 0.f ? 1.f : (c < 0.f ? -1.f : 0.f);
+    w = w * s.decay - s.lr * sg;
+    m = fmaf(s.b2, m, s.omb2 * g);
+  } else if constexpr (OPT == FORGE_RMSPROP) {
+    float d = fmaf(s.wd, w, g);
+    v = fmaf(s.b2, v, s.omb2 * (d * d));
+    w = w - s.lr * (d / (sqrtf(v) + s.eps));
+  } else if constexpr (OPT == FORGE_ADAGRAD) {
+    float d = fmaf(s.wd, w, g);
+    v = fmaf(d, d, v);
+    w = w - s.lr * (d / (sqrtf(v) + s.eps));
+  } else if constexpr (OPT == FORGE_NADAM) {
+    float d = fmaf(s.wd, w, g);
+    m = fmaf(s.b1, m, s.omb1 * d);
+    v = fmaf(s.b2, v, s.omb2 * (d * d));
+    float denom = fmaf(sqrtf(v), s.inv_sqrt_bc2, s.eps);
+    w = w - fmaf(s.c_g, d, s.c_m * m) / denom;
+  } else {  // FORGE_RADAM
+    float d = fmaf(s.wd, w, g);
+    m = fmaf(s.b1, m, s.omb1 * d);
+    v = fmaf(s.b2, v, s.omb2 * (d * d));
+    if (s.flag)
+      w = w - s.step_size * (m / (sqrtf(v) + s.eps));
+    else
+      w = w - s.step_size * m;
+  }
+}
+
+// Arguments of the optimizer part, shared by the fused epilogue and the
+// stand-alone element-wise kernel of the unfused baseline.
+struct OptArgs {
+  void* W;            // [out, ldw] bf16 or f32
+  void* m;            // [out, ldm] f32 or int8
+  void* v;            // [out, ldv] f32 or uint8
+  float* m_scale;     // [out, in/64]  (Q8 only)
+  float* v_scale;     // [out, in/64]  (Q8 only)
+  int64_t ldw, ldm, ldv;
+  int32_t out, in;
+  uint64_t rng_base;  // rng_base(seed, step)
+  forge_scalars s;
+};
+
+// Loads 4 consecutive weights W[o][i..i+3] as float.
+template <bool W_BF16>
+__device__ __forceinline__ void load_w4(const OptArgs& a, int o, int i, float w[4]) {
+  if constexpr (W_BF16) {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(a.W) + (int64_t)o * a.ldw + i;
+    u32x2 r = *reinterpret_cast<const u32x2*>(p);
+    w[0] = bits_f32(r.x << 16);
+    w[1] = bits_f32(r.x & 0xFFFF0000u);
+    w[2] = bits_f32(r.y << 16);
+    w[3] = bits_f32(r.y & 0xFFFF0000u);
+  } else {
+    const float* p = reinterpret_cast<const float*>(a.W) + (int64_t)o * a.ldw + i;
+    f32x4 r = *reinterpret_cast<const f32x4*>(p);
+    w[0] = r.x; w[1] = r.y; w[2] = r.z; w[3] = r.w;
+  }
+}
+
+// Stores 4 consecutive weights; bfloat16 with stochastic rounding or nearest-even.
+template <bool W_BF16, bool SR>
+__device__ __forceinline__ void store_w4(const OptArgs& a, int o, int i, const float w[4]) {
+  if constexpr (W_BF16) {
+    uint32_t b[4];
+    const uint32_t idx0 = (uint32_t)o * (uint32_t)a.in + (uint32_t)i;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (SR)
+        b[j] = sr_bf16_bits(w[j], rand16_from_base(a.rng_base, idx0 + j));
+      else
+        b[j] = rne_bf16_bits(w[j]);
+    }
+    u32x2 r;
+    r.x = b[0] | (b[1] << 16);
+    r.y = b[2] | (b[3] << 16);
+    uint16_t* p = reinterpret_cast<uint16_t*>(a.W) + (int64_t)o * a.ldw + i;
+    *reinterpret_cast<u32x2*>(p) = r;
+  } else {
+    float* p = reinterpret_cast<float*>(a.W) + (int64_t)o * a.ldw + i;
+    *reinterpret_cast<f32x4*>(p) = f32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+__device__ __forceinline__ void load_f4(const void* base, int64_t ld, int o, int i, float x[4]) {
+  f32x4 r = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + (int64_t)o * ld + i);
+  x[0] = r.x; x[1] = r.y; x[2] = r.z; x[3] = r.w;
+}
+__device__ __forceinline__ void store_f4(void* base, int64_t ld, int o, int i, const float x[4]) {
+  *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + (int64_t)o * ld + i) = f32x4{x[0], x[1], x[2], x[3]};
+}
+
+// INT8 block-64 codec (§2 "Precision and fidelity": INT8 optimizer states with
+// blocks of 64). m: signed codes, value q*s, s = absmax/127. v: unsigned codes
+// of sqrt(v), value (q*s)^2, s = max sqrt(v)/255. All-zero block: s = 0, q = 0.
+__device__ __forceinline__ void dequant_m4(const OptArgs& a, int o, int i, float x[4]) {
+  const int8_t* p = reinterpret_cast<const int8_t*>(a.m) + (int64_t)o * a.ldm + i;
+  uint32_t q = *reinterpret_cast<const uint32_t*>(p);
+  float s = a.m_scale[(int64_t)o * (a.in >> 6) + (i >> 6)];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] = (float)(int8_t)((q >> (8 * j)) & 0xFF) * s;
+}
+__device__ __forceinline__ void dequant_v4(const OptArgs& a, int o, int i, float x[4]) {
+  const uint8_t* p = reinterpret_cast<const uint8_t*>(a.v) + (int64_t)o * a.ldv + i;
+  uint32_t q = *reinterpret_cast<const uint32_t*>(p);
+  float s = a.v_scale[(int64_t)o * (a.in >> 6) + (i >> 6)];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float r = (float)((q >> (8 * j)) & 0xFF) * s;
+    x[j] = r * r;
+  }
+}
+// Quantises 4 values with the block scale s (already reduced over the block).
+__device__ __forceinline__ uint32_t quant_m4(const float x[4], float s) {
+  uint32_t q = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float c = s > 0.f ? rintf(x[j] / s) : 0.f;
+    c = fminf(fmaxf(c, -127.f), 127.f);
+    q |= ((uint32_t)(int32_t)c & 0xFFu) << (8 * j);
+  }
+  return q;
+}
+__device__ __forceinline__ uint32_t quant_v4(const float r[4], float s) {  // r = sqrt(v)
+  uint32_t q = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float c = s > 0.f ? rintf(r[j] / s) : 0.f;
+    c = fminf(fmaxf(c, 0.f), 255.f);
+    q |= ((uint32_t)c & 0xFFu) << (8 * j);
+  }
+  return q;
+}
+
+// Host-side launchers (defined in the .hip files).
+struct GemmDims {
+  int32_t T, out, in;
+  int64_t ldx, lddy;
+};
+
+hipError_t launch_wgrad_fused(int io_bf16, int state_q8, int opt, int sr, const void* X, const void* dY,
+                              const GemmDims& d, const OptArgs& a, hipStream_t stream);
+hipError_t launch_wgrad_store(int io_bf16, const void* X, const void* dY, const GemmDims& d, float* dW,
+                              int64_t ld_dw, hipStream_t stream);
+hipError_t launch_optimizer(int w_bf16, int state_q8, int opt, int sr, const float* dW, int64_t ld_dw,
+                            const OptArgs& a, hipStream_t stream);
+hipError_t launch_dgrad(int io_bf16, const void* dY, int64_t lddy, const void* W, int64_t ldw, void* dX,
+                        int64_t lddx, int32_t T, int32_t out, int32_t in, hipStream_t stream);
+
+}  // namespace forge

@@ -1,0 +1,261 @@
+"""GPU parity of the fused step, dgrad and the unfused baseline against the oracle.
+
+Every case draws seeded inputs (synth), runs the HIP path through the C ABI, and
+checks each step teacher-forced: the oracle starts each step from the GPU's own
+previous W and moments, so per-step tolerances apply (see tests/_parity.py).
+Sizes here are small enough for the full float64 oracle, yet span several
+tiles with ragged tails in every dimension.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import gemm, optim, step
+from synth import LayerSpec, draw_layer_batch, draw_layer_init, f32_from_bf16_bits
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+def _forge():
+    import optimizer_gemm_amd as f
+    return f
+
+
+def _gpu_hyper(hp, sr=True):
+    d = dict(hp)
+    d["nesterov"] = int(bool(d["nesterov"]))
+    d["stochastic_round"] = int(sr)
+    return d
+
+
+def run_case(spec, opt, steps, config=90, layer=0, state="f32", sr=True, rows=None, hp_over=None,
+             seed=None, label=""):
+    f = _forge()
+    print(f"[case] {label} opt={opt} spec={spec} state={state} sr={sr} steps={steps}", flush=True)
+    io = spec.io
+    hp = optim.hyper(opt, **(hp_over or {}))
+    seed = (0x5EED0000 + config) ^ layer if seed is None else seed
+    W0 = draw_layer_init(config, layer, spec)
+    Wd = P.dev_bf16(W0) if io == "bf16" else P.dev(W0)
+    m, v, ms, vs = f.new_states(Wd, opt, state)
+    sel = np.arange(spec.out) if rows is None else np.asarray(rows)
+    report = []
+    for t in range(1, steps + 1):
+        X, dY = draw_layer_batch(config, layer, t, spec)
+        Xd = P.dev_bf16(X) if io == "bf16" else P.dev(X)
+        dYd = P.dev_bf16(dY) if io == "bf16" else P.dev(dY)
+        W_b = P.host(Wd)[sel]
+        m_b = None if m is None else P.host(m)[sel]
+        v_b = None if v is None else P.host(v)[sel]
+        ms_b = None if ms is None else P.host(ms)[sel]
+        vs_b = None if vs is None else P.host(vs)[sel]
+        f.wgrad_step(Xd, dYd, Wd, m, v, opt, _gpu_hyper(hp, sr), t, seed, ms, vs)
+        torch.cuda.synchronize()
+        ref = step.wgrad_step(opt, X, dY, W_b, m_b, v_b, hp, t, seed, io=io, state=state, sr=sr,
+                              rows=sel, m_scale=ms_b, v_scale=vs_b)
+        W_a = P.host(Wd)[sel]
+        if io == "bf16":
+            ok, n, mx = P.bf16_sr_ok(W_a, ref["W"])
+            assert ok, f"step {t}: {n} bf16 weights differ (max {mx} steps) of {W_a.size}"
+        else:
+            err = np.max(np.abs(W_a.astype(np.float64) - ref["theta"])) if W_a.size else 0.0
+            assert err <= 1e-3 * hp["lr"], f"step {t}: fp32 W error {err}"
+        for slot, t_gpu, t_scale in (("m", m, ms), ("v", v, vs)):
+            if t_gpu is None:
+                continue
+            got = P.host(t_gpu)[sel]
+            if state == "f32":
+                bad, worst = P.state_ok(got, ref[slot])
+                assert bad == 0, f"step {t}: {slot}: {bad} elements out of tolerance (worst {worst:.3g}x)"
+            else:
+                big, nd, mx = P.codes_ok(got, ref[slot])
+                assert big == 0, f"step {t}: {slot} codes: {big} off by more than one step"
+                bad, worst = P.state_ok(P.host(t_scale)[sel], ref[slot + "_scale"])
+                assert bad == 0, f"step {t}: {slot} scales: {bad} out of tolerance"
+        report.append(t)
+    return Wd, m, v
+
+
+# ---------------------------------------------------------------- fp32 path
+def test_fp32_256_adamw_three_steps():
+    run_case(LayerSpec("linear", 256, 256, 512, io="f32", dy_std=1e-2), "adamw", 3, config=0, sr=False,
+             label="fp32 256x256 T512")
+
+
+@pytest.mark.parametrize("opt", optim.OPTIMIZERS)
+def test_fp32_ragged_all_optimizers(opt):
+    over = {} if opt in ("adamw", "lion") else dict(weight_decay=0.01)
+    run_case(LayerSpec("r", 72, 100, 70, io="f32", dy_std=1e-2), opt, 3, config=91, hp_over=over, sr=False,
+             label="fp32 ragged")
+
+
+# ---------------------------------------------------------------- bf16 path
+@pytest.mark.parametrize("opt", optim.OPTIMIZERS)
+def test_bf16_ragged_all_optimizers_sr(opt):
+    # 200 = 128 + 72 rows, 328 = 2*128 + 72 columns, 130 = 2*64 + 2 tokens
+    run_case(LayerSpec("r", 200, 328, 130), opt, 3, config=92, label="bf16 ragged")
+
+
+def test_bf16_nesterov_and_dampening():
+    run_case(LayerSpec("r", 136, 264, 96), "sgd_momentum", 3, config=93,
+             hp_over=dict(nesterov=True, weight_decay=0.02), label="nesterov")
+    run_case(LayerSpec("r", 136, 264, 96), "sgd_momentum", 3, config=93, layer=1,
+             hp_over=dict(dampening=0.25), label="dampening")
+
+
+def test_bf16_round_to_nearest_mode():
+    run_case(LayerSpec("r", 256, 384, 256), "adamw", 2, config=94, sr=False, label="bf16 rne")
+
+
+def test_bf16_several_tiles():
+    run_case(LayerSpec("m", 512, 640, 1000), "adamw", 2, config=95, label="bf16 512x640 T1000")
+
+
+def test_radam_crosses_rectification():
+    run_case(LayerSpec("r", 128, 128, 64), "radam", 7, config=96, label="radam 7 steps")
+
+
+def test_empty_tokens_zero_gradient():
+    # T == 0: dW = 0, the optimizer still applies decay/momentum
+    run_case(LayerSpec("e", 128, 256, 0), "adamw", 2, config=97, label="T=0")
+    run_case(LayerSpec("e", 64, 64, 0, io="f32"), "sgd_momentum", 2, config=97, sr=False, label="T=0 fp32")
+
+
+# ---------------------------------------------------------------- INT8 states
+@pytest.mark.parametrize("opt", ["adamw", "lion", "rmsprop", "sgd_momentum", "nadam"])
+def test_q8_states(opt):
+    run_case(LayerSpec("q", 136, 320, 200, outlier_frac=0.01), opt, 3, config=98, state="q8", label="q8")
+
+
+# ---------------------------------------------------------------- dgrad
+@pytest.mark.parametrize("shape,io", [((130, 200, 328), "bf16"), ((512, 384, 256), "bf16"),
+                                      ((512, 256, 256), "f32"), ((70, 72, 100), "f32")])
+def test_dgrad(shape, io):
+    f = _forge()
+    T, n_out, n_in = shape
+    spec = LayerSpec("d", n_out, n_in, T, io=io)
+    W = draw_layer_init(99, 0, spec)
+    X, dY = draw_layer_batch(99, 0, 1, spec)
+    if io == "bf16":
+        dX = f.dgrad(P.dev_bf16(dY), P.dev_bf16(W))
+        torch.cuda.synchronize()
+        ref = gemm.dgrad(f32_from_bf16_bits(dY), f32_from_bf16_bits(W))
+        bad, worst = P.dgrad_bf16_ok(P.host_bits(dX), ref)
+        assert bad == 0, f"{bad} dX elements beyond one bf16 ulp (worst {worst:.3g})"
+    else:
+        dX = f.dgrad(P.dev(dY), P.dev(W))
+        torch.cuda.synchronize()
+        ref = gemm.dgrad(dY, W)
+        bad, worst = P.state_ok(dX.cpu().numpy(), ref, rel=1e-5, floor=0.01)
+        assert bad == 0, f"{bad} fp32 dX elements out of tolerance (worst {worst:.3g})"
+
+
+def test_dgrad_reads_old_weights_before_step():
+    # dgrad enqueued before the fused step on the same stream sees the old W
+    f = _forge()
+    spec = LayerSpec("o", 256, 256, 256)
+    W = draw_layer_init(100, 0, spec)
+    X, dY = draw_layer_batch(100, 0, 1, spec)
+    Wd = P.dev_bf16(W)
+    m, v, _, _ = f.new_states(Wd, "sgd")
+    dX = f.dgrad(P.dev_bf16(dY), Wd)
+    f.wgrad_step(P.dev_bf16(X), P.dev_bf16(dY), Wd, m, v, "sgd", dict(lr=0.5), 1, 1)
+    torch.cuda.synchronize()
+    ref = gemm.dgrad(f32_from_bf16_bits(dY), f32_from_bf16_bits(W))
+    bad, _ = P.dgrad_bf16_ok(P.host_bits(dX), ref)
+    assert bad == 0
+    assert not np.array_equal(P.host_bits(Wd), W)  # the step did change W afterwards
+
+
+# ---------------------------------------------------------------- unfused baseline
+@pytest.mark.parametrize("opt,state", [("adamw", "f32"), ("lion", "f32"), ("radam", "f32"), ("adamw", "q8"),
+                                       ("rmsprop", "q8")])
+def test_unfused_matches_fused(opt, state):
+    f = _forge()
+    spec = LayerSpec("u", 200, 320, 300)
+    W0 = draw_layer_init(101, 0, spec)
+    outs = []
+    for fused in (True, False):
+        Wd = P.dev_bf16(W0)
+        m, v, ms, vs = f.new_states(Wd, opt, state)
+        for t in (1, 2):
+            X, dY = draw_layer_batch(101, 0, t, spec)
+            args = (P.dev_bf16(X), P.dev_bf16(dY), Wd, m, v, opt, None, t, 7, ms, vs)
+            if fused:
+                f.wgrad_step(*args)
+            else:
+                f.wgrad_unfused(*args)
+        torch.cuda.synchronize()
+        outs.append([P.host(x) for x in (Wd, m, v, ms, vs) if x is not None])
+    for a, b in zip(*outs):
+        if a.dtype == np.uint16:
+            ok, n, mx = P.bf16_sr_ok(a, b)
+            assert ok, (n, mx)
+        elif a.dtype in (np.int8, np.uint8):
+            assert P.codes_ok(a, b)[0] == 0
+        else:
+            assert P.state_ok(a, b, rel=1e-6)[0] == 0
+
+
+def test_unfused_dw_matches_oracle():
+    f = _forge()
+    spec = LayerSpec("u", 200, 328, 130)
+    X, dY = draw_layer_batch(102, 0, 1, spec)
+    dW = f.wgrad(P.dev_bf16(X), P.dev_bf16(dY))
+    torch.cuda.synchronize()
+    ref = gemm.wgrad(f32_from_bf16_bits(X), f32_from_bf16_bits(dY))
+    bad, worst = P.state_ok(dW.cpu().numpy(), ref, rel=1e-5, floor=0.01)
+    assert bad == 0, (bad, worst)
+
+
+# ---------------------------------------------------------------- invariants
+def test_bitwise_deterministic_and_resumable():
+    f = _forge()
+    spec = LayerSpec("d", 384, 512, 700)
+    W0 = draw_layer_init(103, 0, spec)
+    res = []
+    for split in (False, True):
+        Wd = P.dev_bf16(W0)
+        m, v, _, _ = f.new_states(Wd, "adamw")
+        for t in (1, 2, 3, 4):
+            if split and t == 3:
+                # "checkpoint": round-trip the state through host memory, then continue
+                Wd = P.dev_bf16(P.host(Wd))
+                m = P.dev(P.host(m))
+                v = P.dev(P.host(v))
+            X, dY = draw_layer_batch(103, 0, t, spec)
+            f.wgrad_step(P.dev_bf16(X), P.dev_bf16(dY), Wd, m, v, "adamw", None, t, 11)
+        torch.cuda.synchronize()
+        res.append((P.host(Wd), P.host(m), P.host(v)))
+    for a, b in zip(*res):
+        assert np.array_equal(a, b)
+
+
+def test_tensor_parallel_shards_equal_unsharded():
+    # exactness under TP (§2 distributed compatibility): row shards (column-parallel layers) and
+    # column shards (row-parallel layers) of W, each updated from its local gradient only,
+    # reproduce the unsharded update bit for bit. Shards are views of one buffer at tile
+    # boundaries, so each element sees the same accumulation order; nearest rounding is used
+    # because the stochastic-rounding counter is the index within the tensor passed in.
+    f = _forge()
+    spec = LayerSpec("tp", 256, 512, 256)
+    W0 = draw_layer_init(104, 0, spec)
+    X, dY = draw_layer_batch(104, 0, 1, spec)
+    Xd, dYd = P.dev_bf16(X), P.dev_bf16(dY)
+    hp = dict(stochastic_round=0)
+    Wn = P.dev_bf16(W0)
+    mn, vn, _, _ = f.new_states(Wn, "adamw")
+    f.wgrad_step(Xd, dYd, Wn, mn, vn, "adamw", hp, 1, 5)
+    Wr = P.dev_bf16(W0)
+    mr, vr, _, _ = f.new_states(Wr, "adamw")
+    for r0 in (0, 128):  # column-parallel: split out-rows, dY columns
+        f.wgrad_step(Xd, dYd[:, r0:r0 + 128], Wr[r0:r0 + 128], mr[r0:r0 + 128], vr[r0:r0 + 128], "adamw", hp, 1, 5)
+    Wc = P.dev_bf16(W0)
+    mc, vc, _, _ = f.new_states(Wc, "adamw")
+    for c0 in (0, 256):  # row-parallel: split in-columns, X columns
+        f.wgrad_step(Xd[:, c0:c0 + 256], dYd, Wc[:, c0:c0 + 256], mc[:, c0:c0 + 256], vc[:, c0:c0 + 256],
+                     "adamw", hp, 1, 5)
+    torch.cuda.synchronize()
+    for got in ((Wr, mr, vr), (Wc, mc, vc)):
+        for a, b in zip(got, (Wn, mn, vn)):
+            assert np.array_equal(P.host(a), P.host(b))
