@@ -51,11 +51,29 @@ def parse():
     p.add_argument("--opt", default="adamw")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-unfused", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run only a plain 1 GiB device copy (3 times) to calibrate HBM byte counters")
     return p.parse_args()
+
+
+def calibrate_copy() -> int:
+    """A plain copy of known size: 1 GiB read + 1 GiB written per dispatch."""
+    import torch
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read_per_dispatch": 4 * n, "bytes_written_per_dispatch": 4 * n}))
+    return 0
 
 
 def main() -> int:
     args = parse()
+    if args.calibrate_copy:
+        return calibrate_copy()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
               "(tensor-parallel shards run the same kernel on each GPU's share)", file=sys.stderr)

@@ -7,5 +7,5 @@ of results, no quantisation.
 """
 from .inputs import (  # noqa: F401
     LayerSpec, WORKLOADS, bf16_bits_from_f32, f32_from_bf16_bits, draw_normal,
-    draw_layer_init, draw_layer_batch, outlier_rows, sample_rows, layer_seed,
+    draw_layer_init, draw_layer_batch, outlier_rows, sample_rows, layer_seed, llama8b_stack,
 )

@@ -5,11 +5,16 @@ The pages evaluate on Llama-3.1-8B and Qwen3 layers (FORGE explainer, section 4
 is drawn from numpy's PCG64 generator seeded by
 ``SeedSequence([0xF06E, config, layer, step, tensor_id])`` with
 tensor_id 0 = W init, 1 = X, 2 = dY, 3 = X outlier rows, 4 = dY outlier rows.
-"N(0, s)" means standard deviation s. bfloat16 tensors are the round-to-nearest-
-even bfloat16 of the float32 sample, done on the bit patterns.
+Dense tensors are drawn in chunks of whole rows (about 4M values each); chunk k
+uses the same seed sequence extended by k, so the values do not depend on the
+number of threads that fill them. "N(0, s)" means standard deviation s.
+bfloat16 tensors are the round-to-nearest-even bfloat16 of the float32 sample,
+done on the bit patterns.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Tuple
 
@@ -19,24 +24,64 @@ ROOT_TAG = 0xF06E
 TID_W, TID_X, TID_DY, TID_X_OUT, TID_DY_OUT = 0, 1, 2, 3, 4
 
 
+_THREADS = max(1, min(16, os.cpu_count() or 1))
+_CHUNK = 1 << 22
+
+
 def layer_seed(config: int, layer: int, step: int, tensor_id: int) -> np.random.Generator:
     """PCG64 generator for one tensor of one layer at one step."""
     ss = np.random.SeedSequence([ROOT_TAG, int(config), int(layer), int(step), int(tensor_id)])
     return np.random.Generator(np.random.PCG64(ss))
 
 
+def _row_chunks(rows: int, cols: int):
+    step = max(1, _CHUNK // max(cols, 1))
+    return [(r0, min(rows, r0 + step)) for r0 in range(0, rows, step)]
+
+
+def _parallel(fn, n):
+    if n <= 1:
+        for k in range(n):
+            fn(k)
+        return
+    with ThreadPoolExecutor(max_workers=min(_THREADS, n)) as ex:
+        list(ex.map(fn, range(n)))
+
+
+def _bf16_rne_inplace(x: np.ndarray, out: np.ndarray) -> None:
+    u = x.view(np.uint32)
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u                      # < 2**32 for every finite float32
+    r >>= np.uint32(16)
+    out[...] = r
+
+
 def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
     """Round float32 samples to bfloat16 (nearest, ties to even); returns uint16 bits.
 
-    Only finite samples occur in these workloads; NaN inputs are rejected.
+    Only finite samples occur in these workloads; NaN or Inf inputs are rejected.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    if not np.all(np.isfinite(x)):
+    out = np.empty(x.shape, dtype=np.uint16)
+    if x.ndim < 2:
+        flat_x, flat_o = x.reshape(1, -1), out.reshape(1, -1)
+    else:
+        flat_x, flat_o = x.reshape(-1, x.shape[-1]), out.reshape(-1, x.shape[-1])
+    chunks = _row_chunks(flat_x.shape[0], flat_x.shape[1])
+    bad = [False] * len(chunks)
+
+    def work(k):
+        r0, r1 = chunks[k]
+        if not np.all(np.isfinite(flat_x[r0:r1])):
+            bad[k] = True
+            return
+        _bf16_rne_inplace(flat_x[r0:r1], flat_o[r0:r1])
+
+    _parallel(work, len(chunks))
+    if any(bad):
         raise ValueError("synthetic inputs must be finite")
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
-    return r.astype(np.uint16)
+    return out
 
 
 def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
@@ -45,11 +90,20 @@ def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def draw_normal(gen: np.random.Generator, shape: Tuple[int, ...], std: float) -> np.ndarray:
-    """float32 N(0, std) samples."""
-    x = gen.standard_normal(size=shape, dtype=np.float32)
-    if std != 1.0:
-        x *= np.float32(std)
+def draw_normal(key: Tuple[int, ...], shape: Tuple[int, int], std: float) -> np.ndarray:
+    """float32 N(0, std) samples of a 2-D tensor; `key` = (config, layer, step, tensor_id)."""
+    rows, cols = shape
+    x = np.empty((rows, cols), dtype=np.float32)
+    chunks = _row_chunks(rows, cols)
+
+    def work(k):
+        r0, r1 = chunks[k]
+        ss = np.random.SeedSequence([ROOT_TAG] + [int(v) for v in key] + [k])
+        np.random.Generator(np.random.PCG64(ss)).standard_normal(out=x[r0:r1], dtype=np.float32)
+        if std != 1.0:
+            x[r0:r1] *= np.float32(std)
+
+    _parallel(work, len(chunks))
     return x
 
 
@@ -92,14 +146,14 @@ def _to_io(x32: np.ndarray, io: str) -> np.ndarray:
 
 def draw_layer_init(config: int, layer: int, spec: LayerSpec) -> np.ndarray:
     """Initial W (uint16 bf16 bits or float32)."""
-    w = draw_normal(layer_seed(config, layer, 0, TID_W), (spec.out, spec.inn), spec.w_std)
+    w = draw_normal((config, layer, 0, TID_W), (spec.out, spec.inn), spec.w_std)
     return _to_io(w, spec.io)
 
 
 def draw_layer_batch(config: int, layer: int, step: int, spec: LayerSpec) -> Tuple[np.ndarray, np.ndarray]:
     """Fresh (X, dY) for one step (step is 1-based); bf16 bits or float32."""
-    x = draw_normal(layer_seed(config, layer, step, TID_X), (spec.T, spec.inn), spec.x_std)
-    dy = draw_normal(layer_seed(config, layer, step, TID_DY), (spec.T, spec.out), spec.dy_std)
+    x = draw_normal((config, layer, step, TID_X), (spec.T, spec.inn), spec.x_std)
+    dy = draw_normal((config, layer, step, TID_DY), (spec.T, spec.out), spec.dy_std)
     if spec.outlier_frac > 0.0:
         rx = outlier_rows(config, layer, step, TID_X_OUT, spec.T, spec.outlier_frac)
         rd = outlier_rows(config, layer, step, TID_DY_OUT, spec.T, spec.outlier_frac)

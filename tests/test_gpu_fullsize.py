@@ -1,0 +1,110 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration bench.py times.
+
+The GPU runs whole layers; the float64 oracle checks a seeded sample of output
+rows (row-sampled mode: the same oracle restricted to those rows, exact because
+the update is element-wise and INT8 blocks never cross rows). Every checked
+step is teacher-forced from the GPU's previous state. dgrad is checked on a
+seeded sample of token rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import gemm, optim
+from synth import WORKLOADS, draw_layer_batch, draw_layer_init, f32_from_bf16_bits, sample_rows
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _forge():
+    import optimizer_gemm_amd as f
+    return f
+
+
+def _gh(hp, sr=True):
+    return dict(hp, nesterov=int(bool(hp["nesterov"])), stochastic_round=int(sr))
+
+
+def _check_dgrad(f, dYd, Wd, dY, W_bits, config, layer, n_tok=48):
+    dX = f.dgrad(dYd, Wd)
+    torch.cuda.synchronize()
+    T = dY.shape[0]
+    trows = np.sort(np.random.default_rng(config * 1000 + layer).choice(T, size=min(n_tok, T), replace=False))
+    ref = f32_from_bf16_bits(dY[trows]).astype(np.float64) @ f32_from_bf16_bits(W_bits).astype(np.float64)
+    bad, worst = P.dgrad_bf16_ok(P.host_bits(dX)[trows], ref)
+    assert bad == 0, f"dgrad: {bad} sampled dX elements beyond one bf16 ulp (worst {worst:.3g})"
+
+
+def _run_layer(f, wl, li, spec, opt, n_steps, check_steps, n_rows, check_dgrad_step=1):
+    hp = optim.hyper(opt)
+    seed = (0x5EED0000 + wl.config) ^ li
+    W0 = draw_layer_init(wl.config, li, spec)
+    Wd = P.dev_bf16(W0)
+    m, v, ms, vs = f.new_states(Wd, opt, wl.state)
+    sel = sample_rows(wl.config, li, spec.out, n_rows)
+    for t in range(1, n_steps + 1):
+        X, dY = draw_layer_batch(wl.config, li, t, spec)
+        Xd, dYd = P.dev_bf16(X), P.dev_bf16(dY)
+        check = t in check_steps
+        if t == check_dgrad_step:
+            _check_dgrad(f, dYd, Wd, dY, P.host(Wd), wl.config, li)
+        before = P.snapshot((Wd, m, v, ms, vs), sel) if check else None
+        f.wgrad_step(Xd, dYd, Wd, m, v, opt, _gh(hp, wl.stochastic_round), t, seed, ms, vs)
+        torch.cuda.synchronize()
+        if check:
+            after = P.snapshot((Wd, m, v, ms, vs), sel)
+            P.verify_step(opt, X, dY, before, after, hp, t, seed, "bf16", wl.state, wl.stochastic_round, sel)
+            print(f"[ok] {spec.name} {spec.out}x{spec.inn} T={spec.T} {opt} step {t}", flush=True)
+        del Xd, dYd
+
+
+@pytest.mark.timeout(300)
+def test_q_proj_8192_ten_steps():
+    f = _forge()
+    wl = WORKLOADS["q_proj_8192"]
+    _run_layer(f, wl, 0, wl.layers[0], "adamw", 10, set(range(1, 11)), 256)
+
+
+@pytest.mark.timeout(300)
+def test_llama8b_decoder_layer_all_seven_linears():
+    f = _forge()
+    wl = WORKLOADS["llama8b_layer_8192"]
+    for li, spec in enumerate(wl.layers):
+        _run_layer(f, wl, li, spec, "adamw", 1, {1}, 128)
+
+
+@pytest.mark.timeout(600)
+def test_down_proj_int8_states_twenty_steps():
+    f = _forge()
+    wl = WORKLOADS["down_q8_16384"]
+    _run_layer(f, wl, 0, wl.layers[0], "adamw", 20, {1, 2, 3, 10, 20}, 128)
+
+
+@pytest.mark.timeout(600)
+def test_qwen14b_mlp_eight_optimizers_ten_steps():
+    # all eight optimizers on the same per-step inputs; every step checked on sampled rows
+    f = _forge()
+    wl = WORKLOADS["qwen14b_mlp_4096"]
+    spec = wl.layers[0]
+    W0 = draw_layer_init(wl.config, 0, spec)
+    sel = sample_rows(wl.config, 0, spec.out, 96)
+    runs = {}
+    for opt in wl.optimizers:
+        Wd = P.dev_bf16(W0)
+        runs[opt] = (Wd,) + tuple(f.new_states(Wd, opt, "f32"))
+    for t in range(1, wl.steps + 1):
+        X, dY = draw_layer_batch(wl.config, 0, t, spec)
+        Xd, dYd = P.dev_bf16(X), P.dev_bf16(dY)
+        g = gemm.wgrad_rows(f32_from_bf16_bits(X), f32_from_bf16_bits(dY), sel)
+        for opt in wl.optimizers:
+            Wd, m, v, ms, vs = runs[opt]
+            hp = optim.hyper(opt)
+            seed = (0x5EED0000 + wl.config) ^ optim.OPTIMIZERS.index(opt)
+            before = P.snapshot((Wd, m, v, ms, vs), sel)
+            f.wgrad_step(Xd, dYd, Wd, m, v, opt, _gh(hp), t, seed, ms, vs)
+            torch.cuda.synchronize()
+            after = P.snapshot((Wd, m, v, ms, vs), sel)
+            P.verify_step(opt, X, dY, before, after, hp, t, seed, "bf16", "f32", True, sel, g=g)
+        print(f"[ok] qwen mlp step {t}: all eight optimizers", flush=True)
+        del Xd, dYd

@@ -39,40 +39,15 @@ def run_case(spec, opt, steps, config=90, layer=0, state="f32", sr=True, rows=No
     Wd = P.dev_bf16(W0) if io == "bf16" else P.dev(W0)
     m, v, ms, vs = f.new_states(Wd, opt, state)
     sel = np.arange(spec.out) if rows is None else np.asarray(rows)
-    report = []
     for t in range(1, steps + 1):
         X, dY = draw_layer_batch(config, layer, t, spec)
         Xd = P.dev_bf16(X) if io == "bf16" else P.dev(X)
         dYd = P.dev_bf16(dY) if io == "bf16" else P.dev(dY)
-        W_b = P.host(Wd)[sel]
-        m_b = None if m is None else P.host(m)[sel]
-        v_b = None if v is None else P.host(v)[sel]
-        ms_b = None if ms is None else P.host(ms)[sel]
-        vs_b = None if vs is None else P.host(vs)[sel]
+        before = P.snapshot((Wd, m, v, ms, vs), sel)
         f.wgrad_step(Xd, dYd, Wd, m, v, opt, _gpu_hyper(hp, sr), t, seed, ms, vs)
         torch.cuda.synchronize()
-        ref = step.wgrad_step(opt, X, dY, W_b, m_b, v_b, hp, t, seed, io=io, state=state, sr=sr,
-                              rows=sel, m_scale=ms_b, v_scale=vs_b)
-        W_a = P.host(Wd)[sel]
-        if io == "bf16":
-            ok, n, mx = P.bf16_sr_ok(W_a, ref["W"])
-            assert ok, f"step {t}: {n} bf16 weights differ (max {mx} steps) of {W_a.size}"
-        else:
-            err = np.max(np.abs(W_a.astype(np.float64) - ref["theta"])) if W_a.size else 0.0
-            assert err <= 1e-3 * hp["lr"], f"step {t}: fp32 W error {err}"
-        for slot, t_gpu, t_scale in (("m", m, ms), ("v", v, vs)):
-            if t_gpu is None:
-                continue
-            got = P.host(t_gpu)[sel]
-            if state == "f32":
-                bad, worst = P.state_ok(got, ref[slot])
-                assert bad == 0, f"step {t}: {slot}: {bad} elements out of tolerance (worst {worst:.3g}x)"
-            else:
-                big, nd, mx = P.codes_ok(got, ref[slot])
-                assert big == 0, f"step {t}: {slot} codes: {big} off by more than one step"
-                bad, worst = P.state_ok(P.host(t_scale)[sel], ref[slot + "_scale"])
-                assert bad == 0, f"step {t}: {slot} scales: {bad} out of tolerance"
-        report.append(t)
+        after = P.snapshot((Wd, m, v, ms, vs), sel)
+        P.verify_step(opt, X, dY, before, after, hp, t, seed, io, state, sr, sel)
     return Wd, m, v
 
 

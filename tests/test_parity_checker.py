@@ -1,0 +1,66 @@
+"""CPU checks of the parity checker (tests/_parity.py) on planted differences.
+
+The "GPU" result here is the oracle's own output with a planted change, so the
+checker must accept exact results, accept a several-step change only where the
+update is ill-conditioned in the gradient (g ~ 0 under an adaptive optimizer),
+and reject the same change at an ordinary element or too many changed elements.
+"""
+import numpy as np
+
+from oracle import optim, step
+from synth import LayerSpec, draw_layer_batch, draw_layer_init
+from tests import _parity as P
+
+
+def _case(opt="nadam"):
+    spec = LayerSpec("c", 64, 128, 130)
+    W = draw_layer_init(92, 0, spec)
+    X, dY = draw_layer_batch(92, 0, 1, spec)
+    hp = optim.hyper(opt)
+    z = np.zeros(W.shape, np.float32)
+    ref = step.wgrad_step(opt, X, dY, W, z, z, hp, 1, 77)
+    return spec, W, X, dY, hp, z, ref
+
+
+def _shift(bits, steps):
+    o = P._ordered(np.array([bits]))[0] + steps
+    return np.uint16((0x8000 | (-o)) if o < 0 else o)
+
+
+def test_exact_result_passes():
+    spec, W, X, dY, hp, z, ref = _case()
+    ok, n, unexp, _ = P.bf16_step_explained(ref["W"].copy(), ref, "nadam", X, dY, W, z, z, hp, 1, 77, "bf16", "f32",
+                                            np.arange(spec.out))
+    assert ok and n == 0
+
+
+def test_ill_conditioned_element_is_explained_ordinary_is_not():
+    spec, W, X, dY, hp, z, ref = _case()
+    # g[5, 3] = sum of +-0.01 * 1.0 over 130 tokens = 0 exactly, while sum |terms| = 1.3: the
+    # FP32 summation bound (~1e-5) dwarfs eps, so NAdam's g / (|g| + eps) can land anywhere.
+    X2, dY2 = X.copy(), dY.copy()
+    X2[:, 3] = 0x3F80                      # bf16 1.0
+    dY2[:, 5] = np.where(np.arange(130) % 2 == 0, 0x3C24, 0xBC24)  # bf16 +-0.01
+    X, dY = X2, dY2
+    ref2 = step.wgrad_step("nadam", X, dY2, W, z, z, hp, 1, 77)
+    assert ref2["g"][5, 3] == 0.0
+    sel = np.arange(spec.out)
+    gpu = ref2["W"].copy()
+    i_ill = 3
+    gpu[5, i_ill] = _shift(gpu[5, i_ill], 3)
+    ok, n, unexp, _ = P.bf16_step_explained(gpu, ref2, "nadam", X, dY2, W, z, z, hp, 1, 77, "bf16", "f32", sel)
+    assert n == 1 and unexp == 0 and ok
+    gpu = ref2["W"].copy()
+    gpu[10, 7] = _shift(gpu[10, 7], 3)
+    ok, n, unexp, _ = P.bf16_step_explained(gpu, ref2, "nadam", X, dY2, W, z, z, hp, 1, 77, "bf16", "f32", sel)
+    assert n == 1 and unexp == 1 and not ok
+
+
+def test_too_many_boundary_flips_fail():
+    spec, W, X, dY, hp, z, ref = _case("sgd")
+    gpu = ref["W"].copy()
+    for k in range(3):  # 3 > max(1, 1e-4 * 8192) changed elements
+        gpu[k, k] = _shift(gpu[k, k], 1)
+    ok, n, _, _ = P.bf16_step_explained(gpu, ref, "sgd", X, dY, W, None, None, hp, 1, 77, "bf16", "f32",
+                                        np.arange(spec.out))
+    assert n == 3 and not ok
