@@ -113,6 +113,9 @@ def describe(t: Optional[torch.Tensor], scale: Optional[torch.Tensor] = None, *,
         raise ValueError("forge kernels take device tensors")
     if t.dtype not in _DT:
         raise ValueError(f"unsupported dtype {t.dtype}")
+    if t.numel() == 0:
+        return ForgeTensor(None, _DT[t.dtype], 0, t.shape[0], t.shape[1], t.shape[1],
+                           scale.data_ptr() if scale is not None and scale.numel() else None)
     if t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError("rows must be contiguous (stride(1) == 1)")
     ld = t.stride(0) if t.shape[0] > 1 else max(t.shape[1], t.stride(0))

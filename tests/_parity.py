@@ -13,7 +13,10 @@ Tolerances (float point; integer/bit results are exact unless stated):
     more than one step; everywhere else it reduces to "one step at a rounding boundary".
   * INT8 codes: within one quantisation step; scales as fp32 moments.
   * dgrad bf16 output: within one bfloat16 ulp of the float64 value, the ulp taken at
-    max(|ref|, 0.01 * rms(ref)); fp32 output: 1e-5 relative with the same kind of floor.
+    max(|ref|, 0.01 * rms(ref)).
+  * fp32 GEMM outputs (fp32 dgrad, the baseline's stored dW): the a-priori bound of
+    floating-point summation in any order, |gpu - ref| <= K * 2^-24 * sum_k |a_k b_k|
+    per element (K = length of the contraction).
 """
 from __future__ import annotations
 
@@ -73,6 +76,13 @@ def dgrad_bf16_ok(gpu_bits: np.ndarray, ref64: np.ndarray):
     ulp = 2.0 ** (np.floor(np.log2(np.maximum(mag, 1e-300))) - 7)
     err = np.abs(g - ref64)
     return int(np.count_nonzero(err > ulp)), float(np.max(err / ulp)) if err.size else 0.0
+
+
+def summation_bound_ok(gpu: np.ndarray, ref: np.ndarray, abs_sum: np.ndarray, K: int):
+    """(n_bad, worst ratio) for |gpu - ref| <= K * 2^-24 * abs_sum elementwise."""
+    bound = K * 2.0 ** -24 * np.asarray(abs_sum, dtype=np.float64)
+    err = np.abs(np.asarray(gpu, dtype=np.float64) - ref)
+    return int(np.count_nonzero(err > bound)), float(np.max(err / np.maximum(bound, 1e-300))) if err.size else 0.0
 
 
 def codes_ok(gpu: np.ndarray, ref: np.ndarray):
