@@ -17,7 +17,9 @@
  *   - W and the moments are [out, in]; X is [T, in]; dY is [T, out]; dX is [T, in].
  *   - `ld` is the row pitch in elements (ld >= cols). Data pointers must be
  *     16-byte aligned; cols and ld must be multiples of 8 (bf16) or 4 (fp32).
- *     A tensor with no elements may have a NULL data pointer.
+ *     A tensor with no elements may have a NULL data pointer. Every tensor must
+ *     span less than 2^31 bytes (rows * ld * element size); larger ones are
+ *     rejected with FORGE_ERR_UNSUPPORTED.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *     null stream). No entry point synchronises the host.
  *   - Arguments are validated on the host before anything is enqueued; on an

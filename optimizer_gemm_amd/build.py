@@ -20,7 +20,7 @@ LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libforge.so")
 ARCH = os.environ.get("FORGE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["forge_wgrad.hip", "forge_dgrad.hip", "forge_api.hip"]
+SOURCES = ["forge_gemm.hip", "forge_wgrad.hip", "forge_dgrad.hip", "forge_api.hip"]
 
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -47,6 +47,11 @@ int check_io(const forge_tensor* t, int dtype) {
 
 bool finite(double x) { return isfinite(x) != 0; }
 
+// The kernels address each tensor through 32-bit byte offsets below 2^31.
+bool fits_31(const forge_tensor* t) {
+  return !t || !t->data || t->rows * t->ld * (int64_t)elem_size(t->dtype) < ((int64_t)1 << 31);
+}
+
 int check_hyper(int opt, const forge_hyper* h, int64_t step) {
   if (!h) return FORGE_ERR_NULL;
   if (opt < FORGE_ADAMW || opt > FORGE_RADAM) return FORGE_ERR_HYPER;
@@ -283,6 +288,8 @@ int forge_linear_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge
   if (fmt < 0) return fmt;
   if (W->rows * W->cols >= ((int64_t)1 << 32)) return FORGE_ERR_UNSUPPORTED;
   const int sl = opt_slots(opt);
+  if (!fits_31(X) || !fits_31(dY) || !fits_31(W) || ((sl & 1) && !fits_31(m)) || ((sl & 2) && !fits_31(v)))
+    return FORGE_ERR_UNSUPPORTED;
   const forge_tensor* outs[3] = {W, (sl & 1) ? m : nullptr, (sl & 2) ? v : nullptr};
   const forge_tensor* ins[2] = {X, dY};
   if ((r = check_alias(outs, 3, ins, 2))) return r;
@@ -304,6 +311,7 @@ int forge_linear_dgrad(const forge_tensor* dY, const forge_tensor* W, forge_tens
   int r;
   if ((r = check_io(dY, io)) || (r = check_io(W, io)) || (r = check_io(dX, io))) return r;
   if (dY->cols != W->rows || dX->rows != dY->rows || dX->cols != W->cols) return FORGE_ERR_SHAPE;
+  if (!fits_31(dY) || !fits_31(W) || !fits_31(dX)) return FORGE_ERR_UNSUPPORTED;
   const forge_tensor* outs[1] = {dX};
   const forge_tensor* ins[2] = {dY, W};
   if ((r = check_alias(outs, 1, ins, 2))) return r;
@@ -324,6 +332,7 @@ int forge_linear_wgrad(const forge_tensor* X, const forge_tensor* dY, float* dW,
   if (ld_dw < X->cols) return FORGE_ERR_SHAPE;
   if (!aligned16(dW) || ld_dw % 4) return FORGE_ERR_ALIGN;
   const forge_tensor dWt{dW, FORGE_F32, 0, dY->cols, X->cols, ld_dw, nullptr};
+  if (!fits_31(X) || !fits_31(dY) || !fits_31(&dWt)) return FORGE_ERR_UNSUPPORTED;
   const forge_tensor* outs[1] = {&dWt};
   const forge_tensor* ins[2] = {X, dY};
   if ((r = check_alias(outs, 1, ins, 2))) return r;

@@ -1,28 +1,15 @@
-// Input gradient dX = dY W of a linear layer (FORGE explainer, §5 limitations:
-// the input gradient must be read from the old weights, before the update), and
-// the stand-alone element-wise optimizer pass of the two-phase baseline (§1).
+// float32 input gradient dX = dY W of a linear layer (FORGE explainer, §5
+// limitations: the input gradient is read from the old weights, before the
+// update; the bfloat16 kernel lives in forge_gemm.hip), and the stand-alone
+// element-wise optimizer pass of the two-phase baseline (§1).
 //
-// dgrad mapping on gfx950: the MFMA computes C[m = i][n = t] = sum_o W[o][i] dY[t][o],
-// i.e. dX^T tiles, so a lane's four accumulator rows are four consecutive
-// columns of one dX row (one 8- or 16-byte store). W is staged in LDS as it
-// sits in memory (rows of `out`, contiguous along `in`) and read K-major with
-// the LDS transpose read; dY rows are already contiguous along the contraction
-// index and are read with plain 16-byte LDS reads from a padded layout.
+// dgrad mapping: the MFMA (v_mfma_f32_16x16x4_f32) computes
+// C[m = i][n = t] = sum_o W[o][i] dY[t][o], i.e. dX^T tiles, so a lane's four
+// accumulator rows are four consecutive columns of one dX row. W rows and dY
+// rows are staged in LDS as they sit in memory (padded rows) and read directly.
 #include "forge_internal.h"
 
 namespace forge {
-
-__device__ __forceinline__ int dswz(int row) { return (row & 3) | ((row >> 1) & 4); }
-
-__device__ __forceinline__ bf16x4 lds_read_tr_d(const uint16_t* p) {
-  typedef __bf16 v4bf_t __attribute__((__vector_size__(8)));
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Wold-style-cast"
-  auto lp = (__attribute__((address_space(3))) v4bf_t*)(const_cast<uint16_t*>(p));
-#pragma clang diagnostic pop
-  v4bf_t r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp);
-  return __builtin_bit_cast(bf16x4, r);
-}
 
 // BM (in) x BN (tokens) output tile, BK (out) per stage, WM x WN waves.
 template <int BM_, int BN_, int BK_, int WM_, int WN_>
@@ -32,15 +19,15 @@ struct DCfg {
   static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
 };
 
-template <class C, bool BF16>
-__global__ __launch_bounds__(C::NT) void dgrad_kernel(const void* __restrict__ dYp, int64_t lddy,
+template <class C>
+__global__ __launch_bounds__(C::NT) void dgrad_f32_kernel(const void* __restrict__ dYp, int64_t lddy,
                                                       const void* __restrict__ Wp, int64_t ldw,
                                                       void* __restrict__ dXp, int64_t lddx, int T, int n_out,
                                                       int n_in) {
-  constexpr int ES = BF16 ? 2 : 4;               // element size
+  constexpr int ES = 4;                          // element size
   constexpr int VE = 16 / ES;                    // elements per 16-byte chunk
-  constexpr int LA = BF16 ? C::BM : C::BM + 16;  // W stage row pitch (elements)
-  constexpr int LB = C::BK + (BF16 ? 8 : 4);     // dY stage row pitch (elements), padded
+  constexpr int LA = C::BM + 16;                 // W stage row pitch (elements)
+  constexpr int LB = C::BK + 4;                  // dY stage row pitch (elements), padded
   constexpr int STAGE = (C::BK * LA + C::BN * LB) * ES;
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
@@ -95,13 +82,7 @@ __global__ __launch_bounds__(C::NT) void dgrad_kernel(const void* __restrict__ d
       const int c = tid + j * C::NT;
       if (CA % C::NT == 0 || c < CA) {
         const int row = c / (C::BM / VE), cc = c % (C::BM / VE);
-        int off;
-        if constexpr (BF16) {
-          const int grp = (cc >> 1) ^ (dswz(row) & (C::BM / 16 - 1));
-          off = row * LA + grp * 16 + (cc & 1) * 8;
-        } else {
-          off = row * LA + cc * 4;
-        }
+        const int off = row * LA + cc * 4;
         *reinterpret_cast<u32x4*>(As(buf) + off * ES) = ra[j];
       }
     }
@@ -125,32 +106,7 @@ __global__ __launch_bounds__(C::NT) void dgrad_kernel(const void* __restrict__ d
   for (int s = 0; s < nstages; ++s) {
     const int buf = s & 1;
     if (s + 1 < nstages) gload(s + 1);
-    if constexpr (BF16) {
-      const uint16_t* A = reinterpret_cast<const uint16_t*>(As(buf));
-      const uint16_t* B = reinterpret_cast<const uint16_t*>(Bs(buf));
-#pragma unroll
-      for (int kk = 0; kk < C::BK / 32; ++kk) {
-        const int k0 = kk * 32 + 8 * g16 + r4, k1 = k0 + 4;
-        bf16x8 af[C::FM], bfr[C::FN];
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) {
-          const int grp = (wave_m0 >> 4) + fm;
-          bf16x4 lo = lds_read_tr_d(A + k0 * LA + ((grp ^ (dswz(k0) & (C::BM / 16 - 1))) << 4) + 4 * c4);
-          bf16x4 hi = lds_read_tr_d(A + k1 * LA + ((grp ^ (dswz(k1) & (C::BM / 16 - 1))) << 4) + 4 * c4);
-          af[fm] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-#pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) {
-          const int row = wave_n0 + 16 * fn + l16;
-          bfr[fn] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(B + row * LB + kk * 32 + 8 * g16));
-        }
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn)
-            acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
-      }
-    } else {
+    {
       const float* A = reinterpret_cast<const float*>(As(buf));
       const float* B = reinterpret_cast<const float*>(Bs(buf));
 #pragma unroll
@@ -180,38 +136,22 @@ __global__ __launch_bounds__(C::NT) void dgrad_kernel(const void* __restrict__ d
     for (int fm = 0; fm < C::FM; ++fm) {
       const int i = i0 + wave_m0 + 16 * fm + 4 * g16;
       if (t < T && i < n_in) {
-        const f32x4 c = acc[fm][fn];
-        if constexpr (BF16) {
-          u32x2 r;
-          r.x = rne_bf16_bits(c.x) | (rne_bf16_bits(c.y) << 16);
-          r.y = rne_bf16_bits(c.z) | (rne_bf16_bits(c.w) << 16);
-          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(dXp) + (int64_t)t * lddx + i) = r;
-        } else {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dXp) + (int64_t)t * lddx + i) = c;
-        }
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dXp) + (int64_t)t * lddx + i) = acc[fm][fn];
       }
     }
   }
 }
 
-using DCfgBF16 = DCfg<128, 128, 64, 2, 2>;
 using DCfgF32 = DCfg<64, 64, 16, 2, 2>;
 
 hipError_t launch_dgrad(int io_bf16, const void* dY, int64_t lddy, const void* W, int64_t ldw, void* dX,
                         int64_t lddx, int32_t T, int32_t n_out, int32_t n_in, hipStream_t stream) {
-  if (io_bf16) {
-    using C = DCfgBF16;
-    const int tiles = ((n_in + C::BM - 1) / C::BM) * ((T + C::BN - 1) / C::BN);
-    if (tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL((dgrad_kernel<C, true>), dim3(tiles), dim3(C::NT), 0, stream, dY, lddy, W, ldw, dX, lddx, T,
-                       n_out, n_in);
-  } else {
-    using C = DCfgF32;
-    const int tiles = ((n_in + C::BM - 1) / C::BM) * ((T + C::BN - 1) / C::BN);
-    if (tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL((dgrad_kernel<C, false>), dim3(tiles), dim3(C::NT), 0, stream, dY, lddy, W, ldw, dX, lddx, T,
-                       n_out, n_in);
-  }
+  if (io_bf16) return launch_dgrad_bf16(dY, lddy, W, ldw, dX, lddx, T, n_out, n_in, stream);
+  using C = DCfgF32;
+  const int tiles = ((n_in + C::BM - 1) / C::BM) * ((T + C::BN - 1) / C::BN);
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((dgrad_f32_kernel<C>), dim3(tiles), dim3(C::NT), 0, stream, dY, lddy, W, ldw, dX, lddx, T,
+                     n_out, n_in);
   return hipGetLastError();
 }
 

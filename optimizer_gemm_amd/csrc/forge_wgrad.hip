@@ -1,18 +1,16 @@
-// Weight-gradient GEMM dW = dY^T X over tokens, tile by tile, with either the
+// float32 weight-gradient GEMM dW = dY^T X over tokens, tile by tile, with the
 // fused optimizer epilogue (FORGE, §2 Method, "Core mechanism": accumulate the
-// tile in FP32 registers, update it in registers, discard it, write back only
-// W and the moments) or a plain float32 dW store (the two-phase baseline of §1).
+// tile in FP32 registers, update it in registers, write back only W and the
+// moments) or a plain float32 dW store (the two-phase baseline of §1). The
+// bfloat16 path lives in forge_gemm.hip; this kernel serves float32 layers.
 //
-// gfx950 mapping. A workgroup owns a BM x BN tile of dW^T (BM along `in`, BN
-// along `out`); its waves form a WM x WN grid of wave tiles, replicated KS times
-// for an in-workgroup split of the token range (reduced through LDS at the end,
-// never through device memory). Tokens are the contraction index and are the
-// slow index of both X [T, in] and dY [T, out], so both operands are staged in
-// LDS exactly as they sit in memory (rows of tokens, coalesced 16-byte loads)
-// and turned K-major on the way to the matrix cores by the LDS transpose read
-// ds_read_b64_tr_b16. The MFMA computes C[m = i][n = o], so each lane's four
-// accumulator rows are four consecutive `in` columns of one W row, which makes
-// the epilogue's W/m/v accesses 8- and 16-byte vectors.
+// Mapping: a workgroup owns a BM x BN tile of dW^T (BM along `in`, BN along
+// `out`) with WM x WN wave tiles, replicated KS times to split the token range
+// inside the workgroup (partial tiles are summed through LDS, never through
+// device memory). v_mfma_f32_16x16x4_f32 reads one float per lane per operand,
+// so X and dY token rows are staged in LDS as they sit in memory (padded rows)
+// and read directly; the accumulator layout gives each lane four consecutive
+// `in` elements of one W row.
 #include "forge_internal.h"
 
 namespace forge {
@@ -69,10 +67,10 @@ __device__ __forceinline__ void tile_coords(int tiles_o, int tiles_i, int& bo, i
 // Epilogue kinds.
 enum { EPI_STORE = 0, EPI_OPT = 1 };
 
-template <class C, bool BF16>
+template <class C>
 struct Smem {
-  static constexpr int PADF = 16;  // fp32 staging row pad (floats)
-  static constexpr int STAGE_BYTES = BF16 ? C::BK * (C::BM + C::BN) * 2 : C::BK * (C::BM + C::BN + 2 * PADF) * 4;
+  static constexpr int PADF = 16;  // staging row pad (floats)
+  static constexpr int STAGE_BYTES = C::BK * (C::BM + C::BN + 2 * PADF) * 4;
   static constexpr int RED_BYTES = (C::KS - 1) * C::BM * C::BN * 4;
   static constexpr int BYTES = (2 * STAGE_BYTES > RED_BYTES) ? 2 * STAGE_BYTES : RED_BYTES;
 };
@@ -80,11 +78,11 @@ struct Smem {
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
-template <class C, bool BF16, int EPI, int OPT, bool Q8, bool SR>
-__global__ __launch_bounds__(C::NT) void wgrad_kernel(const void* __restrict__ Xp, const void* __restrict__ dYp,
-                                                      GemmDims d, OptArgs a, float* __restrict__ dW,
-                                                      int64_t ld_dw) {
-  using S = Smem<C, BF16>;
+template <class C, int EPI, int OPT>
+__global__ __launch_bounds__(C::NT) void wgrad_f32_kernel(const void* __restrict__ Xp, const void* __restrict__ dYp,
+                                                          GemmDims d, OptArgs a, float* __restrict__ dW,
+                                                          int64_t ld_dw) {
+  using S = Smem<C>;
   __shared__ __attribute__((aligned(16))) char smem[S::BYTES];
 
   const int tid = threadIdx.x;
@@ -110,100 +108,7 @@ __global__ __launch_bounds__(C::NT) void wgrad_kernel(const void* __restrict__ X
 
   const int nstages = (d.T + C::BK - 1) / C::BK;
 
-  if constexpr (BF16) {
-    // ---------------- bf16 mainloop ----------------
-    constexpr int CA = C::BK * C::BM / 8;  // 16-byte chunks per stage of X
-    constexpr int CB = C::BK * C::BN / 8;
-    constexpr int PA = (CA + C::NT - 1) / C::NT;
-    constexpr int PB = (CB + C::NT - 1) / C::NT;
-    const uint16_t* X = reinterpret_cast<const uint16_t*>(Xp);
-    const uint16_t* dY = reinterpret_cast<const uint16_t*>(dYp);
-    auto As = [&](int buf) { return reinterpret_cast<uint16_t*>(smem) + buf * (C::BK * (C::BM + C::BN)); };
-    auto Bs = [&](int buf) { return As(buf) + C::BK * C::BM; };
-
-    u32x4 ra[PA], rb[PB];
-    auto gload = [&](int s) {
-      const int t0 = s * C::BK;
-#pragma unroll
-      for (int j = 0; j < PA; ++j) {
-        const int c = tid + j * C::NT;
-        const int row = c / (C::BM / 8), col = (c % (C::BM / 8)) * 8;
-        const int t = t0 + row, i = i0 + col;
-        ra[j] = u32x4{0u, 0u, 0u, 0u};
-        if ((CA % C::NT == 0 || c < CA) && t < d.T && i < d.in)
-          ra[j] = *reinterpret_cast<const u32x4*>(X + (int64_t)t * d.ldx + i);
-      }
-#pragma unroll
-      for (int j = 0; j < PB; ++j) {
-        const int c = tid + j * C::NT;
-        const int row = c / (C::BN / 8), col = (c % (C::BN / 8)) * 8;
-        const int t = t0 + row, o = o0 + col;
-        rb[j] = u32x4{0u, 0u, 0u, 0u};
-        if ((CB % C::NT == 0 || c < CB) && t < d.T && o < d.out)
-          rb[j] = *reinterpret_cast<const u32x4*>(dY + (int64_t)t * d.lddy + o);
-      }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-      for (int j = 0; j < PA; ++j) {
-        const int c = tid + j * C::NT;
-        if (CA % C::NT == 0 || c < CA) {
-          const int row = c / (C::BM / 8), c8 = c % (C::BM / 8);
-          const int grp = (c8 >> 1) ^ (swz(row) & (C::BM / 16 - 1));
-          *reinterpret_cast<u32x4*>(As(buf) + row * C::BM + grp * 16 + (c8 & 1) * 8) = ra[j];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < PB; ++j) {
-        const int c = tid + j * C::NT;
-        if (CB % C::NT == 0 || c < CB) {
-          const int row = c / (C::BN / 8), c8 = c % (C::BN / 8);
-          const int grp = (c8 >> 1) ^ (swz(row) & (C::BN / 16 - 1));
-          *reinterpret_cast<u32x4*>(Bs(buf) + row * C::BN + grp * 16 + (c8 & 1) * 8) = rb[j];
-        }
-      }
-    };
-
-    if (nstages > 0) {
-      gload(0);
-      sstore(0);
-    }
-    __syncthreads();
-    const int r4 = l16 >> 2, c4 = l16 & 3;
-    for (int s = 0; s < nstages; ++s) {
-      const int buf = s & 1;
-      if (s + 1 < nstages) gload(s + 1);
-      const uint16_t* A = As(buf);
-      const uint16_t* B = Bs(buf);
-#pragma unroll
-      for (int kk = 0; kk < C::BKG / 32; ++kk) {
-        const int k0 = kg * C::BKG + kk * 32 + 8 * g16 + r4;
-        const int k1 = k0 + 4;
-        bf16x8 af[C::FM], bfr[C::FN];
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) {
-          const int grp = (wave_m0 >> 4) + fm;
-          bf16x4 lo = lds_read_tr(A + k0 * C::BM + ((grp ^ (swz(k0) & (C::BM / 16 - 1))) << 4) + 4 * c4);
-          bf16x4 hi = lds_read_tr(A + k1 * C::BM + ((grp ^ (swz(k1) & (C::BM / 16 - 1))) << 4) + 4 * c4);
-          af[fm] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-#pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) {
-          const int grp = (wave_n0 >> 4) + fn;
-          bf16x4 lo = lds_read_tr(B + k0 * C::BN + ((grp ^ (swz(k0) & (C::BN / 16 - 1))) << 4) + 4 * c4);
-          bf16x4 hi = lds_read_tr(B + k1 * C::BN + ((grp ^ (swz(k1) & (C::BN / 16 - 1))) << 4) + 4 * c4);
-          bfr[fn] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn)
-            acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
-      }
-      if (s + 1 < nstages) sstore(buf ^ 1);
-      __syncthreads();
-    }
-  } else {
+  {
     // ---------------- fp32 mainloop ----------------
     constexpr int PADF = S::PADF;
     constexpr int LA = C::BM + PADF, LB = C::BN + PADF;
@@ -278,6 +183,7 @@ __global__ __launch_bounds__(C::NT) void wgrad_kernel(const void* __restrict__ X
       if (s + 1 < nstages) sstore(buf ^ 1);
       __syncthreads();
     }
+
   }
 
   // ---------------- in-workgroup split-K reduction through LDS ----------------
@@ -328,123 +234,61 @@ __global__ __launch_bounds__(C::NT) void wgrad_kernel(const void* __restrict__ X
       if (fn / FNO != kg) continue;
       const int o = o_base + 16 * fn;
       const bool ov = o < d.out;
-      if constexpr (!Q8) {
 #pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) {
-          const int i = i_base + 16 * fm;
-          if (!(ov && i < d.in)) continue;
-          float w[4], m[4] = {0.f, 0.f, 0.f, 0.f}, v[4] = {0.f, 0.f, 0.f, 0.f};
-          load_w4<BF16>(a, o, i, w);
-          if constexpr (HAS_M) load_f4(a.m, a.ldm, o, i, m);
-          if constexpr (HAS_V) load_f4(a.v, a.ldv, o, i, v);
-          const float g[4] = {acc[fm][fn].x, acc[fm][fn].y, acc[fm][fn].z, acc[fm][fn].w};
+      for (int fm = 0; fm < C::FM; ++fm) {
+        const int i = i_base + 16 * fm;
+        if (!(ov && i < d.in)) continue;
+        float w[4], m[4] = {0.f, 0.f, 0.f, 0.f}, v[4] = {0.f, 0.f, 0.f, 0.f};
+        load_w4<false>(a, o, i, w);
+        if constexpr (HAS_M) load_f4(a.m, a.ldm, o, i, m);
+        if constexpr (HAS_V) load_f4(a.v, a.ldv, o, i, v);
+        const float g[4] = {acc[fm][fn].x, acc[fm][fn].y, acc[fm][fn].z, acc[fm][fn].w};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) opt_apply<OPT>(g[j], w[j], m[j], v[j], a.s);
-          store_w4<BF16, SR>(a, o, i, w);
-          if constexpr (HAS_M) store_f4(a.m, a.ldm, o, i, m);
-          if constexpr (HAS_V) store_f4(a.v, a.ldv, o, i, v);
-        }
-      } else {
-        // INT8 block-64 states: a wave tile is 64 wide along `in`, so the 16 values
-        // of this lane and those of lanes ^16, ^32, ^48 form one block of row o.
-        static_assert(C::TM == 64, "INT8 states need 64-wide wave tiles");
-        float mq[C::FM][4], vq[C::FM][4];
-        float mmax = 0.f, vmax = 0.f;
-        const bool blk_ok = ov && (i0 + wave_m0) < d.in;
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) {
-          const int i = i_base + 16 * fm;
-          float w[4], m[4] = {0.f, 0.f, 0.f, 0.f}, v[4] = {0.f, 0.f, 0.f, 0.f};
-          if (blk_ok) {
-            load_w4<BF16>(a, o, i, w);
-            if constexpr (HAS_M) dequant_m4(a, o, i, m);
-            if constexpr (HAS_V) dequant_v4(a, o, i, v);
-            const float g[4] = {acc[fm][fn].x, acc[fm][fn].y, acc[fm][fn].z, acc[fm][fn].w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) opt_apply<OPT>(g[j], w[j], m[j], v[j], a.s);
-            store_w4<BF16, SR>(a, o, i, w);
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            mq[fm][j] = m[j];
-            vq[fm][j] = sqrtf(v[j]);
-            mmax = fmaxf(mmax, fabsf(m[j]));
-            vmax = fmaxf(vmax, vq[fm][j]);
-          }
-        }
-        mmax = fmaxf(mmax, __shfl_xor(mmax, 16));
-        mmax = fmaxf(mmax, __shfl_xor(mmax, 32));
-        vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
-        vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
-        const float sm = mmax / 127.f, sv = vmax / 255.f;
-        if (blk_ok) {
-#pragma unroll
-          for (int fm = 0; fm < C::FM; ++fm) {
-            const int i = i_base + 16 * fm;
-            if constexpr (HAS_M)
-              *reinterpret_cast<uint32_t*>(reinterpret_cast<int8_t*>(a.m) + (int64_t)o * a.ldm + i) = quant_m4(mq[fm], sm);
-            if constexpr (HAS_V)
-              *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.v) + (int64_t)o * a.ldv + i) = quant_v4(vq[fm], sv);
-          }
-          if (g16 == 0) {
-            const int64_t si = (int64_t)o * (a.in >> 6) + ((i0 + wave_m0) >> 6);
-            if constexpr (HAS_M) a.m_scale[si] = sm;
-            if constexpr (HAS_V) a.v_scale[si] = sv;
-          }
-        }
+        for (int j = 0; j < 4; ++j) opt_apply<OPT>(g[j], w[j], m[j], v[j], a.s);
+        store_w4<false, false>(a, o, i, w);
+        if constexpr (HAS_M) store_f4(a.m, a.ldm, o, i, m);
+        if constexpr (HAS_V) store_f4(a.v, a.ldv, o, i, v);
       }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Launchers.
+// Launchers (float32; bfloat16 goes to forge_gemm.hip).
 // ---------------------------------------------------------------------------
-using CfgBF16 = TileCfg<128, 128, 32, 2, 2, 2>;  // 8 waves: 2x2 wave tiles of 64x64, 2-way token split
-using CfgF32 = TileCfg<64, 64, 16, 2, 2, 2>;     // 8 waves: 2x2 wave tiles of 32x32, 2-way token split
+using CfgF32 = TileCfg<64, 64, 16, 2, 2, 2>;  // 8 waves: 2x2 wave tiles of 32x32, 2-way token split
 
-template <class C, bool BF16, int EPI, int OPT, bool Q8, bool SR>
-static hipError_t launch_one(const void* X, const void* dY, const GemmDims& d, const OptArgs& a, float* dW,
+template <int EPI, int OPT>
+static hipError_t launch_f32(const void* X, const void* dY, const GemmDims& d, const OptArgs& a, float* dW,
                              int64_t ld_dw, hipStream_t stream) {
+  using C = CfgF32;
   const int tiles = ((d.out + C::BN - 1) / C::BN) * ((d.in + C::BM - 1) / C::BM);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((wgrad_kernel<C, BF16, EPI, OPT, Q8, SR>), dim3(tiles), dim3(C::NT), 0, stream, X, dY, d, a,
-                     dW, ld_dw);
+  hipLaunchKernelGGL((wgrad_f32_kernel<C, EPI, OPT>), dim3(tiles), dim3(C::NT), 0, stream, X, dY, d, a, dW, ld_dw);
   return hipGetLastError();
-}
-
-template <int OPT>
-static hipError_t launch_fused_opt(int io_bf16, int q8, int sr, const void* X, const void* dY, const GemmDims& d,
-                                   const OptArgs& a, hipStream_t st) {
-  if (!io_bf16) return launch_one<CfgF32, false, EPI_OPT, OPT, false, false>(X, dY, d, a, nullptr, 0, st);
-  if (q8) {
-    if (sr) return launch_one<CfgBF16, true, EPI_OPT, OPT, true, true>(X, dY, d, a, nullptr, 0, st);
-    return launch_one<CfgBF16, true, EPI_OPT, OPT, true, false>(X, dY, d, a, nullptr, 0, st);
-  }
-  if (sr) return launch_one<CfgBF16, true, EPI_OPT, OPT, false, true>(X, dY, d, a, nullptr, 0, st);
-  return launch_one<CfgBF16, true, EPI_OPT, OPT, false, false>(X, dY, d, a, nullptr, 0, st);
 }
 
 hipError_t launch_wgrad_fused(int io_bf16, int state_q8, int opt, int sr, const void* X, const void* dY,
                               const GemmDims& d, const OptArgs& a, hipStream_t stream) {
+  if (io_bf16) return launch_wgrad_fused_bf16(state_q8, opt, sr, X, dY, d, a, stream);
   switch (opt) {
-    case FORGE_ADAMW: return launch_fused_opt<FORGE_ADAMW>(io_bf16, state_q8, sr, X, dY, d, a, stream);
-    case FORGE_SGD: return launch_fused_opt<FORGE_SGD>(io_bf16, state_q8, sr, X, dY, d, a, stream);
-    case FORGE_SGD_MOMENTUM: return launch_fused_opt<FORGE_SGD_MOMENTUM>(io_bf16, state_q8, sr, X, dY, d, a, stream);
-    case FORGE_LION: return launch_fused_opt<FORGE_LION>(io_bf16, state_q8, sr, X, dY, d, a, stream);
-    case FORGE_RMSPROP: return launch_fused_opt<FORGE_RMSPROP>(io_bf16, state_q8, sr, X, dY, d, a, stream);
-    case FORGE_ADAGRAD: return launch_fused_opt<FORGE_ADAGRAD>(io_bf16, state_q8, sr, X, dY, d, a, stream);
-    case FORGE_NADAM: return launch_fused_opt<FORGE_NADAM>(io_bf16, state_q8, sr, X, dY, d, a, stream);
-    case FORGE_RADAM: return launch_fused_opt<FORGE_RADAM>(io_bf16, state_q8, sr, X, dY, d, a, stream);
+    case FORGE_ADAMW: return launch_f32<EPI_OPT, FORGE_ADAMW>(X, dY, d, a, nullptr, 0, stream);
+    case FORGE_SGD: return launch_f32<EPI_OPT, FORGE_SGD>(X, dY, d, a, nullptr, 0, stream);
+    case FORGE_SGD_MOMENTUM: return launch_f32<EPI_OPT, FORGE_SGD_MOMENTUM>(X, dY, d, a, nullptr, 0, stream);
+    case FORGE_LION: return launch_f32<EPI_OPT, FORGE_LION>(X, dY, d, a, nullptr, 0, stream);
+    case FORGE_RMSPROP: return launch_f32<EPI_OPT, FORGE_RMSPROP>(X, dY, d, a, nullptr, 0, stream);
+    case FORGE_ADAGRAD: return launch_f32<EPI_OPT, FORGE_ADAGRAD>(X, dY, d, a, nullptr, 0, stream);
+    case FORGE_NADAM: return launch_f32<EPI_OPT, FORGE_NADAM>(X, dY, d, a, nullptr, 0, stream);
+    case FORGE_RADAM: return launch_f32<EPI_OPT, FORGE_RADAM>(X, dY, d, a, nullptr, 0, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_wgrad_store(int io_bf16, const void* X, const void* dY, const GemmDims& d, float* dW,
                               int64_t ld_dw, hipStream_t stream) {
+  if (io_bf16) return launch_wgrad_store_bf16(X, dY, d, dW, ld_dw, stream);
   OptArgs a{};
-  if (io_bf16) return launch_one<CfgBF16, true, EPI_STORE, FORGE_SGD, false, false>(X, dY, d, a, dW, ld_dw, stream);
-  return launch_one<CfgF32, false, EPI_STORE, FORGE_SGD, false, false>(X, dY, d, a, dW, ld_dw, stream);
+  return launch_f32<EPI_STORE, FORGE_SGD>(X, dY, d, a, dW, ld_dw, stream);
 }
 
 }  // namespace forge
