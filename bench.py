@@ -35,7 +35,7 @@ HBM_GBS = 8000.0
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in ("forge_internal.h", "forge_wgrad.hip"):
+    for name in ("forge_internal.h", "forge_gemm.hip", "forge_wgrad.hip"):
         with open(os.path.join(ROOT, "optimizer_gemm_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -58,10 +58,11 @@ struct GCfg {
   static constexpr int A_ELEMS = BK * LDA;
   static constexpr int B_ELEMS = B_TR ? BK * LDB : BN * LDB;
   static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
-  // LDS: two operand stages, reused after the mainloop for one TN-row chunk of the
-  // finished tile as float rows of BM + 4.
+  // LDS: a ring of three operand stages, reused after the mainloop for one TN-row
+  // chunk of the finished tile as float rows of BM + 4.
+  static constexpr int NSTAGE = 3;
   static constexpr int EPI_ELEMS = TN * (BM + 4) * 2;
-  static constexpr int SMEM_ELEMS = 2 * STAGE_ELEMS > EPI_ELEMS ? 2 * STAGE_ELEMS : EPI_ELEMS;
+  static constexpr int SMEM_ELEMS = NSTAGE * STAGE_ELEMS > EPI_ELEMS ? NSTAGE * STAGE_ELEMS : EPI_ELEMS;
   static constexpr int A_CPR = BM / 8;                     // 16-byte chunks per A row
   static constexpr int B_CPR = B_TR ? BN / 8 : BK / 8;     // chunks per B row
   static constexpr int CA = BK * A_CPR;
@@ -158,7 +159,6 @@ void gemm_kernel(GArgs g, OptArgs a) {
   const int ntm = (g.M + C::BM - 1) / C::BM, ntn = (g.N + C::BN - 1) / C::BN;
   const int ntiles = ntm * ntn;
   const int nst = (g.K + C::BK - 1) / C::BK;
-  const int nst2 = (nst + 1) & ~1;  // stages beyond K load zeros
 
   // This thread's staging chunks: chunk j of a stage is tid + j*NT, i.e. the same
   // column and rows spaced NT / chunks-per-row apart.
@@ -228,53 +228,83 @@ void gemm_kernel(GArgs g, OptArgs a) {
 #pragma unroll
       for (int j = 0; j < C::PB; ++j) *reinterpret_cast<u32x4*>(S + b_st + j * B_RSTEP * C::LDB) = rb[j];
     };
-    auto compute = [&](int buf) {
+    // Operand fragments of one 16-deep k-step.
+    struct Frag {
+      bf16x8 a[C::FM], b[C::FN];
+    };
+    auto load_frag = [&](Frag& F, int buf, int kk) {
       const uint16_t* S = smem + buf * C::STAGE_ELEMS;
 #pragma unroll
-      for (int kk = 0; kk < C::KSTEPS; ++kk) {
-        bf16x8 af[C::FM], bfr[C::FN];
+      for (int fm = 0; fm < C::FM; ++fm) {
+        const uint16_t* p = S + a_fr + kk * 16 * C::LDA + 32 * fm;
+        bf16x4 x0 = lds_tr(p), x1 = lds_tr(p + 4 * C::LDA);
+        F.a[fm] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
 #pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) {
-          const uint16_t* p = S + a_fr + kk * 16 * C::LDA + 32 * fm;
-          bf16x4 x0 = lds_tr(p), x1 = lds_tr(p + 4 * C::LDA);
-          af[fm] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+      for (int fn = 0; fn < C::FN; ++fn) {
+        if constexpr (C::B_TR) {
+          const uint16_t* p = S + b_fr + kk * 16 * C::LDB + 32 * fn;
+          bf16x4 y0 = lds_tr(p), y1 = lds_tr(p + 4 * C::LDB);
+          F.b[fn] = __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+          F.b[fn] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(S + b_fr + 32 * fn * C::LDB + kk * 16));
         }
-#pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) {
-          if constexpr (C::B_TR) {
-            const uint16_t* p = S + b_fr + kk * 16 * C::LDB + 32 * fn;
-            bf16x4 y0 = lds_tr(p), y1 = lds_tr(p + 4 * C::LDB);
-            bfr[fn] = __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7);
-          } else {
-            bfr[fn] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(S + b_fr + 32 * fn * C::LDB + kk * 16));
-          }
-        }
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn)
-            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
       }
     };
+    auto mma = [&](const Frag& F) {
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[fm], F.b[fn], acc[fm][fn], 0, 0, 0);
+    };
 
-    // ---- mainloop: stage s+1 is in registers while s is computed; s+3 is loaded after s ----
+    // ---- mainloop ----
+    // LDS ring of three stages and two register staging sets: while stage s is
+    // multiplied, stage s+1 is already in LDS, stage s+2 moves from registers to
+    // LDS, and stage s+4 is being fetched. Fragments of the next k-step (the next
+    // stage's first one at the end of a stage) are read while the current k-step's
+    // MFMAs run, so the matrix pipe keeps working across the stage barrier.
+    static_assert(C::KSTEPS % 2 == 0, "fragment double-buffering pairs k-steps");
     {
       u32x4 ra0[C::PA], rb0[C::PB], ra1[C::PA], rb1[C::PB];
+      Frag F0, F1;
       gload(0, ra0, rb0);
       gload(1, ra1, rb1);
-      __syncthreads();  // the previous tile's last stage has been read by every wave
+      __syncthreads();  // the previous tile's epilogue is done with LDS
       sstore(0, ra0, rb0);
-      __syncthreads();
       gload(2, ra0, rb0);
-      for (int s = 0; s < nst2; s += 2) {
-        compute(0);               // stage s
-        sstore(1, ra1, rb1);      // stage s+1
+      sstore(1, ra1, rb1);
+      gload(3, ra1, rb1);
+      __syncthreads();
+      load_frag(F0, 0, 0);
+      // Stage st of the ring: R = st % 6 fixes every LDS buffer index at compile time.
+      auto stage = [&](auto R_c, int st, u32x4 (&ra)[C::PA], u32x4 (&rb)[C::PB]) {
+        constexpr int R = decltype(R_c)::value;
+        constexpr int cur = R % 3, nxt = (R + 1) % 3, fill = (R + 2) % 3;
+#pragma unroll
+        for (int kk = 0; kk < C::KSTEPS; kk += 2) {
+          load_frag(F1, cur, kk + 1);
+          mma(F0);
+          if (kk == 0) {
+            sstore(fill, ra, rb);     // stage st+2
+            gload(st + 4, ra, rb);
+          }
+          if (kk + 2 < C::KSTEPS) load_frag(F0, cur, kk + 2);
+          else load_frag(F0, nxt, 0);  // first k-step of stage st+1
+          mma(F1);
+        }
         __syncthreads();
-        gload(s + 3, ra1, rb1);
-        compute(1);               // stage s+1
-        sstore(0, ra0, rb0);      // stage s+2
-        __syncthreads();
-        gload(s + 4, ra0, rb0);
+      };
+      // stages past the last one read zeros; the count is rounded up to a multiple of 6
+      const int nst6 = ((nst + 5) / 6) * 6;
+      for (int st = 0; st < nst6; st += 6) {
+        stage(std::integral_constant<int, 0>{}, st + 0, ra0, rb0);
+        stage(std::integral_constant<int, 1>{}, st + 1, ra1, rb1);
+        stage(std::integral_constant<int, 2>{}, st + 2, ra0, rb0);
+        stage(std::integral_constant<int, 3>{}, st + 3, ra1, rb1);
+        stage(std::integral_constant<int, 4>{}, st + 4, ra0, rb0);
+        stage(std::integral_constant<int, 5>{}, st + 5, ra1, rb1);
       }
     }
 
@@ -327,7 +357,8 @@ void gemm_kernel(GArgs g, OptArgs a) {
         const EpiRes R = epi_res<OPT, Q8>(a);
         // loads of KB vectors are issued before any of them is consumed; KB bounds the
         // registers a batch holds next to the accumulators still to be written out
-        constexpr int KB = (C::OCC >= 2 && NV > 2) ? 2 : NV;
+        constexpr int KB_MAX = C::OCC >= 2 ? 2 : (Q8 ? 4 : 8);
+        constexpr int KB = NV > KB_MAX ? KB_MAX : NV;
 #pragma unroll
         for (int kb = 0; kb < NV; kb += KB) {
         uint32_t ow[KB], om[KB], ov_[KB], osc[KB];
