@@ -101,7 +101,9 @@ def main() -> int:
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     # one (X, dY, dX) buffer set per distinct shape; W and its moments per layer
+    # (in the 224-layer stack, layers of one shape start from that shape's initial W)
     shape_bufs = {}
+    shape_w0 = {}
     per_layer = []
     t0 = time.perf_counter()
     for li, spec in enumerate(layers):
@@ -109,11 +111,19 @@ def main() -> int:
         if key not in shape_bufs:
             X, dY = draw_layer_batch(wl_config, li, 1, spec)
             shape_bufs[key] = (to_dev(X), to_dev(dY), torch.empty((spec.T, spec.inn), dtype=tdt, device=dev))
-        W = to_dev(draw_layer_init(wl_config, li if args.workload != "stack" else li % 7, spec))
+        if args.workload == "stack":
+            if key not in shape_w0:
+                shape_w0[key] = to_dev(draw_layer_init(wl_config, li, spec))
+            W = shape_w0[key].clone()
+        else:
+            W = to_dev(draw_layer_init(wl_config, li, spec))
         m, v, ms, vs = forge.new_states(W, opt, state)
         per_layer.append((spec, W, m, v, ms, vs, ((0x5EED0000 + wl_config) ^ li)))
+    shape_w0.clear()
+    torch.cuda.synchronize()
+    resident = torch.cuda.memory_allocated()
     print(f"[bench] setup {time.perf_counter() - t0:.1f}s: {len(layers)} layer(s), workload {args.workload}, "
-          f"opt {opt}, states {state}", file=sys.stderr, flush=True)
+          f"opt {opt}, states {state}, resident {resident / 2**30:.2f} GiB", file=sys.stderr, flush=True)
     hyper = forge.make_hyper(opt, stochastic_round=int(sr))
 
     step_counter = [0]
@@ -139,6 +149,7 @@ def main() -> int:
           for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
     wall0 = time.perf_counter()
     start.record()
     for k in range(args.steps):
@@ -146,6 +157,7 @@ def main() -> int:
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    peak_transient = torch.cuda.max_memory_allocated() - resident
     elapsed_ms = start.elapsed_time(end)
     ms_per_step = elapsed_ms / args.steps
     total_flops = 2.0 * sum(flops_gemm) * args.steps  # dgrad + wgrad per layer per step
@@ -208,6 +220,28 @@ def main() -> int:
                    "peak_transient_bytes": {"fused": int(fused_transient), "unfused": int(unfused_transient)},
                    "layer": f"{spec.name} {spec.out}x{spec.inn} T={spec.T}"}
 
+    # --- the stack under the two-phase schedule: every layer's fp32 dW resident before the update ---
+    stack_two_phase = None
+    if args.workload == "stack" and not args.no_unfused:
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dWs = []
+        for (spec, W, m, v, ms, vs, seed) in per_layer:
+            X, dY, dX = shape_bufs[(spec.out, spec.inn, spec.T)]
+            forge.dgrad(dY, W, dX)
+            dWs.append(forge.wgrad(X, dY))
+        for (spec, W, m, v, ms, vs, seed), dW in zip(per_layer, dWs):
+            forge.optimizer_step(dW, W, m, v, opt, hyper, 20_000, seed, ms, vs)
+        e1.record()
+        torch.cuda.synchronize()
+        floor = torch.cuda.max_memory_allocated() - base
+        del dWs
+        stack_two_phase = {"ms_per_pass": round(e0.elapsed_time(e1), 3), "peak_transient_bytes": int(floor),
+                           "largest_layer_dW_bytes": int(max(4 * s.out * s.inn for s, *_ in per_layer))}
+
     # --- CPU baseline: the float64 oracle on a bounded sample (first layer) ---
     cpu = None
     if not args.no_cpu_baseline:
@@ -266,8 +300,12 @@ def main() -> int:
                      "frac": round(fused_tflops / peak, 4), "traffic": traffic},
         "cpu_baseline": cpu,
         "unfused": unfused,
+        "resident_bytes": int(resident),
+        "peak_transient_bytes": int(peak_transient),
         "wall_s": round(wall, 3),
     }
+    if stack_two_phase is not None:
+        rec["two_phase_schedule"] = stack_two_phase
     print(json.dumps(rec))
     return 0
 
