@@ -53,7 +53,55 @@ def parse():
     p.add_argument("--no-unfused", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain 1 GiB device copy (3 times) to calibrate HBM byte counters")
+    p.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"),
+                   help="no GPU work: turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE databases of this bench (and of "
+                        "--calibrate-copy) into profiles/traffic_<workload>.json for the current kernel source")
     return p.parse_args()
+
+
+def _counter_means(db: str, counter: str) -> dict:
+    """Mean per dispatch of one counter, per kernel name, from a rocprofv3 results database."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    cols = [d[1] for d in con.execute("pragma table_info(counters_collection)")]
+    acc = {}
+    for row in con.execute("select * from counters_collection"):
+        d = dict(zip(cols, row))
+        if d["counter_name"] == counter:
+            acc.setdefault(d["kernel_name"], []).append(float(d["value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def record_traffic(args) -> int:
+    """HBM bytes per launch of the fused kernel: counters in KiB, scaled by what the same
+    counters read for a copy of known size."""
+    fetch_db, write_db, cfetch_db, cwrite_db = args.record_traffic
+    copy_bytes = 4 * (1 << 28)
+    cf = [v for k, v in _counter_means(cfetch_db, "FETCH_SIZE").items() if "copyBuffer" in k]
+    cw = [v for k, v in _counter_means(cwrite_db, "WRITE_SIZE").items() if "copyBuffer" in k]
+    if not cf or not cw:
+        print("no copy kernel in the calibration databases", file=sys.stderr)
+        return 1
+    f_scale, w_scale = copy_bytes / (cf[0] * 1024), copy_bytes / (cw[0] * 1024)
+
+    def fused(means):
+        # the optimizer epilogue is template argument EPI = 1 of gemm_kernel
+        hits = [v for k, v in means.items() if "gemm_kernel<" in k and ">, 1, " in k]
+        if len(hits) != 1:
+            raise SystemExit(f"expected one fused kernel in the counters, found {len(hits)}")
+        return hits[0] * 1024
+
+    fetch = fused(_counter_means(fetch_db, "FETCH_SIZE")) * f_scale
+    write = fused(_counter_means(write_db, "WRITE_SIZE")) * w_scale
+    rec = {"workload": args.workload, "opt": args.opt, "kernel_source_hash": kernel_source_hash(),
+           "bytes_per_launch": int(round(fetch + write)), "fetch_bytes": int(round(fetch)),
+           "write_bytes": int(round(write)), "fetch_scale": f_scale, "write_scale": w_scale,
+           "source": f"profiles/wgrad_fused_{args.workload}.md"}
+    out = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+    return 0
 
 
 def calibrate_copy() -> int:
@@ -74,6 +122,8 @@ def main() -> int:
     args = parse()
     if args.calibrate_copy:
         return calibrate_copy()
+    if args.record_traffic:
+        return record_traffic(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
               "(tensor-parallel shards run the same kernel on each GPU's share)", file=sys.stderr)

@@ -12,15 +12,21 @@
 // so each lane's accumulator rows are consecutive `in` elements of one W (or dX)
 // row: the epilogue moves W/m/v/dX as 8- and 16-byte vectors.
 // A is always stored with k as the slow index (rows of X or W), B either the same
-// way (wgrad: rows of dY) or with k fast (dgrad: rows of dY). Rows are staged in
-// LDS as they sit in memory and turned K-major for the matrix cores by the LDS
-// transpose read ds_read_b64_tr_b16; k-fast B rows are read with 16-byte LDS reads.
-// Matrix instruction: v_mfma_f32_32x32x16_bf16 (the 16x16x32 form issues at half
-// the rate on this part). Each workgroup has WM x WN waves; a wave owns a
-// (BM/WM) x (BN/WN) block of C. Operand stages of BK tokens are prefetched
-// two stages ahead into registers and double-buffered in LDS. Tiles are walked by
-// a persistent grid in an XCD-aware order so the workgroups that run at the same
-// time on one XCD share the X/dY panels in that XCD's L2.
+// way (wgrad: rows of dY) or with k fast (dgrad: rows of dY).
+//
+// Mainloop. Operand stages of BK tokens go from global memory straight into LDS:
+// buffer loads with the LDS bit write one wave's 64 x 16 bytes to 1 KiB of
+// consecutive LDS, and out-of-range offsets write zeros (ragged k needs no other
+// masking). Four stages are in flight in a ring, so a stage's loads are issued three
+// stages before it is multiplied. Rows are kept as they sit in memory; the matrix
+// cores get them K-major through the LDS transpose read ds_read_b64_tr_b16 (k-fast B
+// rows through 16-byte reads), and XOR swizzles of the 16-byte chunks keep those
+// reads free of bank conflicts. Matrix instruction: v_mfma_f32_32x32x16_bf16 (the
+// 16x16x32 form issues at half the rate on this part). Each workgroup has WM x WN
+// waves; a wave owns a (BM/WM) x (BN/WN) block of C. The fragments of the next
+// k-step are read between the MFMAs of the current one. Tiles are walked by a
+// persistent grid in an XCD-aware order so the workgroups that run at the same time
+// on one XCD share the X/dY panels in that XCD's L2.
 #include <type_traits>
 
 #include "forge_internal.h"
@@ -50,27 +56,36 @@ struct GCfg {
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
   static constexpr int KSTEPS = BK / 16;
-  // LDS stage rows. Rows read with the transpose read are padded by 64 bytes so the
-  // four rows one read touches fall into four different bank windows; k-fast B rows
-  // are padded by 16 bytes for the 16-byte reads.
-  static constexpr int LDA = BM + 32;
-  static constexpr int LDB = B_TR ? BN + 32 : BK + 8;
-  static constexpr int A_ELEMS = BK * LDA;
-  static constexpr int B_ELEMS = B_TR ? BK * LDB : BN * LDB;
-  static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
-  // LDS: a ring of three operand stages, reused after the mainloop for one TN-row
-  // chunk of the finished tile as float rows of BM + 4.
-  static constexpr int NSTAGE = 3;
+  // One LDS stage: A as BK rows of BM; B as BK rows of BN (B_TR) or BN rows of BK.
+  static constexpr int A_ELEMS = BK * BM, B_ELEMS = BK * BN;
+  // LDS: a ring of four stages (the A parts of all stages first, then the B parts, so
+  // every fragment read reaches its stage through an immediate offset below 64 KiB),
+  // reused after the mainloop for one TN-row chunk of the finished tile as float rows
+  // of BM + 4.
+  static constexpr int NSTAGE = 4;
+  static constexpr int a_base(int buf) { return buf * A_ELEMS; }
+  static constexpr int b_base(int buf) { return NSTAGE * A_ELEMS + buf * B_ELEMS; }
   static constexpr int EPI_ELEMS = TN * (BM + 4) * 2;
-  static constexpr int SMEM_ELEMS = NSTAGE * STAGE_ELEMS > EPI_ELEMS ? NSTAGE * STAGE_ELEMS : EPI_ELEMS;
+  static constexpr int RING_ELEMS = NSTAGE * (A_ELEMS + B_ELEMS);
+  static constexpr int SMEM_ELEMS = RING_ELEMS > EPI_ELEMS ? RING_ELEMS : EPI_ELEMS;
   static constexpr int A_CPR = BM / 8;                     // 16-byte chunks per A row
   static constexpr int B_CPR = B_TR ? BN / 8 : BK / 8;     // chunks per B row
-  static constexpr int CA = BK * A_CPR;
-  static constexpr int CB = B_TR ? BK * B_CPR : BN * B_CPR;
-  static constexpr int PA = CA / NT, PB = CB / NT;         // chunks per thread per stage
-  static_assert(CA % NT == 0 && CB % NT == 0, "stage must split evenly over threads");
+  static constexpr int PA = BK * A_CPR / NT, PB = BK * BN / 8 / NT;  // chunks per thread per stage
+  static_assert((BK * A_CPR) % NT == 0 && (BK * BN / 8) % NT == 0, "stage must split evenly over threads");
   static_assert(NT % A_CPR == 0 && NT % B_CPR == 0, "a thread's chunks share a column");
-  static_assert(TM % 32 == 0 && TN % 32 == 0 && BK % 16 == 0, "tile shape");
+  static_assert(TM % 32 == 0 && TN % 32 == 0 && BK % 16 == 0 && KSTEPS % 2 == 0, "tile shape");
+  // Chunk swizzles: rows read with the transpose read XOR their 16-byte chunk index
+  // with 4 * (row % 4), so the four rows one read touches land in four different
+  // 64-byte bank groups (needs 16 or more chunks per row); k-fast B rows of 4 chunks
+  // XOR it with (row / 4) % 4, so 16 consecutive rows cover all 16 bank groups. A
+  // thread's chunks are NT / chunks-per-row rows apart, a multiple of the swizzle
+  // period, so they all share one swizzled column.
+  static_assert(A_CPR >= 16 && (NT / A_CPR) % 4 == 0, "A swizzle");
+  static_assert(B_TR ? (B_CPR >= 16 && (NT / B_CPR) % 4 == 0) : (B_CPR == 4 && (NT / B_CPR) % 16 == 0), "B swizzle");
+  // the 16-bit offset field of the LDS reads
+  static_assert(2 * ((NSTAGE - 1) * A_ELEMS + (KSTEPS - 1) * 16 * BM + 4 * BM) < 65536, "A read offsets");
+  static_assert(2 * ((NSTAGE - 1) * B_ELEMS + (B_TR ? (KSTEPS - 1) * 16 * BN + 4 * BN : 32 * (FN - 1) * BK)) < 65536,
+                "B read offsets");
 };
 
 struct GArgs {
@@ -91,13 +106,52 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ bf16x4 lds_tr(const uint16_t* p) {
-  typedef __bf16 v4bf_t __attribute__((__vector_size__(8)));
+// Fragment reads, written as inline assembly with explicit lgkmcnt waits: an LDS read
+// the compiler can see makes it wait for every outstanding global->LDS load first
+// (vmcnt(0)), which would drain the ring at every k-step. Target builtins and LDS
+// address casts stay in these __device__ helpers: in a kernel body the host pass
+// rejects them and silently drops the kernel's launch stub.
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_tr_asm(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_b128_asm(uint32_t addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+// 32-bit LDS byte address of a __shared__ location.
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Wold-style-cast"
-  auto lp = (__attribute__((address_space(3))) v4bf_t*)(const_cast<uint16_t*>(p));
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t*)p;
 #pragma clang diagnostic pop
-  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
+}
+// 16 bytes per lane from buffer offset off into LDS at dst + 16 * lane (zeros where
+// off is out of range).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* dst, uint32_t off) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wold-style-cast"
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+#pragma clang diagnostic pop
+}
+// An empty asm that claims to rewrite v: any use of v after it is ordered after the
+// wait that precedes it.
+__device__ __forceinline__ void pin_reg(u32x2& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin_reg(u32x4& v) { asm volatile("" : "+v"(v)); }
+// Waits until at most N LDS reads of this wave are outstanding (they complete in order).
+template <int N>
+__device__ __forceinline__ void lgkm_wait() {
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N) : "memory");
+}
+// Waits until at most N global loads of this wave are outstanding and no LDS read is,
+// then joins the workgroup barrier.
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(N) : "memory");
 }
 
 // Persistent tile order: tile ids a workgroup takes are blockIdx.x + r*gridDim.x.
@@ -148,6 +202,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC, C
 void gemm_kernel(GArgs g, OptArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[C::SMEM_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int wm = wave % C::WM, wn = wave / C::WM;
   const int wave_m0 = wm * C::TM, wave_n0 = wn * C::TN;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -159,18 +214,42 @@ void gemm_kernel(GArgs g, OptArgs a) {
   const int ntm = (g.M + C::BM - 1) / C::BM, ntn = (g.N + C::BN - 1) / C::BN;
   const int ntiles = ntm * ntn;
   const int nst = (g.K + C::BK - 1) / C::BK;
+  // Stages are issued in groups of the ring size; stages past the last one, like rows
+  // past the last token, load through out-of-range offsets and so hold zeros.
+  const int nst4 = ((nst + C::NSTAGE - 1) / C::NSTAGE) * C::NSTAGE;
+  constexpr int LPS = C::PA + C::PB;                              // loads per stage and wave
+  constexpr int NR = 2 * C::FM + (C::B_TR ? 2 * C::FN : C::FN);  // LDS reads per k-step and wave
+  static_assert(3 * LPS <= 63, "vmcnt range");
 
-  // This thread's staging chunks: chunk j of a stage is tid + j*NT, i.e. the same
-  // column and rows spaced NT / chunks-per-row apart.
-  const int a_row0 = tid / C::A_CPR, a_col = (tid % C::A_CPR) * 8;
-  const int b_row0 = tid / C::B_CPR, b_col = (tid % C::B_CPR) * 8;
+  // Staging: the LDS slot of this thread's chunk j in a stage is tid + j*NT (a wave's
+  // load fills 64 consecutive 16-byte slots); the swizzle picks the global chunk that
+  // lands there. Chunk j is A_RSTEP (B_RSTEP) rows below chunk 0.
+  const int a_row0 = tid / C::A_CPR, b_row0 = tid / C::B_CPR;
+  const int a_col = ((tid % C::A_CPR) ^ (4 * (a_row0 & 3))) * 8;
+  const int b_col = ((tid % C::B_CPR) ^ (C::B_TR ? 4 * (b_row0 & 3) : (b_row0 >> 2) & 3)) * 8;
   constexpr int A_RSTEP = C::NT / C::A_CPR, B_RSTEP = C::NT / C::B_CPR;
-  // LDS element offsets of the staging chunks and of this lane's fragment reads
-  const int a_st = a_row0 * C::LDA + a_col;
-  const int b_st = C::A_ELEMS + b_row0 * C::LDB + b_col;
-  const int a_fr = (8 * hi + r4) * C::LDA + wave_m0 + 16 * half + 4 * c4;
-  const int b_fr = C::B_TR ? C::A_ELEMS + (8 * hi + r4) * C::LDB + wave_n0 + 16 * half + 4 * c4
-                           : C::A_ELEMS + (wave_n0 + l32) * C::LDB + 8 * hi;
+  const uint32_t a_rowb = (uint32_t)(A_RSTEP * g.lda * 2), a_stageb = (uint32_t)(C::BK * g.lda * 2);
+  const uint32_t b_rowb = (uint32_t)(B_RSTEP * g.ldb * 2);
+  const uint32_t b_stageb = C::B_TR ? (uint32_t)(C::BK * g.ldb * 2) : (uint32_t)(C::BK * 2);
+
+  // Byte addresses of this lane's fragment reads in stage buffer 0, k-step 0, with the
+  // chunk index swizzled as the loads placed it; buffers and k-steps are immediates.
+  const uint32_t lds0 = lds_addr(smem);
+  uint32_t a_ad[C::FM], b_ad[C::B_TR ? C::FN : C::KSTEPS];
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+    a_ad[fm] = lds0 + 2u * (uint32_t)((8 * hi + r4) * C::BM + 8 * (((wave_m0 + 32 * fm) / 8) ^ (4 * r4)) + 16 * half +
+                                      4 * c4);
+  if constexpr (C::B_TR) {
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+      b_ad[fn] = lds0 + 2u * (uint32_t)(C::b_base(0) + (8 * hi + r4) * C::BN +
+                                        8 * (((wave_n0 + 32 * fn) / 8) ^ (4 * r4)) + 16 * half + 4 * c4);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < C::KSTEPS; ++kk)
+      b_ad[kk] = lds0 + 2u * (uint32_t)(C::b_base(0) + (wave_n0 + l32) * C::BK + 8 * ((2 * kk + hi) ^ ((l32 >> 2) & 3)));
+  }
 
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     int tm, tn;
@@ -185,128 +264,137 @@ void gemm_kernel(GArgs g, OptArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[fm][fn][e] = 0.f;
 
-    // Byte offsets of this thread's chunks in stage 0 (kOOB where the column is out
-    // of range); stage s adds s * BK rows (A, B_TR) or s * BK columns (!B_TR).
-    const bool a_cok = m0 + a_col < g.M;
-    const uint32_t a_off0 = a_cok ? (uint32_t)((a_row0 * g.lda + m0 + a_col) * 2) : kOOB;
-    const uint32_t a_rowb = (uint32_t)(A_RSTEP * g.lda * 2), a_stageb = (uint32_t)(C::BK * g.lda * 2);
-    uint32_t b_off0, b_rowb, b_stageb;
-    if constexpr (C::B_TR) {
-      b_off0 = (n0 + b_col < g.N) ? (uint32_t)((b_row0 * g.ldb + n0 + b_col) * 2) : kOOB;
-      b_rowb = (uint32_t)(B_RSTEP * g.ldb * 2);
-      b_stageb = (uint32_t)(C::BK * g.ldb * 2);
-    } else {
-      b_off0 = (uint32_t)(((int64_t)(n0 + b_row0) * g.ldb + b_col) * 2);
-      b_rowb = (uint32_t)(B_RSTEP * g.ldb * 2);
-      b_stageb = (uint32_t)(C::BK * 2);
-    }
-
-    // ---- staging: global -> registers -> LDS ----
-    auto gload = [&](int s, u32x4 (&ra)[C::PA], u32x4 (&rb)[C::PB]) {
+    // Only the k range is checked per load: a chunk past the M or N edge feeds
+    // accumulator rows or columns that are never stored (the buffer resource still
+    // bounds every access), while a k past the end must read as zero.
+    const uint32_t a_base0 = (uint32_t)((a_row0 * g.lda + m0 + a_col) * 2);
+    uint32_t b_base0;
+    if constexpr (C::B_TR)
+      b_base0 = (uint32_t)((b_row0 * g.ldb + n0 + b_col) * 2);
+    else
+      b_base0 = (uint32_t)(((int64_t)(n0 + b_row0) * g.ldb + b_col) * 2);
+    auto dma = [&](auto buf_c, int s) {
+      constexpr int buf = decltype(buf_c)::value;
       const int k0 = s * C::BK;
 #pragma unroll
       for (int j = 0; j < C::PA; ++j) {
-        const bool ok = a_cok && (k0 + a_row0 + j * A_RSTEP < g.K);
-        const uint32_t off = ok ? a_off0 + (uint32_t)s * a_stageb + (uint32_t)j * a_rowb : kOOB;
-        ra[j] = __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0);
+        const uint32_t off = (k0 + a_row0 + j * A_RSTEP < g.K) ? a_base0 + (uint32_t)s * a_stageb + (uint32_t)j * a_rowb : kOOB;
+        dma16(rA, smem + C::a_base(buf) + (j * C::NT + wave_u * 64) * 8, off);
       }
 #pragma unroll
       for (int j = 0; j < C::PB; ++j) {
-        bool ok;
-        if constexpr (C::B_TR)
-          ok = (b_off0 != kOOB) && (k0 + b_row0 + j * B_RSTEP < g.K);
-        else
-          ok = (n0 + b_row0 + j * B_RSTEP < g.N) && (k0 + b_col < g.K);
-        const uint32_t off = ok ? b_off0 + (uint32_t)s * b_stageb + (uint32_t)j * b_rowb : kOOB;
-        rb[j] = __builtin_amdgcn_raw_buffer_load_b128(rB, off, 0, 0);
+        const int kb = C::B_TR ? k0 + b_row0 + j * B_RSTEP : k0 + b_col;
+        const uint32_t off = (kb < g.K) ? b_base0 + (uint32_t)s * b_stageb + (uint32_t)j * b_rowb : kOOB;
+        dma16(rB, smem + C::b_base(buf) + (j * C::NT + wave_u * 64) * 8, off);
       }
     };
-    auto sstore = [&](int buf, const u32x4 (&ra)[C::PA], const u32x4 (&rb)[C::PB]) {
-      uint16_t* S = smem + buf * C::STAGE_ELEMS;
-#pragma unroll
-      for (int j = 0; j < C::PA; ++j) *reinterpret_cast<u32x4*>(S + a_st + j * A_RSTEP * C::LDA) = ra[j];
-#pragma unroll
-      for (int j = 0; j < C::PB; ++j) *reinterpret_cast<u32x4*>(S + b_st + j * B_RSTEP * C::LDB) = rb[j];
-    };
-    // Operand fragments of one 16-deep k-step.
+    // Operand fragments of one k-step as the LDS reads return them: two 4-deep
+    // halves per transposed operand, one 16-byte read per k-fast B operand.
     struct Frag {
-      bf16x8 a[C::FM], b[C::FN];
+      u32x2 a[C::FM][2];
+      u32x2 bt[C::B_TR ? C::FN : 1][2];
+      u32x4 bk[C::B_TR ? 1 : C::FN];
     };
-    auto load_frag = [&](Frag& F, int buf, int kk) {
-      const uint16_t* S = smem + buf * C::STAGE_ELEMS;
+    // The r-th of the NR reads of a k-step's fragments.
+    auto read_one = [&](Frag& F, auto buf_c, auto kk_c, auto r_c) {
+      constexpr int buf = decltype(buf_c)::value, kk = decltype(kk_c)::value, r = decltype(r_c)::value;
+      if constexpr (r < 2 * C::FM) {
+        constexpr int fm = r / 2, h = r % 2;
+        F.a[fm][h] = ds_tr_asm<2 * (C::a_base(buf) + kk * 16 * C::BM + 4 * h * C::BM)>(a_ad[fm]);
+      } else if constexpr (C::B_TR) {
+        constexpr int fn = (r - 2 * C::FM) / 2, h = (r - 2 * C::FM) % 2;
+        F.bt[fn][h] = ds_tr_asm<2 * (buf * C::B_ELEMS + kk * 16 * C::BN + 4 * h * C::BN)>(b_ad[fn]);
+      } else {
+        constexpr int fn = r - 2 * C::FM;
+        F.bk[fn] = ds_b128_asm<2 * (buf * C::B_ELEMS + 32 * fn * C::BK)>(b_ad[kk]);
+      }
+    };
+    // Orders every later use of F's registers after the wait that precedes this.
+    auto settle = [&](Frag& F) {
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm) {
-        const uint16_t* p = S + a_fr + kk * 16 * C::LDA + 32 * fm;
-        bf16x4 x0 = lds_tr(p), x1 = lds_tr(p + 4 * C::LDA);
-        F.a[fm] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+        pin_reg(F.a[fm][0]);
+        pin_reg(F.a[fm][1]);
       }
+      if constexpr (C::B_TR) {
 #pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn) {
-        if constexpr (C::B_TR) {
-          const uint16_t* p = S + b_fr + kk * 16 * C::LDB + 32 * fn;
-          bf16x4 y0 = lds_tr(p), y1 = lds_tr(p + 4 * C::LDB);
-          F.b[fn] = __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7);
-        } else {
-          F.b[fn] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(S + b_fr + 32 * fn * C::LDB + kk * 16));
+        for (int fn = 0; fn < C::FN; ++fn) {
+          pin_reg(F.bt[fn][0]);
+          pin_reg(F.bt[fn][1]);
         }
+      } else {
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) pin_reg(F.bk[fn]);
       }
     };
-    auto mma = [&](const Frag& F) {
-#pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[fm], F.b[fn], acc[fm][fn], 0, 0, 0);
+    auto mfma_one = [&](const Frag& F, auto i_c) {
+      constexpr int fm = decltype(i_c)::value / C::FN, fn = decltype(i_c)::value % C::FN;
+      const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{F.a[fm][0].x, F.a[fm][0].y, F.a[fm][1].x, F.a[fm][1].y});
+      bf16x8 bv;
+      if constexpr (C::B_TR)
+        bv = __builtin_bit_cast(bf16x8, u32x4{F.bt[fn][0].x, F.bt[fn][0].y, F.bt[fn][1].x, F.bt[fn][1].y});
+      else
+        bv = __builtin_bit_cast(bf16x8, F.bk[fn]);
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[fm][fn], 0, 0, 0);
+    };
+    // The MFMAs of fragment set F, with the reads of the next set G spread over the
+    // first half of them and `after_first` run after the first; sched_barrier keeps
+    // this order.
+    constexpr int NM = C::FM * C::FN;
+    constexpr int RPM = (NR + NM / 2 - 1) / (NM / 2);
+    auto mma_reading = [&](const Frag& F, Frag& G, auto buf_c, auto kk_c, auto&& after_first) {
+      static_for<0, NM>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        mfma_one(F, i_c);
+        if constexpr (i == 0) after_first();
+        static_for<i * RPM, (i + 1) * RPM < NR ? (i + 1) * RPM : NR>([&](auto r_c) { read_one(G, buf_c, kk_c, r_c); });
+        __builtin_amdgcn_sched_barrier(0);
+      });
     };
 
     // ---- mainloop ----
-    // LDS ring of three stages and two register staging sets: while stage s is
-    // multiplied, stage s+1 is already in LDS, stage s+2 moves from registers to
-    // LDS, and stage s+4 is being fetched. Fragments of the next k-step (the next
-    // stage's first one at the end of a stage) are read while the current k-step's
-    // MFMAs run, so the matrix pipe keeps working across the stage barrier.
-    static_assert(C::KSTEPS % 2 == 0, "fragment double-buffering pairs k-steps");
-    {
-      u32x4 ra0[C::PA], rb0[C::PB], ra1[C::PA], rb1[C::PB];
-      Frag F0, F1;
-      gload(0, ra0, rb0);
-      gload(1, ra1, rb1);
-      __syncthreads();  // the previous tile's epilogue is done with LDS
-      sstore(0, ra0, rb0);
-      gload(2, ra0, rb0);
-      sstore(1, ra1, rb1);
-      gload(3, ra1, rb1);
-      __syncthreads();
-      load_frag(F0, 0, 0);
-      // Stage st of the ring: R = st % 6 fixes every LDS buffer index at compile time.
-      auto stage = [&](auto R_c, int st, u32x4 (&ra)[C::PA], u32x4 (&rb)[C::PB]) {
-        constexpr int R = decltype(R_c)::value;
-        constexpr int cur = R % 3, nxt = (R + 1) % 3, fill = (R + 2) % 3;
-#pragma unroll
-        for (int kk = 0; kk < C::KSTEPS; kk += 2) {
-          load_frag(F1, cur, kk + 1);
-          mma(F0);
-          if (kk == 0) {
-            sstore(fill, ra, rb);     // stage st+2
-            gload(st + 4, ra, rb);
-          }
-          if (kk + 2 < C::KSTEPS) load_frag(F0, cur, kk + 2);
-          else load_frag(F0, nxt, 0);  // first k-step of stage st+1
-          mma(F1);
+    // Stage st sits in ring buffer st % 4. Within a stage the k-steps' MFMAs run
+    // back to back, each set reading the next set's fragments. Between the last two
+    // sets every wave waits for its own loads of stage st+1 and for its LDS reads, the
+    // barrier then makes stage st+1 visible and frees buffer st % 4 (all its reads
+    // are done), and the loads of stage st+4 into that buffer are issued.
+    Frag F0, F1;
+    __syncthreads();  // the previous tile's epilogue is done with LDS
+    dma(std::integral_constant<int, 0>{}, 0);
+    dma(std::integral_constant<int, 1>{}, 1);
+    dma(std::integral_constant<int, 2>{}, 2);
+    dma(std::integral_constant<int, 3>{}, 3);
+    vm_wait_barrier<3 * LPS>();
+    static_for<0, NR>([&](auto r_c) {
+      read_one(F0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, r_c);
+    });
+    auto stage = [&](auto R_c, int st) {
+      constexpr int R = decltype(R_c)::value;
+      static_for<0, C::KSTEPS / 2>([&](auto p_c) {
+        constexpr int kk = 2 * decltype(p_c)::value;
+        lgkm_wait<0>();
+        settle(F0);
+        mma_reading(F0, F1, R_c, std::integral_constant<int, kk + 1>{}, [] {});
+        if constexpr (kk + 2 < C::KSTEPS) {
+          lgkm_wait<0>();
+          settle(F1);
+          mma_reading(F1, F0, R_c, std::integral_constant<int, kk + 2>{}, [] {});
+        } else {
+          vm_wait_barrier<2 * LPS>();
+          settle(F1);
+          mma_reading(F1, F0, std::integral_constant<int, (R + 1) % 4>{}, std::integral_constant<int, 0>{},
+                      [&] { dma(R_c, st + 4); });
         }
-        __syncthreads();
-      };
-      // stages past the last one read zeros; the count is rounded up to a multiple of 6
-      const int nst6 = ((nst + 5) / 6) * 6;
-      for (int st = 0; st < nst6; st += 6) {
-        stage(std::integral_constant<int, 0>{}, st + 0, ra0, rb0);
-        stage(std::integral_constant<int, 1>{}, st + 1, ra1, rb1);
-        stage(std::integral_constant<int, 2>{}, st + 2, ra0, rb0);
-        stage(std::integral_constant<int, 3>{}, st + 3, ra1, rb1);
-        stage(std::integral_constant<int, 4>{}, st + 4, ra0, rb0);
-        stage(std::integral_constant<int, 5>{}, st + 5, ra1, rb1);
-      }
+      });
+    };
+    for (int st = 0; st < nst4; st += 4) {
+      stage(std::integral_constant<int, 0>{}, st);
+      stage(std::integral_constant<int, 1>{}, st + 1);
+      stage(std::integral_constant<int, 2>{}, st + 2);
+      stage(std::integral_constant<int, 3>{}, st + 3);
     }
+    // the loads issued past the end still write LDS: let them land before it is reused
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 
     // ---- epilogue ----
     // The finished tile is handed through LDS one wave-column (TN rows of n) at a
