@@ -47,22 +47,27 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 enum { G_EPI_STORE = 0, G_EPI_OPT = 1, G_EPI_DX = 2 };
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, bool B_TR_, int OCC_>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, bool B_TR_, int OCC_, int NSTAGE_ = 4, int KS_ = 1>
 struct GCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
   static constexpr int OCC = OCC_;  // waves per SIMD
   static constexpr bool B_TR = B_TR_;
-  static constexpr int NW = WM * WN, NT = 64 * NW;
+  // KS > 1: in-workgroup split-K. KS groups of WM x WN waves each take their own
+  // k-steps of every stage; the partial tiles are summed through LDS in the epilogue.
+  static constexpr int KS = KS_;
+  static constexpr int NW = WM * WN * KS, NT = 64 * NW;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
   static constexpr int KSTEPS = BK / 16;
+  static constexpr int KPW = KSTEPS / KS;  // k-steps of a stage per wave
   // One LDS stage: A as BK rows of BM; B as BK rows of BN (B_TR) or BN rows of BK.
   static constexpr int A_ELEMS = BK * BM, B_ELEMS = BK * BN;
-  // LDS: a ring of four stages (the A parts of all stages first, then the B parts, so
-  // every fragment read reaches its stage through an immediate offset below 64 KiB),
+  // LDS: a ring of NSTAGE stages (the A parts of all stages first, then the B parts,
+  // so every fragment read reaches its stage through an immediate offset below 64 KiB),
   // reused after the mainloop for one TN-row chunk of the finished tile as float rows
   // of BM + 4.
-  static constexpr int NSTAGE = 4;
+  static constexpr int NSTAGE = NSTAGE_;
+  static_assert(NSTAGE >= 2, "ring");
   static constexpr int a_base(int buf) { return buf * A_ELEMS; }
   static constexpr int b_base(int buf) { return NSTAGE * A_ELEMS + buf * B_ELEMS; }
   static constexpr int EPI_ELEMS = TN * (BM + 4) * 2;
@@ -73,18 +78,20 @@ struct GCfg {
   static constexpr int PA = BK * A_CPR / NT, PB = BK * BN / 8 / NT;  // chunks per thread per stage
   static_assert((BK * A_CPR) % NT == 0 && (BK * BN / 8) % NT == 0, "stage must split evenly over threads");
   static_assert(NT % A_CPR == 0 && NT % B_CPR == 0, "a thread's chunks share a column");
-  static_assert(TM % 32 == 0 && TN % 32 == 0 && BK % 16 == 0 && KSTEPS % 2 == 0, "tile shape");
+  static_assert(TM % 32 == 0 && TN % 32 == 0 && BK % 16 == 0 && KSTEPS % KS == 0 && KPW % 2 == 0, "tile shape");
   // Chunk swizzles: rows read with the transpose read XOR their 16-byte chunk index
   // with 4 * (row % 4), so the four rows one read touches land in four different
-  // 64-byte bank groups (needs 16 or more chunks per row); k-fast B rows of 4 chunks
-  // XOR it with (row / 4) % 4, so 16 consecutive rows cover all 16 bank groups. A
-  // thread's chunks are NT / chunks-per-row rows apart, a multiple of the swizzle
-  // period, so they all share one swizzled column.
+  // 64-byte bank groups (needs 16 or more chunks per row); k-fast B rows of 4 or 8
+  // chunks (KW = 4 or 2 rows per 256 bytes) XOR it with (row / KW) % chunks, so 16
+  // consecutive rows cover all 16 bank groups. A thread's chunks are NT / chunks-per-row
+  // rows apart, a multiple of the swizzle period, so they all share one swizzled column.
+  static constexpr int KW = B_TR ? 1 : 16 / B_CPR;
   static_assert(A_CPR >= 16 && (NT / A_CPR) % 4 == 0, "A swizzle");
-  static_assert(B_TR ? (B_CPR >= 16 && (NT / B_CPR) % 4 == 0) : (B_CPR == 4 && (NT / B_CPR) % 16 == 0), "B swizzle");
+  static_assert(B_TR ? (B_CPR >= 16 && (NT / B_CPR) % 4 == 0)
+                     : ((B_CPR == 4 || B_CPR == 8) && (NT / B_CPR) % 16 == 0), "B swizzle");
   // the 16-bit offset field of the LDS reads
-  static_assert(2 * ((NSTAGE - 1) * A_ELEMS + (KSTEPS - 1) * 16 * BM + 4 * BM) < 65536, "A read offsets");
-  static_assert(2 * ((NSTAGE - 1) * B_ELEMS + (B_TR ? (KSTEPS - 1) * 16 * BN + 4 * BN : 32 * (FN - 1) * BK)) < 65536,
+  static_assert(2 * ((NSTAGE - 1) * A_ELEMS + (KPW - 1) * 16 * BM + 4 * BM) < 65536, "A read offsets");
+  static_assert(2 * ((NSTAGE - 1) * B_ELEMS + (B_TR ? (KPW - 1) * 16 * BN + 4 * BN : 32 * (FN - 1) * BK)) < 65536,
                 "B read offsets");
 };
 
@@ -203,7 +210,8 @@ void gemm_kernel(GArgs g, OptArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[C::SMEM_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int wm = wave % C::WM, wn = wave / C::WM;
+  const int ks = wave / (C::WM * C::WN), wsp = wave % (C::WM * C::WN);
+  const int wm = wsp % C::WM, wn = wsp / C::WM;
   const int wave_m0 = wm * C::TM, wave_n0 = wn * C::TN;
   const int l32 = lane & 31, hi = lane >> 5;
   const int r4 = (lane & 15) >> 2, c4 = lane & 3, half = (lane >> 4) & 1;
@@ -216,17 +224,17 @@ void gemm_kernel(GArgs g, OptArgs a) {
   const int nst = (g.K + C::BK - 1) / C::BK;
   // Stages are issued in groups of the ring size; stages past the last one, like rows
   // past the last token, load through out-of-range offsets and so hold zeros.
-  const int nst4 = ((nst + C::NSTAGE - 1) / C::NSTAGE) * C::NSTAGE;
+  const int nstr = ((nst + C::NSTAGE - 1) / C::NSTAGE) * C::NSTAGE;
   constexpr int LPS = C::PA + C::PB;                              // loads per stage and wave
   constexpr int NR = 2 * C::FM + (C::B_TR ? 2 * C::FN : C::FN);  // LDS reads per k-step and wave
-  static_assert(3 * LPS <= 63, "vmcnt range");
+  static_assert((C::NSTAGE - 1) * LPS <= 63, "vmcnt range");
 
   // Staging: the LDS slot of this thread's chunk j in a stage is tid + j*NT (a wave's
   // load fills 64 consecutive 16-byte slots); the swizzle picks the global chunk that
   // lands there. Chunk j is A_RSTEP (B_RSTEP) rows below chunk 0.
   const int a_row0 = tid / C::A_CPR, b_row0 = tid / C::B_CPR;
   const int a_col = ((tid % C::A_CPR) ^ (4 * (a_row0 & 3))) * 8;
-  const int b_col = ((tid % C::B_CPR) ^ (C::B_TR ? 4 * (b_row0 & 3) : (b_row0 >> 2) & 3)) * 8;
+  const int b_col = ((tid % C::B_CPR) ^ (C::B_TR ? 4 * (b_row0 & 3) : (b_row0 / C::KW) % C::B_CPR)) * 8;
   constexpr int A_RSTEP = C::NT / C::A_CPR, B_RSTEP = C::NT / C::B_CPR;
   const uint32_t a_rowb = (uint32_t)(A_RSTEP * g.lda * 2), a_stageb = (uint32_t)(C::BK * g.lda * 2);
   const uint32_t b_rowb = (uint32_t)(B_RSTEP * g.ldb * 2);
@@ -235,20 +243,23 @@ void gemm_kernel(GArgs g, OptArgs a) {
   // Byte addresses of this lane's fragment reads in stage buffer 0, k-step 0, with the
   // chunk index swizzled as the loads placed it; buffers and k-steps are immediates.
   const uint32_t lds0 = lds_addr(smem);
-  uint32_t a_ad[C::FM], b_ad[C::B_TR ? C::FN : C::KSTEPS];
+  // A wave of k-split group ks reads k-steps ks*KPW .. ks*KPW + KPW-1 of each stage.
+  uint32_t a_ad[C::FM], b_ad[C::B_TR ? C::FN : C::KPW];
+  const int kr0 = ks * C::KPW * 16;  // first k row of this wave in a stage
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm)
-    a_ad[fm] = lds0 + 2u * (uint32_t)((8 * hi + r4) * C::BM + 8 * (((wave_m0 + 32 * fm) / 8) ^ (4 * r4)) + 16 * half +
-                                      4 * c4);
+    a_ad[fm] = lds0 + 2u * (uint32_t)((kr0 + 8 * hi + r4) * C::BM + 8 * (((wave_m0 + 32 * fm) / 8) ^ (4 * r4)) +
+                                      16 * half + 4 * c4);
   if constexpr (C::B_TR) {
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn)
-      b_ad[fn] = lds0 + 2u * (uint32_t)(C::b_base(0) + (8 * hi + r4) * C::BN +
+      b_ad[fn] = lds0 + 2u * (uint32_t)(C::b_base(0) + (kr0 + 8 * hi + r4) * C::BN +
                                         8 * (((wave_n0 + 32 * fn) / 8) ^ (4 * r4)) + 16 * half + 4 * c4);
   } else {
 #pragma unroll
-    for (int kk = 0; kk < C::KSTEPS; ++kk)
-      b_ad[kk] = lds0 + 2u * (uint32_t)(C::b_base(0) + (wave_n0 + l32) * C::BK + 8 * ((2 * kk + hi) ^ ((l32 >> 2) & 3)));
+    for (int kk = 0; kk < C::KPW; ++kk)
+      b_ad[kk] = lds0 + 2u * (uint32_t)(C::b_base(0) + (wave_n0 + l32) * C::BK +
+                                        8 * ((2 * (ks * C::KPW + kk) + hi) ^ ((l32 / C::KW) % C::B_CPR)));
   }
 
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
@@ -353,46 +364,39 @@ void gemm_kernel(GArgs g, OptArgs a) {
     };
 
     // ---- mainloop ----
-    // Stage st sits in ring buffer st % 4. Within a stage the k-steps' MFMAs run
+    // Stage st sits in ring buffer st % NSTAGE. Within a stage the k-steps' MFMAs run
     // back to back, each set reading the next set's fragments. Between the last two
     // sets every wave waits for its own loads of stage st+1 and for its LDS reads, the
-    // barrier then makes stage st+1 visible and frees buffer st % 4 (all its reads
+    // barrier then makes stage st+1 visible and frees buffer st % NSTAGE (all its reads
     // are done), and the loads of stage st+4 into that buffer are issued.
     Frag F0, F1;
     __syncthreads();  // the previous tile's epilogue is done with LDS
-    dma(std::integral_constant<int, 0>{}, 0);
-    dma(std::integral_constant<int, 1>{}, 1);
-    dma(std::integral_constant<int, 2>{}, 2);
-    dma(std::integral_constant<int, 3>{}, 3);
-    vm_wait_barrier<3 * LPS>();
+    static_for<0, C::NSTAGE>([&](auto b_c) { dma(b_c, decltype(b_c)::value); });
+    vm_wait_barrier<(C::NSTAGE - 1) * LPS>();
     static_for<0, NR>([&](auto r_c) {
       read_one(F0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, r_c);
     });
     auto stage = [&](auto R_c, int st) {
       constexpr int R = decltype(R_c)::value;
-      static_for<0, C::KSTEPS / 2>([&](auto p_c) {
+      static_for<0, C::KPW / 2>([&](auto p_c) {
         constexpr int kk = 2 * decltype(p_c)::value;
         lgkm_wait<0>();
         settle(F0);
         mma_reading(F0, F1, R_c, std::integral_constant<int, kk + 1>{}, [] {});
-        if constexpr (kk + 2 < C::KSTEPS) {
+        if constexpr (kk + 2 < C::KPW) {
           lgkm_wait<0>();
           settle(F1);
           mma_reading(F1, F0, R_c, std::integral_constant<int, kk + 2>{}, [] {});
         } else {
-          vm_wait_barrier<2 * LPS>();
+          vm_wait_barrier<(C::NSTAGE - 2) * LPS>();
           settle(F1);
-          mma_reading(F1, F0, std::integral_constant<int, (R + 1) % 4>{}, std::integral_constant<int, 0>{},
-                      [&] { dma(R_c, st + 4); });
+          mma_reading(F1, F0, std::integral_constant<int, (R + 1) % C::NSTAGE>{}, std::integral_constant<int, 0>{},
+                      [&] { dma(R_c, st + C::NSTAGE); });
         }
       });
     };
-    for (int st = 0; st < nst4; st += 4) {
-      stage(std::integral_constant<int, 0>{}, st);
-      stage(std::integral_constant<int, 1>{}, st + 1);
-      stage(std::integral_constant<int, 2>{}, st + 2);
-      stage(std::integral_constant<int, 3>{}, st + 3);
-    }
+    for (int st = 0; st < nstr; st += C::NSTAGE)
+      static_for<0, C::NSTAGE>([&](auto r_c) { stage(r_c, st + decltype(r_c)::value); });
     // the loads issued past the end still write LDS: let them land before it is reused
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 
@@ -411,17 +415,24 @@ void gemm_kernel(GArgs g, OptArgs a) {
     __syncthreads();  // every wave is done reading the operand stages
 #pragma unroll 1
     for (int c = 0; c < C::WN; ++c) {
-      if (wn == c) {
+      // k-split group 0 writes its partial tile, groups 1.. add theirs in order
+#pragma unroll 1
+      for (int kg = 0; kg < C::KS; ++kg) {
+        if (wn == c && ks == kg) {
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn)
+          for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
-          for (int fm = 0; fm < C::FM; ++fm)
+            for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              *reinterpret_cast<f32x4*>(E + (32 * fn + l32) * LDE + wave_m0 + 32 * fm + 8 * q + 4 * hi) =
-                  f32x4{acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3]};
+              for (int q = 0; q < 4; ++q) {
+                f32x4* e = reinterpret_cast<f32x4*>(E + (32 * fn + l32) * LDE + wave_m0 + 32 * fm + 8 * q + 4 * hi);
+                f32x4 x{acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3]};
+                if (kg > 0) x = *e + x;
+                *e = x;
+              }
+        }
+        __syncthreads();
       }
-      __syncthreads();
       const int nrow0 = n0 + c * C::TN;
       if constexpr (EPI == G_EPI_STORE || EPI == G_EPI_DX) {
         const __amdgpu_buffer_rsrc_t rO = make_rsrc(g.out, g.out_bytes);
@@ -552,15 +563,21 @@ void gemm_kernel(GArgs g, OptArgs a) {
 // ---------------------------------------------------------------------------
 // Launchers. Large problems use 256x256 workgroup tiles (8 waves of 128x64, two
 // per SIMD); problems with fewer such tiles than compute units use 128x128 tiles
-// (4 waves of 64x64, two workgroups per compute unit).
+// (4 waves of 64x64, two workgroups per compute unit), and when even those are
+// scarce (fewer than two per compute unit) 128x128 tiles with a 2-way in-workgroup
+// split-K (8 waves of 64x64, one workgroup per compute unit), so a compute unit
+// that holds a single tile still runs two waves per SIMD.
 // ---------------------------------------------------------------------------
-// Tile configurations (BM, BN, BK, WM, WN, B_TR, OCC); FORGE_*_CFG override them
-// at build time for tuning sweeps.
+// Tile configurations (BM, BN, BK, WM, WN, B_TR, OCC[, NSTAGE, KS]); FORGE_*_CFG
+// override them at build time for tuning sweeps.
 #ifndef FORGE_WGRAD_BIG_CFG
 #define FORGE_WGRAD_BIG_CFG 256, 256, 32, 2, 4, true, 2
 #endif
 #ifndef FORGE_WGRAD_SMALL_CFG
 #define FORGE_WGRAD_SMALL_CFG 128, 128, 32, 2, 2, true, 2
+#endif
+#ifndef FORGE_WGRAD_SPLIT_CFG
+#define FORGE_WGRAD_SPLIT_CFG 128, 128, 64, 2, 2, true, 2, 4, 2
 #endif
 #ifndef FORGE_DGRAD_BIG_CFG
 #define FORGE_DGRAD_BIG_CFG 256, 256, 32, 2, 4, false, 2
@@ -568,10 +585,15 @@ void gemm_kernel(GArgs g, OptArgs a) {
 #ifndef FORGE_DGRAD_SMALL_CFG
 #define FORGE_DGRAD_SMALL_CFG 128, 128, 32, 2, 2, false, 2
 #endif
+#ifndef FORGE_DGRAD_SPLIT_CFG
+#define FORGE_DGRAD_SPLIT_CFG 128, 128, 64, 2, 2, false, 2, 4, 2
+#endif
 using WgradBig = GCfg<FORGE_WGRAD_BIG_CFG>;
 using WgradSmall = GCfg<FORGE_WGRAD_SMALL_CFG>;
+using WgradSplit = GCfg<FORGE_WGRAD_SPLIT_CFG>;
 using DgradBig = GCfg<FORGE_DGRAD_BIG_CFG>;
 using DgradSmall = GCfg<FORGE_DGRAD_SMALL_CFG>;
+using DgradSplit = GCfg<FORGE_DGRAD_SPLIT_CFG>;
 
 static int g_num_cus() {
   static int n = 0;
@@ -595,25 +617,26 @@ static hipError_t g_launch(const GArgs& g, const OptArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <class Big>
-static bool use_big(const GArgs& g) {
-  const int big = ((g.M + Big::BM - 1) / Big::BM) * ((g.N + Big::BN - 1) / Big::BN);
-  return big >= g_num_cus();
+template <class C>
+static int g_tiles(const GArgs& g) {
+  return ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN);
+}
+
+// Calls f(C{}) with the tile configuration for this problem size.
+template <class Big, class Small, class Split, class F>
+static hipError_t g_pick(const GArgs& g, F&& f) {
+  if (g_tiles<Big>(g) >= g_num_cus()) return f(Big{});
+  if (g_tiles<Small>(g) >= 2 * g_num_cus()) return f(Small{});
+  return f(Split{});
 }
 
 template <int OPT>
 static hipError_t wgrad_opt_v2(int q8, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
-  const bool big = use_big<WgradBig>(g);
-  if (q8) {
-    if (sr) return big ? g_launch<WgradBig, G_EPI_OPT, OPT, true, true>(g, a, st)
-                       : g_launch<WgradSmall, G_EPI_OPT, OPT, true, true>(g, a, st);
-    return big ? g_launch<WgradBig, G_EPI_OPT, OPT, true, false>(g, a, st)
-               : g_launch<WgradSmall, G_EPI_OPT, OPT, true, false>(g, a, st);
-  }
-  if (sr) return big ? g_launch<WgradBig, G_EPI_OPT, OPT, false, true>(g, a, st)
-                     : g_launch<WgradSmall, G_EPI_OPT, OPT, false, true>(g, a, st);
-  return big ? g_launch<WgradBig, G_EPI_OPT, OPT, false, false>(g, a, st)
-             : g_launch<WgradSmall, G_EPI_OPT, OPT, false, false>(g, a, st);
+  return g_pick<WgradBig, WgradSmall, WgradSplit>(g, [&](auto c) {
+    using C = decltype(c);
+    if (q8) return sr ? g_launch<C, G_EPI_OPT, OPT, true, true>(g, a, st) : g_launch<C, G_EPI_OPT, OPT, true, false>(g, a, st);
+    return sr ? g_launch<C, G_EPI_OPT, OPT, false, true>(g, a, st) : g_launch<C, G_EPI_OPT, OPT, false, false>(g, a, st);
+  });
 }
 
 static uint32_t extent(int64_t rows, int64_t ld, int64_t es) { return (uint32_t)(rows * ld * es); }
@@ -640,8 +663,8 @@ hipError_t launch_wgrad_store_bf16(const void* X, const void* dY, const GemmDims
   GArgs g{reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(dY), d.ldx, d.lddy,
           d.in, d.out, d.T, dW, ld_dw, extent(d.T, d.ldx, 2), extent(d.T, d.lddy, 2), extent(d.out, ld_dw, 4)};
   OptArgs a{};
-  return use_big<WgradBig>(g) ? g_launch<WgradBig, G_EPI_STORE, FORGE_SGD, false, false>(g, a, st)
-                          : g_launch<WgradSmall, G_EPI_STORE, FORGE_SGD, false, false>(g, a, st);
+  return g_pick<WgradBig, WgradSmall, WgradSplit>(
+      g, [&](auto c) { return g_launch<decltype(c), G_EPI_STORE, FORGE_SGD, false, false>(g, a, st); });
 }
 
 hipError_t launch_dgrad_bf16(const void* dY, int64_t lddy, const void* W, int64_t ldw, void* dX, int64_t lddx,
@@ -649,8 +672,8 @@ hipError_t launch_dgrad_bf16(const void* dY, int64_t lddy, const void* W, int64_
   GArgs g{reinterpret_cast<const uint16_t*>(W), reinterpret_cast<const uint16_t*>(dY), ldw, lddy,
           n_in, T, n_out, dX, lddx, extent(n_out, ldw, 2), extent(T, lddy, 2), extent(T, lddx, 2)};
   OptArgs a{};
-  return use_big<DgradBig>(g) ? g_launch<DgradBig, G_EPI_DX, FORGE_SGD, false, false>(g, a, st)
-                           : g_launch<DgradSmall, G_EPI_DX, FORGE_SGD, false, false>(g, a, st);
+  return g_pick<DgradBig, DgradSmall, DgradSplit>(
+      g, [&](auto c) { return g_launch<decltype(c), G_EPI_DX, FORGE_SGD, false, false>(g, a, st); });
 }
 
 }  // namespace forge

@@ -102,6 +102,47 @@ def test_q8_states(opt):
     run_case(LayerSpec("q", 136, 320, 200, outlier_frac=0.01), opt, 3, config=98, state="q8", label="q8")
 
 
+# ---------------------------------------------------------------- tile configurations
+def _tile_config_shapes():
+    """(rows, cols) of C = (in, out) for wgrad or (in, T) for dgrad that select each
+    tile configuration of the launcher on this device: 256x256 tiles when there are
+    at least as many as compute units, else 128x128 tiles when there are at least two
+    per compute unit, else 128x128 tiles with the in-workgroup split-K."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    big = (4096, 256 * -(-cus // 16))
+    small = (4096, 128 * -(-cus // 16))
+    split = (1024, 520)
+    tiles = lambda mn, t: -(-mn[0] // t) * -(-mn[1] // t)
+    assert tiles(big, 256) >= cus
+    assert tiles(small, 256) < cus and tiles(small, 128) >= 2 * cus
+    assert tiles(split, 256) < cus and tiles(split, 128) < 2 * cus
+    return {"big": big, "small": small, "split": split}
+
+
+@pytest.mark.parametrize("cfg", ["big", "small", "split"])
+@pytest.mark.parametrize("state", ["f32", "q8"])
+def test_each_tile_configuration_fused(cfg, state):
+    n_in, n_out = _tile_config_shapes()[cfg]
+    rows = np.unique(np.concatenate([np.arange(0, n_out, max(1, n_out // 96)), [n_out - 1]]))
+    run_case(LayerSpec("c", n_out, n_in, 72), "adamw", 2, config=88, state=state, rows=rows,
+             label=f"tile config {cfg}")
+
+
+@pytest.mark.parametrize("cfg", ["big", "small", "split"])
+def test_each_tile_configuration_dgrad(cfg):
+    f = _forge()
+    n_in, T = _tile_config_shapes()[cfg]
+    spec = LayerSpec("d", 136, n_in, T)
+    print(f"[case] dgrad tile config {cfg}: T={T} out=136 in={n_in}", flush=True)
+    W = draw_layer_init(87, 0, spec)
+    X, dY = draw_layer_batch(87, 0, 1, spec)
+    dX = f.dgrad(P.dev_bf16(dY), P.dev_bf16(W))
+    torch.cuda.synchronize()
+    ref = gemm.dgrad(f32_from_bf16_bits(dY), f32_from_bf16_bits(W))
+    bad, worst = P.dgrad_bf16_ok(P.host_bits(dX), ref)
+    assert bad == 0, f"{bad} dX elements beyond one bf16 ulp (worst {worst:.3g})"
+
+
 # ---------------------------------------------------------------- dgrad
 @pytest.mark.parametrize("shape,io", [((130, 200, 328), "bf16"), ((512, 384, 256), "bf16"),
                                       ((512, 256, 256), "f32"), ((70, 72, 100), "f32")])
