@@ -66,15 +66,15 @@ __host__ __device__ __forceinline__ float bits_f32(uint32_t u) {
 
 // bfloat16 bits of x rounded stochastically with random bits r16 < 2^16.
 __host__ __device__ __forceinline__ uint32_t sr_bf16_bits(float x, uint32_t r16) {
-  uint32_t u = f32_bits(x);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
-  return (u + r16) >> 16;
+  const uint32_t u = f32_bits(x);
+  const uint32_t rounded = (u + r16) >> 16, qnan = ((u >> 16) & 0x8000u) | 0x7FC0u;
+  return (u & 0x7FFFFFFFu) > 0x7F800000u ? qnan : rounded;  // a select, not a branch
 }
 // bfloat16 bits of x rounded to nearest, ties to even.
 __host__ __device__ __forceinline__ uint32_t rne_bf16_bits(float x) {
-  uint32_t u = f32_bits(x);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t u = f32_bits(x);
+  const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16, qnan = ((u >> 16) & 0x8000u) | 0x7FC0u;
+  return (u & 0x7FFFFFFFu) > 0x7F800000u ? qnan : rounded;
 }
 __host__ __device__ __forceinline__ float bf16_bits_f32(uint32_t b) { return bits_f32(b << 16); }
 

@@ -30,21 +30,6 @@ struct TileCfg {
   static_assert(KS == 1 || (KS == 2 && FN % 2 == 0), "split-K of 1 or 2 wave groups");
 };
 
-// XOR swizzle of 32-byte column groups within an LDS row of a bf16 stage, so the
-// rows one transpose read touches (k, k+1, k+2, k+3 and k+8..k+11) fall in
-// different banks.
-__device__ __forceinline__ int swz(int row) { return (row & 3) | ((row >> 1) & 4); }
-
-__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t* p) {
-  typedef __bf16 v4bf_t __attribute__((__vector_size__(8)));
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Wold-style-cast"
-  auto lp = (__attribute__((address_space(3))) v4bf_t*)(const_cast<uint16_t*>(p));
-#pragma clang diagnostic pop
-  v4bf_t r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp);
-  return __builtin_bit_cast(bf16x4, r);
-}
-
 // XCD-aware tile order: consecutive workgroup ids are dealt round-robin to the
 // 8 XCDs, so remap them so each XCD walks a contiguous range of tiles, and walk
 // that range in column groups so concurrently resident tiles share X/dY panels

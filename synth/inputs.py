@@ -171,6 +171,18 @@ def _llama8b_layers(T: int) -> List[LayerSpec]:
     ]
 
 
+def _llama8b_tp8_layers(T: int) -> List[LayerSpec]:
+    """One GPU's shards of the seven linears under 8-way tensor parallelism: the
+    column-parallel ones (q, k, v, gate, up) split `out`, the row-parallel ones (o,
+    down) split `in`; every GPU sees all T tokens."""
+    h, kv, ff, tp = 4096, 1024, 14336, 8
+    return [
+        LayerSpec("q_proj", h // tp, h, T), LayerSpec("k_proj", kv // tp, h, T), LayerSpec("v_proj", kv // tp, h, T),
+        LayerSpec("o_proj", h, h // tp, T), LayerSpec("gate_proj", ff // tp, h, T), LayerSpec("up_proj", ff // tp, h, T),
+        LayerSpec("down_proj", h, ff // tp, T),
+    ]
+
+
 @dataclass
 class Workload:
     """A named workload: its layers, optimizer(s), step count and state format."""
@@ -200,6 +212,8 @@ WORKLOADS: Dict[str, Workload] = {
     "qwen14b_mlp_4096": Workload(4, "qwen14b_mlp_4096", [LayerSpec("mlp_up", 17408, 5120, 4096)], steps=10,
                                  optimizers=("adamw", "nadam", "radam", "lion", "rmsprop", "adagrad",
                                              "sgd", "sgd_momentum")),
+    # one GPU's 8-way tensor-parallel shards of the Llama-3.1-8B-shaped layer, 8192 tokens
+    "llama8b_tp8_8192": Workload(6, "llama8b_tp8_8192", _llama8b_tp8_layers(8192), steps=1),
 }
 
 

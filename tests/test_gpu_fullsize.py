@@ -74,6 +74,14 @@ def test_llama8b_decoder_layer_all_seven_linears():
         _run_layer(f, wl, li, spec, "adamw", 1, {1}, 128)
 
 
+def test_llama8b_tp8_shards_all_seven_linears():
+    # one GPU's 8-way tensor-parallel shards (k/v: 128 x 4096, 32 tiles of 128x128)
+    f = _forge()
+    wl = WORKLOADS["llama8b_tp8_8192"]
+    for li, spec in enumerate(wl.layers):
+        _run_layer(f, wl, li, spec, "adamw", 2, {1, 2}, 96)
+
+
 @pytest.mark.timeout(600)
 def test_down_proj_int8_states_twenty_steps():
     f = _forge()

@@ -64,3 +64,48 @@ def test_too_many_boundary_flips_fail():
     ok, n, _, _ = P.bf16_step_explained(gpu, ref, "sgd", X, dY, W, None, None, hp, 1, 77, "bf16", "f32",
                                         np.arange(spec.out))
     assert n == 3 and not ok
+
+
+def test_moment_checker_floor_and_drift():
+    spec, W, X, dY, hp, z, ref = _case("adamw")
+    m = ref["m"].astype(np.float64)
+    assert P.state_ok(m.copy(), m)[0] == 0
+    # a drift of 2e-4 relative at a large element fails; below the 0.1*rms floor it is absorbed
+    rms = float(np.sqrt(np.mean(m * m)))
+    big = int(np.argmax(np.abs(m)))
+    small = int(np.argmin(np.abs(m)))
+    drift = m.copy().ravel()
+    drift[big] *= 1 + 2e-4
+    assert P.state_ok(drift.reshape(m.shape), m)[0] == 1
+    drift = m.copy().ravel()
+    drift[small] += 0.5e-4 * 0.1 * rms
+    assert P.state_ok(drift.reshape(m.shape), m)[0] == 0
+
+
+def test_int8_code_checker_allows_one_step_only():
+    ref = np.array([[-127, -3, 0, 5, 127]], dtype=np.int8)
+    assert P.codes_ok(ref.copy(), ref)[0] == 0
+    one = ref.copy()
+    one[0, 1] += 1
+    assert P.codes_ok(one, ref)[:2] == (0, 1)
+    two = ref.copy()
+    two[0, 3] += 2
+    assert P.codes_ok(two, ref)[0] == 1
+
+
+def test_dgrad_checker_one_ulp_and_summation_bound():
+    from synth import bf16_bits_from_f32
+    rng = np.random.default_rng(5)
+    ref = rng.normal(size=(16, 32))
+    bits = bf16_bits_from_f32(ref.astype(np.float32)).reshape(ref.shape)
+    assert P.dgrad_bf16_ok(bits, ref)[0] == 0
+    off = bits.copy()
+    off[3, 4] = _shift(off[3, 4], 3)   # three bf16 steps away
+    assert P.dgrad_bf16_ok(off, ref)[0] == 1
+    # the fp32 summation bound: an error of 1.5x the bound at one element fails
+    abs_sum = np.abs(ref) * 10
+    K = 64
+    gpu = ref.copy()
+    assert P.summation_bound_ok(gpu, ref, abs_sum, K)[0] == 0
+    gpu[2, 2] += 1.5 * K * 2.0 ** -24 * abs_sum[2, 2]
+    assert P.summation_bound_ok(gpu, ref, abs_sum, K)[0] == 1
