@@ -26,7 +26,7 @@ from typing import Dict, Optional
 
 import numpy as np
 
-from . import gemm, optim, q8, rounding
+from . import fp8, gemm, optim, q8, rounding
 
 
 def _widen(a: np.ndarray, io: str) -> np.ndarray:
@@ -74,12 +74,15 @@ def wgrad_step(opt: str, X: np.ndarray, dY: np.ndarray, W: np.ndarray,
                seed: int, *, io: str = "bf16", state: str = "f32", sr: bool = True,
                rows: Optional[np.ndarray] = None,
                m_scale: Optional[np.ndarray] = None, v_scale: Optional[np.ndarray] = None,
-               g: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+               g: Optional[np.ndarray] = None, x_fmt: Optional[str] = None, dy_fmt: Optional[str] = None,
+               x_scale: float = 1.0, dy_scale: float = 1.0) -> Dict[str, np.ndarray]:
     """One step. With `rows`, W/m/v/scales hold only those output rows.
 
     X [T, in], dY [T, out] and W are bf16 bit patterns (uint16) when io == "bf16",
-    float32 arrays when io == "f32". A precomputed float64 gradient `g` for the
-    selected rows may be passed to avoid recomputing it.
+    float32 arrays when io == "f32". With x_fmt / dy_fmt ("e4m3" or "e5m2") X / dY
+    are uint8 OCP FP8 codes of value code * x_scale / dy_scale (W stays in `io`).
+    A precomputed float64 gradient `g` for the selected rows may be passed to avoid
+    recomputing it.
     Returns W (stored format), m, v (stored format), m_scale, v_scale, and the
     float64 intermediates g, theta, m64, v64, x32 for tolerance checks.
     """
@@ -87,7 +90,9 @@ def wgrad_step(opt: str, X: np.ndarray, dY: np.ndarray, W: np.ndarray,
     n_in = X.shape[1]
     rows = np.arange(n_out) if rows is None else np.asarray(rows)
     if g is None:
-        g = gemm.wgrad_rows(_widen(X, io), _widen(dY, io), rows)
+        Xw = fp8.dequant(X, x_fmt, x_scale) if x_fmt else _widen(X, io)
+        dYw = fp8.dequant(dY, dy_fmt, dy_scale) if dy_fmt else _widen(dY, io)
+        g = gemm.wgrad_rows(Xw, dYw, rows)
     theta0 = _widen(W, io)
     slots = optim.SLOTS[opt]
     m64 = load_state("m", m, m_scale, state) if "m" in slots else None
