@@ -7,6 +7,8 @@ then the fused dW = dY^T X + optimizer update of W and its moments. The default
 workload is the q_proj-shaped layer (W 4096x4096 bf16, fp32 AdamW moments,
 8192 tokens, stochastic rounding). `value` counts the algorithmic FLOPs of both
 GEMMs of every step (4 * T * out * in per layer) over the timed wall time.
+With --inputs fp8 the fused step reads X as E4M3 and dY as E5M2 codes, each with
+one float32 scale (dgrad keeps bf16), and its roofline peak is the FP8 one.
 
 Besides the JSON line's contract fields it reports:
   roofline      the fused kernel's achieved TFLOP/s (2*T*out*in per launch over its
@@ -29,7 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "fused wgrad+AdamW TFLOP/s & ms/layer (Llama-8B shapes), % MFMA peak, dW HBM bytes"
-PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA peaks
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8": 5000.0}   # MI355X dense MFMA peaks
 HBM_GBS = 8000.0
 
 
@@ -52,6 +54,9 @@ def parse():
     p.add_argument("--cold-calls", type=int, default=10,
                    help="fused calls of the first layer timed after a 1 GiB write that evicts the memory-side cache")
     p.add_argument("--opt", default="adamw")
+    p.add_argument("--inputs", default="native", choices=("native", "fp8"),
+                   help="fp8: the fused step reads X as E4M3 and dY as E5M2 codes with per-tensor scales "
+                        "(W and dgrad stay bf16)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-unfused", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -73,6 +78,10 @@ def _counter_means(db: str, counter: str) -> dict:
         if d["counter_name"] == counter:
             acc.setdefault(d["kernel_name"], []).append(float(d["value"]))
     return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def _traffic_name(args) -> str:
+    return args.workload + ("_fp8" if args.inputs == "fp8" else "")
 
 
 def record_traffic(args) -> int:
@@ -99,8 +108,8 @@ def record_traffic(args) -> int:
     rec = {"workload": args.workload, "opt": args.opt, "kernel_source_hash": kernel_source_hash(),
            "bytes_per_launch": int(round(fetch + write)), "fetch_bytes": int(round(fetch)),
            "write_bytes": int(round(write)), "fetch_scale": f_scale, "write_scale": w_scale,
-           "source": f"profiles/wgrad_fused_{args.workload}.md"}
-    out = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+           "inputs": args.inputs, "source": f"profiles/wgrad_fused_{_traffic_name(args)}.md"}
+    out = os.path.join(ROOT, "profiles", f"traffic_{_traffic_name(args)}.json")
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
@@ -135,7 +144,7 @@ def main() -> int:
     import torch
 
     import optimizer_gemm_amd as forge
-    from synth import WORKLOADS, draw_layer_batch, draw_layer_init, llama8b_stack
+    from synth import WORKLOADS, draw_layer_batch, draw_layer_batch_fp8, draw_layer_init, llama8b_stack
 
     if args.workload == "stack":
         layers = llama8b_stack(8192, 32)
@@ -147,6 +156,10 @@ def main() -> int:
     dev = torch.device("cuda:0")
     io = layers[0].io
     tdt = torch.bfloat16 if io == "bf16" else torch.float32
+    fp8 = args.inputs == "fp8"
+    if fp8 and (io != "bf16" or state != "f32"):
+        print("FP8 inputs need bf16 weights and float32 moments", file=sys.stderr)
+        return 2
 
     def to_dev(a):
         if io == "bf16":
@@ -163,7 +176,17 @@ def main() -> int:
         key = (spec.out, spec.inn, spec.T)
         if key not in shape_bufs:
             X, dY = draw_layer_batch(wl_config, li, 1, spec)
-            shape_bufs[key] = (to_dev(X), to_dev(dY), torch.empty((spec.T, spec.inn), dtype=tdt, device=dev))
+            bufs = [to_dev(X), to_dev(dY), torch.empty((spec.T, spec.inn), dtype=tdt, device=dev), None, None]
+            if fp8:
+                # the fused step reads FP8 codes; dgrad keeps the bf16 dY
+                Xq, dYq, sx, sd = draw_layer_batch_fp8(wl_config, li, 1, spec, "e4m3", "e5m2")
+                bufs[0] = torch.from_numpy(Xq).to(dev).view(torch.float8_e4m3fn)
+                bufs.append(torch.from_numpy(dYq).to(dev).view(torch.float8_e5m2))
+                bufs[3] = torch.tensor([sx], dtype=torch.float32, device=dev)
+                bufs[4] = torch.tensor([sd], dtype=torch.float32, device=dev)
+            else:
+                bufs.append(bufs[1])
+            shape_bufs[key] = tuple(bufs)
         if args.workload == "stack":
             if key not in shape_w0:
                 shape_w0[key] = to_dev(draw_layer_init(wl_config, li, spec))
@@ -176,7 +199,8 @@ def main() -> int:
     torch.cuda.synchronize()
     resident = torch.cuda.memory_allocated()
     print(f"[bench] setup {time.perf_counter() - t0:.1f}s: {len(layers)} layer(s), workload {args.workload}, "
-          f"opt {opt}, states {state}, resident {resident / 2**30:.2f} GiB", file=sys.stderr, flush=True)
+          f"opt {opt}, states {state}, inputs {args.inputs}, resident {resident / 2**30:.2f} GiB",
+          file=sys.stderr, flush=True)
     hyper = forge.make_hyper(opt, stochastic_round=int(sr))
 
     step_counter = [0]
@@ -185,11 +209,11 @@ def main() -> int:
         step_counter[0] += 1
         t = step_counter[0]
         for k, (spec, W, m, v, ms, vs, seed) in enumerate(per_layer):
-            X, dY, dX = shape_bufs[(spec.out, spec.inn, spec.T)]
+            X, dY, dX, xs, ds, dYf = shape_bufs[(spec.out, spec.inn, spec.T)]
             forge.dgrad(dY, W, dX)
             if fused_events is not None:
                 fused_events[k][0].record()
-            forge.wgrad_step(X, dY, W, m, v, opt, hyper, t, seed, ms, vs)
+            forge.wgrad_step(X, dYf, W, m, v, opt, hyper, t, seed, ms, vs, x_scale=xs, dy_scale=ds)
             if fused_events is not None:
                 fused_events[k][1].record()
 
@@ -219,7 +243,7 @@ def main() -> int:
     fused_ms_layer = np.mean(np.array(fused_ms), axis=0)           # mean per layer
     fused_total = float(np.sum(fused_ms_layer))
     fused_tflops = sum(flops_gemm) / (fused_total * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[io]
+    peak = PEAK_TFLOPS["fp8" if fp8 else io]
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step, fused {fused_total:.3f} ms/step "
           f"({fused_tflops:.1f} TFLOP/s), wall {wall:.2f}s", file=sys.stderr, flush=True)
 
@@ -235,14 +259,15 @@ def main() -> int:
                   "unit": "us", "warm": pct([fused_ms[k][0] * 1e3 for k in range(args.steps)])}
     if args.cold_calls > 0:
         spec0, W0d, m0, v0, ms0, vs0, seed0 = per_layer[0]
-        X0, dY0, _ = shape_bufs[(spec0.out, spec0.inn, spec0.T)]
+        X0, _, _, xs0, ds0, dY0 = shape_bufs[(spec0.out, spec0.inn, spec0.T)]
         flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         cold = []
         for r in range(args.cold_calls):
             flush.fill_(float(r))
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            forge.wgrad_step(X0, dY0, W0d, m0, v0, opt, hyper, 30_000 + r, seed0, ms0, vs0)
+            forge.wgrad_step(X0, dY0, W0d, m0, v0, opt, hyper, 30_000 + r, seed0, ms0, vs0, x_scale=xs0,
+                             dy_scale=ds0)
             e1.record()
             torch.cuda.synchronize()
             cold.append(e0.elapsed_time(e1) * 1e3)
@@ -251,7 +276,7 @@ def main() -> int:
 
     # --- traffic from committed rocprofv3 counters (only if taken on this kernel source) ---
     traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+    tfile = os.path.join(ROOT, "profiles", f"traffic_{_traffic_name(args)}.json")
     if os.path.exists(tfile):
         with open(tfile) as f:
             tr = json.load(f)
@@ -262,17 +287,18 @@ def main() -> int:
     unfused = None
     if not args.no_unfused and args.workload != "stack":
         spec, W, m, v, ms, vs, seed = per_layer[0]
-        X, dY, dX = shape_bufs[(spec.out, spec.inn, spec.T)]
+        X, _, dX, xs, ds, dY = shape_bufs[(spec.out, spec.inn, spec.T)]
+        sc = dict(x_scale=xs, dy_scale=ds)
         n_rep = max(3, min(args.steps, 20))
         torch.cuda.synchronize()
         base = torch.cuda.memory_allocated()
         torch.cuda.reset_peak_memory_stats()
-        forge.wgrad_step(X, dY, W, m, v, opt, hyper, 10_000, seed, ms, vs)
+        forge.wgrad_step(X, dY, W, m, v, opt, hyper, 10_000, seed, ms, vs, **sc)
         torch.cuda.synchronize()
         fused_transient = torch.cuda.max_memory_allocated() - base
         torch.cuda.reset_peak_memory_stats()
         dW = torch.empty((spec.out, spec.inn), dtype=torch.float32, device=dev)
-        forge.wgrad_unfused(X, dY, W, m, v, opt, hyper, 10_001, seed, ms, vs, dW_workspace=dW)
+        forge.wgrad_unfused(X, dY, W, m, v, opt, hyper, 10_001, seed, ms, vs, dW_workspace=dW, **sc)
         torch.cuda.synchronize()
         unfused_transient = torch.cuda.max_memory_allocated() - base
         e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
@@ -280,10 +306,10 @@ def main() -> int:
         f_e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_rep)]
         for r in range(n_rep):
             f_e[r][0].record()
-            forge.wgrad_step(X, dY, W, m, v, opt, hyper, 10_002 + r, seed, ms, vs)
+            forge.wgrad_step(X, dY, W, m, v, opt, hyper, 10_002 + r, seed, ms, vs, **sc)
             f_e[r][1].record()
             e[r][0].record()
-            forge.wgrad(X, dY, dW)
+            forge.wgrad(X, dY, dW, **sc)
             e[r][1].record()
             forge.optimizer_step(dW, W, m, v, opt, hyper, 10_002 + r, seed, ms, vs)
             e[r][2].record()
@@ -309,9 +335,9 @@ def main() -> int:
         e0.record()
         dWs = []
         for (spec, W, m, v, ms, vs, seed) in per_layer:
-            X, dY, dX = shape_bufs[(spec.out, spec.inn, spec.T)]
+            X, dY, dX, xs, ds, dYf = shape_bufs[(spec.out, spec.inn, spec.T)]
             forge.dgrad(dY, W, dX)
-            dWs.append(forge.wgrad(X, dY))
+            dWs.append(forge.wgrad(X, dYf, x_scale=xs, dy_scale=ds))
         for (spec, W, m, v, ms, vs, seed), dW in zip(per_layer, dWs):
             forge.optimizer_step(dW, W, m, v, opt, hyper, 20_000, seed, ms, vs)
         e1.record()
@@ -342,12 +368,16 @@ def main() -> int:
         Xw = f32_from_bf16_bits(X) if io == "bf16" else X
         dYw = f32_from_bf16_bits(dY) if io == "bf16" else dY
         Ww = f32_from_bf16_bits(W0[rows]) if io == "bf16" else W0[rows]
+        fkw, Xs, dYs = {}, X, dY
+        if fp8:
+            Xs, dYs, sx, sd = draw_layer_batch_fp8(wl_config, 0, 1, spec, "e4m3", "e5m2")
+            fkw = dict(x_fmt="e4m3", dy_fmt="e5m2", x_scale=sx, dy_scale=sd)
         reps, times = 2, []
         for _ in range(reps):
             c0 = time.perf_counter()
             gemm.dgrad(dYw[:, rows], Ww)  # dX contribution of the sampled rows of W
-            ostep.wgrad_step(opt, X, dY, W0[rows], z if "m" in slots else None, z if "v" in slots else None,
-                             hp, 1, 1, io=io, sr=sr, rows=rows)
+            ostep.wgrad_step(opt, Xs, dYs, W0[rows], z if "m" in slots else None, z if "v" in slots else None,
+                             hp, 1, 1, io=io, sr=sr, rows=rows, **fkw)
             times.append(time.perf_counter() - c0)
         tcpu = float(np.median(times))
         flops = 4.0 * spec.T * n_rows * spec.inn
@@ -366,11 +396,11 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": io,
+        "dtype": "fp8 (e4m3 x e5m2) wgrad, bf16 dgrad" if fp8 else io,
         "data": "synthetic (seeded Gaussian inputs of the layer shapes; random-init weights)",
         "config": {"workload": args.workload, "layers": len(layers),
                    "shapes": sorted({f"{s.out}x{s.inn}" for s in layers}), "tokens": layers[0].T,
-                   "optimizer": opt, "states": state, "stochastic_round": bool(sr),
+                   "optimizer": opt, "states": state, "stochastic_round": bool(sr), "inputs": args.inputs,
                    "step": "dgrad(old W) then fused wgrad+optimizer, per layer"},
         "fused_ms_per_layer": [round(float(x), 4) for x in fused_ms_layer][:8],
         "fused_tflops": round(fused_tflops, 2),

@@ -43,7 +43,9 @@ typedef enum {
   FORGE_F32 = 0,  /* IEEE float32 */
   FORGE_BF16 = 1, /* bfloat16 */
   FORGE_I8 = 2,   /* int8 codes of a signed moment (block-64 absmax, scale/127) */
-  FORGE_U8 = 3    /* uint8 codes of sqrt(second moment) (block-64 absmax, scale/255) */
+  FORGE_U8 = 3,   /* uint8 codes of sqrt(second moment) (block-64 absmax, scale/255) */
+  FORGE_E4M3 = 4, /* OCP FP8 E4M3 input codes (value = decode(code) * scale[0]) */
+  FORGE_E5M2 = 5  /* OCP FP8 E5M2 input codes (value = decode(code) * scale[0]) */
 } forge_dtype;
 
 /* The eight element-wise optimizers the pages list (§3 Contributions, generality). */
@@ -58,10 +60,12 @@ typedef enum {
   FORGE_RADAM = 7
 } forge_opt;
 
-/* A 2-D row-major device tensor. `scale` is used only for FORGE_I8 / FORGE_U8
- * moments: float32 block scales, [rows, cols/64] with row pitch cols/64, one per
- * 64 consecutive elements of a row (§2 "Precision and fidelity": INT8 states
- * with blocks of 64). */
+/* A 2-D row-major device tensor. `scale` is used only for
+ *   - FORGE_I8 / FORGE_U8 moments: float32 block scales, [rows, cols/64] with row
+ *     pitch cols/64, one per 64 consecutive elements of a row (§2 "Precision and
+ *     fidelity": INT8 states with blocks of 64);
+ *   - FORGE_E4M3 / FORGE_E5M2 inputs: one float32 in device memory, the tensor's
+ *     dequantisation scale (element value = decoded code * scale[0]). */
 typedef struct {
   void* data;
   int32_t dtype; /* forge_dtype */
@@ -126,6 +130,11 @@ typedef struct {
  * driven by a counter hash: r16 = top 16 bits of the SplitMix64 output number
  * ((step << 32) | (o*in + i)) + 1 from state `seed`; bf16 = (bits(w32) + r16) >> 16
  * (NaN -> quiet NaN). T == 0 is allowed (zero gradient). Requires out*in < 2^32.
+ * FP8 inputs (the pages' outlook, §5): X FORGE_E4M3 and dY FORGE_E4M3 or
+ * FORGE_E5M2, each with its scale (see forge_tensor), with W FORGE_BF16 and
+ * float32 m, v; cols and ld of X and dY must be multiples of 16 (else
+ * FORGE_ERR_ALIGN); INT8 moments with FP8 inputs return FORGE_ERR_UNSUPPORTED. The
+ * gradient is (sum over tokens of the decoded code products) * scale_X * scale_dY.
  * Must be enqueued after forge_linear_dgrad of the same layer (which reads the old W).
  */
 int forge_linear_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge_tensor* W,
@@ -135,7 +144,8 @@ int forge_linear_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge
 /*
  * Input gradient dX = dY W (§5, limitations: read before the weight update).
  * dY [T, out], W [out, in], dX [T, in]; all FORGE_F32, or all FORGE_BF16
- * (bf16 output rounded to nearest-even from the FP32 accumulator).
+ * (bf16 output rounded to nearest-even from the FP32 accumulator). FP8 dY returns
+ * FORGE_ERR_UNSUPPORTED.
  */
 int forge_linear_dgrad(const forge_tensor* dY, const forge_tensor* W, forge_tensor* dX,
                        forge_stream_t stream);
@@ -144,6 +154,7 @@ int forge_linear_dgrad(const forge_tensor* dY, const forge_tensor* W, forge_tens
  * Unfused baseline, first half: the two-phase schedule the pages describe as
  * the standard one (§1, "the gradient floor"): the same GEMM, but dW [out, in]
  * is written to device memory as float32 (row pitch ld_dw >= in, multiple of 4).
+ * X and dY as for forge_linear_wgrad_step, FP8 included.
  */
 int forge_linear_wgrad(const forge_tensor* X, const forge_tensor* dY, float* dW, int64_t ld_dw,
                        forge_stream_t stream);

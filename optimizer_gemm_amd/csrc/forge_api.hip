@@ -45,6 +45,21 @@ int check_io(const forge_tensor* t, int dtype) {
   return FORGE_OK;
 }
 
+bool is_fp8(int dt) { return dt == FORGE_E4M3 || dt == FORGE_E5M2; }
+
+// FP8 input tensor (X, dY): one byte per element, 16-byte chunks along rows, and a
+// device pointer to its float32 dequantisation scale.
+int check_fp8(const forge_tensor* t, bool allow_e5m2) {
+  if (!t) return FORGE_ERR_NULL;
+  if (!t->data && t->rows != 0 && t->cols != 0) return FORGE_ERR_NULL;
+  if (!(t->dtype == FORGE_E4M3 || (allow_e5m2 && t->dtype == FORGE_E5M2))) return FORGE_ERR_DTYPE;
+  if (!t->scale) return FORGE_ERR_NULL;
+  int r = check_shape(t);
+  if (r) return r;
+  if (!aligned16(t->data) || ((uintptr_t)t->scale & 3u) || t->cols % 16 || t->ld % 16) return FORGE_ERR_ALIGN;
+  return FORGE_OK;
+}
+
 bool finite(double x) { return isfinite(x) != 0; }
 
 // The kernels address each tensor through 32-bit byte offsets below 2^31.
@@ -282,10 +297,17 @@ int forge_linear_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge
   if (r) return r;
   const int io = W->dtype;
   if (io != FORGE_F32 && io != FORGE_BF16) return FORGE_ERR_DTYPE;
-  if ((r = check_io(X, io)) || (r = check_io(dY, io)) || (r = check_io(W, io))) return r;
+  const bool f8 = is_fp8(X->dtype) || is_fp8(dY->dtype);
+  if (f8) {
+    if (io != FORGE_BF16) return FORGE_ERR_DTYPE;
+    if ((r = check_fp8(X, false)) || (r = check_fp8(dY, true)) || (r = check_io(W, io))) return r;
+  } else if ((r = check_io(X, io)) || (r = check_io(dY, io)) || (r = check_io(W, io))) {
+    return r;
+  }
   if (X->rows != dY->rows || X->cols != W->cols || dY->cols != W->rows) return FORGE_ERR_SHAPE;
   const int fmt = check_states(opt, io, W, m, v);
   if (fmt < 0) return fmt;
+  if (f8 && fmt == ST_Q8) return FORGE_ERR_UNSUPPORTED;
   if (W->rows * W->cols >= ((int64_t)1 << 32)) return FORGE_ERR_UNSUPPORTED;
   const int sl = opt_slots(opt);
   if (!fits_31(X) || !fits_31(dY) || !fits_31(W) || ((sl & 1) && !fits_31(m)) || ((sl & 2) && !fits_31(v)))
@@ -299,13 +321,16 @@ int forge_linear_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge
   const OptArgs a = make_args(W, m, v, opt, s, seed, step);
   const GemmDims d{(int32_t)X->rows, (int32_t)W->rows, (int32_t)W->cols, X->ld, dY->ld};
   const int sr = (io == FORGE_BF16 && hyper->stochastic_round) ? 1 : 0;
-  hipError_t e = launch_wgrad_fused(io == FORGE_BF16, fmt == ST_Q8, opt, sr, X->data, dY->data, d, a,
-                                    (hipStream_t)stream);
+  hipError_t e = f8 ? launch_wgrad_fused_f8(dY->dtype == FORGE_E5M2, opt, sr, X->data, X->scale, dY->data, dY->scale,
+                                            d, a, (hipStream_t)stream)
+                    : launch_wgrad_fused(io == FORGE_BF16, fmt == ST_Q8, opt, sr, X->data, dY->data, d, a,
+                                         (hipStream_t)stream);
   return e == hipSuccess ? FORGE_OK : FORGE_ERR_HIP;
 }
 
 int forge_linear_dgrad(const forge_tensor* dY, const forge_tensor* W, forge_tensor* dX, forge_stream_t stream) {
   if (!dY || !W || !dX) return FORGE_ERR_NULL;
+  if (is_fp8(dY->dtype)) return FORGE_ERR_UNSUPPORTED;
   const int io = W->dtype;
   if (io != FORGE_F32 && io != FORGE_BF16) return FORGE_ERR_DTYPE;
   int r;
@@ -325,9 +350,14 @@ int forge_linear_wgrad(const forge_tensor* X, const forge_tensor* dY, float* dW,
                        forge_stream_t stream) {
   if (!X || !dY || !dW) return FORGE_ERR_NULL;
   const int io = X->dtype;
-  if (io != FORGE_F32 && io != FORGE_BF16) return FORGE_ERR_DTYPE;
+  const bool f8 = is_fp8(X->dtype) || is_fp8(dY->dtype);
+  if (!f8 && io != FORGE_F32 && io != FORGE_BF16) return FORGE_ERR_DTYPE;
   int r;
-  if ((r = check_io(X, io)) || (r = check_io(dY, io))) return r;
+  if (f8) {
+    if ((r = check_fp8(X, false)) || (r = check_fp8(dY, true))) return r;
+  } else if ((r = check_io(X, io)) || (r = check_io(dY, io))) {
+    return r;
+  }
   if (X->rows != dY->rows) return FORGE_ERR_SHAPE;
   if (ld_dw < X->cols) return FORGE_ERR_SHAPE;
   if (!aligned16(dW) || ld_dw % 4) return FORGE_ERR_ALIGN;
@@ -338,7 +368,9 @@ int forge_linear_wgrad(const forge_tensor* X, const forge_tensor* dY, float* dW,
   if ((r = check_alias(outs, 1, ins, 2))) return r;
   if (dY->cols == 0 || X->cols == 0) return FORGE_OK;
   const GemmDims d{(int32_t)X->rows, (int32_t)dY->cols, (int32_t)X->cols, X->ld, dY->ld};
-  hipError_t e = launch_wgrad_store(io == FORGE_BF16, X->data, dY->data, d, dW, ld_dw, (hipStream_t)stream);
+  hipError_t e = f8 ? launch_wgrad_store_f8(dY->dtype == FORGE_E5M2, X->data, X->scale, dY->data, dY->scale, d, dW,
+                                            ld_dw, (hipStream_t)stream)
+                    : launch_wgrad_store(io == FORGE_BF16, X->data, dY->data, d, dW, ld_dw, (hipStream_t)stream);
   return e == hipSuccess ? FORGE_OK : FORGE_ERR_HIP;
 }
 

@@ -34,6 +34,7 @@
 namespace forge {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // Compile-time loop: f(std::integral_constant<int, 0>) ... f(<N-1>), always unrolled,
 // so small per-lane arrays indexed by it stay in registers.
@@ -47,62 +48,89 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 enum { G_EPI_STORE = 0, G_EPI_OPT = 1, G_EPI_DX = 2 };
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, bool B_TR_, int OCC_, int NSTAGE_ = 4, int KS_ = 1>
+// Operand formats of the GEMM core: bfloat16, or OCP FP8 (E4M3 / E5M2 per operand).
+enum { G_BF16 = 0, G_FP8 = 1 };
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_, bool B_TR_, int OCC_, int NSTAGE_ = 4, int KS_ = 1,
+          int IN_ = G_BF16, int FA_ = 0, int FB_ = 0>
 struct GCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
   static constexpr int OCC = OCC_;  // waves per SIMD
   static constexpr bool B_TR = B_TR_;
+  // IN = G_FP8: both operands are OCP 8-bit codes, A in format FA and B in format FB
+  // (0 = E4M3, 1 = E5M2), multiplied by v_mfma_f32_32x32x64_f8f6f4 (64 tokens per
+  // instruction) instead of v_mfma_f32_32x32x16_bf16 (16 tokens).
+  static constexpr bool F8 = IN_ == G_FP8;
+  static constexpr int FA = FA_, FB = FB_;
+  static constexpr int EB = F8 ? 1 : 2;        // bytes per operand element
+  static constexpr int KSTEP = F8 ? 64 : 16;   // tokens per MFMA
+  static_assert(!F8 || B_TR, "FP8 operands are token-major on both sides");
   // KS > 1: in-workgroup split-K. KS groups of WM x WN waves each take their own
   // k-steps of every stage; the partial tiles are summed through LDS in the epilogue.
   static constexpr int KS = KS_;
   static constexpr int NW = WM * WN * KS, NT = 64 * NW;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
-  static constexpr int KSTEPS = BK / 16;
+  static constexpr int KSTEPS = BK / KSTEP;
   static constexpr int KPW = KSTEPS / KS;  // k-steps of a stage per wave
-  // One LDS stage: A as BK rows of BM; B as BK rows of BN (B_TR) or BN rows of BK.
-  static constexpr int A_ELEMS = BK * BM, B_ELEMS = BK * BN;
+  // One LDS stage (bytes): A as BK rows of BM; B as BK rows of BN (B_TR) or BN rows of BK.
+  static constexpr int ROWA = BM * EB, ROWB = (B_TR ? BN : BK) * EB;
+  static constexpr int A_BYTES = BK * ROWA, B_BYTES = BK * BN * EB;
   // LDS: a ring of NSTAGE stages (the A parts of all stages first, then the B parts,
   // so every fragment read reaches its stage through an immediate offset below 64 KiB),
   // reused after the mainloop for one TN-row chunk of the finished tile as float rows
   // of BM + 4.
   static constexpr int NSTAGE = NSTAGE_;
   static_assert(NSTAGE >= 2, "ring");
-  static constexpr int a_base(int buf) { return buf * A_ELEMS; }
-  static constexpr int b_base(int buf) { return NSTAGE * A_ELEMS + buf * B_ELEMS; }
-  static constexpr int EPI_ELEMS = TN * (BM + 4) * 2;
-  static constexpr int RING_ELEMS = NSTAGE * (A_ELEMS + B_ELEMS);
-  static constexpr int SMEM_ELEMS = RING_ELEMS > EPI_ELEMS ? RING_ELEMS : EPI_ELEMS;
-  static constexpr int A_CPR = BM / 8;                     // 16-byte chunks per A row
-  static constexpr int B_CPR = B_TR ? BN / 8 : BK / 8;     // chunks per B row
-  static constexpr int PA = BK * A_CPR / NT, PB = BK * BN / 8 / NT;  // chunks per thread per stage
-  static_assert((BK * A_CPR) % NT == 0 && (BK * BN / 8) % NT == 0, "stage must split evenly over threads");
+  static constexpr int a_base(int buf) { return buf * A_BYTES; }
+  static constexpr int b_base(int buf) { return NSTAGE * A_BYTES + buf * B_BYTES; }
+  static constexpr int EPI_BYTES = TN * (BM + 4) * 4;
+  static constexpr int RING_BYTES = NSTAGE * (A_BYTES + B_BYTES);
+  static constexpr int SMEM_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
+  static constexpr int A_CPR = ROWA / 16, B_CPR = ROWB / 16;  // 16-byte chunks per row
+  static constexpr int PA = A_BYTES / 16 / NT, PB = B_BYTES / 16 / NT;  // chunks per thread per stage
+  static_assert((A_BYTES / 16) % NT == 0 && (B_BYTES / 16) % NT == 0, "stage must split evenly over threads");
   static_assert(NT % A_CPR == 0 && NT % B_CPR == 0, "a thread's chunks share a column");
-  static_assert(TM % 32 == 0 && TN % 32 == 0 && BK % 16 == 0 && KSTEPS % KS == 0 && KPW % 2 == 0, "tile shape");
-  // Chunk swizzles: rows read with the transpose read XOR their 16-byte chunk index
-  // with 4 * (row % 4), so the four rows one read touches land in four different
-  // 64-byte bank groups (needs 16 or more chunks per row); k-fast B rows of 4 or 8
-  // chunks (KW = 4 or 2 rows per 256 bytes) XOR it with (row / KW) % chunks, so 16
-  // consecutive rows cover all 16 bank groups. A thread's chunks are NT / chunks-per-row
-  // rows apart, a multiple of the swizzle period, so they all share one swizzled column.
+  static_assert(TM % 32 == 0 && TN % 32 == 0 && BK % KSTEP == 0 && KSTEPS % KS == 0 && KPW >= 1, "tile shape");
+  static_assert(F8 || KPW % 2 == 0, "bf16 stages hold an even number of k-steps per wave");
+  // Chunk swizzles (XOR of the 16-byte chunk index of a row):
+  //  * rows read with the 16-bit transpose read: 4 * (row % 4), so the four rows one read
+  //    touches land in four different 64-byte bank groups (16 or more chunks per row);
+  //  * rows read with the 8-bit transpose read (8 rows x 32 bytes per half-wave): with
+  //    16 or more chunks per row 2 * (row % 8), with 8 chunks 2 * ((row / 2) % 4), so the
+  //    eight 32-byte pieces fall in eight different 32-byte bank groups;
+  //  * k-fast bf16 B rows of 4 or 8 chunks (KW = 4 or 2 rows per 256 bytes):
+  //    (row / KW) % chunks, so 16 consecutive rows cover all 16 bank groups.
+  // A thread's chunks are NT / chunks-per-row rows apart, a multiple of the swizzle
+  // period, so they all share one swizzled column.
   static constexpr int KW = B_TR ? 1 : 16 / B_CPR;
-  static_assert(A_CPR >= 16 && (NT / A_CPR) % 4 == 0, "A swizzle");
-  static_assert(B_TR ? (B_CPR >= 16 && (NT / B_CPR) % 4 == 0)
+  static constexpr int TR_PERIOD = F8 ? 8 : 4;
+  __host__ __device__ static constexpr int swz_tr(int row, int cpr) {
+    return F8 ? (cpr >= 16 ? 2 * (row & 7) : 2 * ((row >> 1) & 3)) : 4 * (row & 3);
+  }
+  __host__ __device__ static constexpr int swz_b(int row) { return B_TR ? swz_tr(row, B_CPR) : (row / KW) % B_CPR; }
+  static_assert((F8 ? A_CPR >= 8 : A_CPR >= 16) && (NT / A_CPR) % TR_PERIOD == 0, "A swizzle");
+  static_assert(B_TR ? ((F8 ? B_CPR >= 8 : B_CPR >= 16) && (NT / B_CPR) % TR_PERIOD == 0)
                      : ((B_CPR == 4 || B_CPR == 8) && (NT / B_CPR) % 16 == 0), "B swizzle");
+  // transpose reads per operand fragment and the k rows one read covers
+  static constexpr int RA = F8 ? 4 : 2, RSTEP = F8 ? 8 : 4;
   // the 16-bit offset field of the LDS reads
-  static_assert(2 * ((NSTAGE - 1) * A_ELEMS + (KPW - 1) * 16 * BM + 4 * BM) < 65536, "A read offsets");
-  static_assert(2 * ((NSTAGE - 1) * B_ELEMS + (B_TR ? (KPW - 1) * 16 * BN + 4 * BN : 32 * (FN - 1) * BK)) < 65536,
+  static_assert((NSTAGE - 1) * A_BYTES + ((KPW - 1) * KSTEP + (RA - 1) * RSTEP) * ROWA < 65536, "A read offsets");
+  static_assert((NSTAGE - 1) * B_BYTES +
+                (B_TR ? ((KPW - 1) * KSTEP + (RA - 1) * RSTEP) * ROWB : 32 * (FN - 1) * ROWB) < 65536,
                 "B read offsets");
 };
 
 struct GArgs {
-  const uint16_t* A;  // wgrad: X; dgrad: W
-  const uint16_t* B;  // dY
-  int64_t lda, ldb;
+  const void* A;      // wgrad: X; dgrad: W
+  const void* B;      // dY
+  int64_t lda, ldb;   // row pitches in elements
   int32_t M, N, K;
   void* out;          // dW (float) or dX (bf16)
   int64_t ldo;
   uint32_t a_bytes, b_bytes, out_bytes;  // extents addressed through buffer resources
+  const float* a_scale;  // FP8 operands: dequantisation scale of A and of B (one float each)
+  const float* b_scale;
 };
 
 // A byte offset that no buffer resource here covers: loads through it return 0,
@@ -125,30 +153,46 @@ __device__ __forceinline__ u32x2 ds_tr_asm(uint32_t addr) {
   return r;
 }
 template <int OFF>
+__device__ __forceinline__ u32x2 ds_tr8_asm(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+template <int OFF>
 __device__ __forceinline__ u32x4 ds_b128_asm(uint32_t addr) {
   u32x4 r;
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
   return r;
 }
 // 32-bit LDS byte address of a __shared__ location.
-__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Wold-style-cast"
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t*)p;
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 #pragma clang diagnostic pop
 }
 // 16 bytes per lane from buffer offset off into LDS at dst + 16 * lane (zeros where
 // off is out of range).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* dst, uint32_t off) {
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* dst, uint32_t off) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Wold-style-cast"
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
 #pragma clang diagnostic pop
 }
+// The first or second of two objects, chosen at compile time (keeps two register sets
+// as separate variables, which the compiler keeps in registers, unlike an array).
+template <int I, class T>
+__device__ __forceinline__ T& pick2(T& a, T& b) {
+  if constexpr (I == 0)
+    return a;
+  else
+    return b;
+}
 // An empty asm that claims to rewrite v: any use of v after it is ordered after the
 // wait that precedes it.
 __device__ __forceinline__ void pin_reg(u32x2& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void pin_reg(u32x4& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin_reg(i32x8& v) { asm volatile("" : "+v"(v)); }
 // Waits until at most N LDS reads of this wave are outstanding (they complete in order).
 template <int N>
 __device__ __forceinline__ void lgkm_wait() {
@@ -207,17 +251,19 @@ __device__ __forceinline__ EpiRes epi_res(const OptArgs& a) {
 template <class C, int EPI, int OPT, bool Q8, bool SR>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
 void gemm_kernel(GArgs g, OptArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[C::SMEM_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::SMEM_BYTES];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int ks = wave / (C::WM * C::WN), wsp = wave % (C::WM * C::WN);
   const int wm = wsp % C::WM, wn = wsp / C::WM;
   const int wave_m0 = wm * C::TM, wave_n0 = wn * C::TN;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int r4 = (lane & 15) >> 2, c4 = lane & 3, half = (lane >> 4) & 1;
 
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A, g.a_bytes);
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.B, g.b_bytes);
+  // FP8 operands: the gradient is the product of the two dequantisation scales times
+  // the sum of code products
+  const float gscale = C::F8 ? g.a_scale[0] * g.b_scale[0] : 1.f;
 
   const int ntm = (g.M + C::BM - 1) / C::BM, ntn = (g.N + C::BN - 1) / C::BN;
   const int ntiles = ntm * ntn;
@@ -225,41 +271,58 @@ void gemm_kernel(GArgs g, OptArgs a) {
   // Stages are issued in groups of the ring size; stages past the last one, like rows
   // past the last token, load through out-of-range offsets and so hold zeros.
   const int nstr = ((nst + C::NSTAGE - 1) / C::NSTAGE) * C::NSTAGE;
-  constexpr int LPS = C::PA + C::PB;                              // loads per stage and wave
-  constexpr int NR = 2 * C::FM + (C::B_TR ? 2 * C::FN : C::FN);  // LDS reads per k-step and wave
+  constexpr int LPS = C::PA + C::PB;                                     // loads per stage and wave
+  constexpr int NRA = C::RA * C::FM, NRB = C::B_TR ? C::RA * C::FN : C::FN;
+  constexpr int NR = NRA + NRB;                                           // LDS reads per k-step and wave
   static_assert((C::NSTAGE - 1) * LPS <= 63, "vmcnt range");
 
   // Staging: the LDS slot of this thread's chunk j in a stage is tid + j*NT (a wave's
   // load fills 64 consecutive 16-byte slots); the swizzle picks the global chunk that
   // lands there. Chunk j is A_RSTEP (B_RSTEP) rows below chunk 0.
   const int a_row0 = tid / C::A_CPR, b_row0 = tid / C::B_CPR;
-  const int a_col = ((tid % C::A_CPR) ^ (4 * (a_row0 & 3))) * 8;
-  const int b_col = ((tid % C::B_CPR) ^ (C::B_TR ? 4 * (b_row0 & 3) : (b_row0 / C::KW) % C::B_CPR)) * 8;
+  const int a_colb = ((tid % C::A_CPR) ^ C::swz_tr(a_row0, C::A_CPR)) * 16;  // byte column in the row
+  const int b_colb = ((tid % C::B_CPR) ^ C::swz_b(b_row0)) * 16;
   constexpr int A_RSTEP = C::NT / C::A_CPR, B_RSTEP = C::NT / C::B_CPR;
-  const uint32_t a_rowb = (uint32_t)(A_RSTEP * g.lda * 2), a_stageb = (uint32_t)(C::BK * g.lda * 2);
-  const uint32_t b_rowb = (uint32_t)(B_RSTEP * g.ldb * 2);
-  const uint32_t b_stageb = C::B_TR ? (uint32_t)(C::BK * g.ldb * 2) : (uint32_t)(C::BK * 2);
+  const uint32_t a_rowb = (uint32_t)(A_RSTEP * g.lda * C::EB), a_stageb = (uint32_t)(C::BK * g.lda * C::EB);
+  const uint32_t b_rowb = (uint32_t)(B_RSTEP * g.ldb * C::EB);
+  const uint32_t b_stageb = C::B_TR ? (uint32_t)(C::BK * g.ldb * C::EB) : (uint32_t)(C::BK * C::EB);
 
   // Byte addresses of this lane's fragment reads in stage buffer 0, k-step 0, with the
-  // chunk index swizzled as the loads placed it; buffers and k-steps are immediates.
+  // chunk index swizzled as the loads placed it; buffers, k-steps and the reads of one
+  // fragment are immediates.
+  //  * 16-bit transpose read: lane (r4, c4, half, hi) reads row 8 hi + r4, elements
+  //    16 half + 4 c4 .. +3 of the 32-wide fragment; the lane receives 4 k of column l32.
+  //  * 8-bit transpose read: lane pair p = (lane % 16) / 2 reads row 32 hi + p, bytes
+  //    16 mh + 8 (lane % 2) .. +7 (mh = (lane / 16) % 2); the lane receives 8 k of
+  //    column l32. Operand byte b of lane l then holds k = 32 (l / 32) + b in both A and B.
   const uint32_t lds0 = lds_addr(smem);
   // A wave of k-split group ks reads k-steps ks*KPW .. ks*KPW + KPW-1 of each stage.
+  const int kr0 = ks * C::KPW * C::KSTEP;  // first k row of this wave in a stage
+  auto tr_addr = [&](int base, int rowbytes, int cpr, int col0) -> uint32_t {
+    int row, chunk, byte;
+    if constexpr (C::F8) {
+      row = kr0 + 32 * hi + ((lane & 15) >> 1);
+      chunk = col0 / 16 + ((lane >> 4) & 1);
+      byte = 8 * (lane & 1);
+    } else {
+      const int r4 = (lane & 15) >> 2, c4 = lane & 3;
+      row = kr0 + 8 * hi + r4;
+      chunk = col0 * 2 / 16 + 2 * ((lane >> 4) & 1) + (c4 >> 1);
+      byte = 8 * (c4 & 1);
+    }
+    return lds0 + (uint32_t)(base + row * rowbytes + 16 * (chunk ^ C::swz_tr(row, cpr)) + byte);
+  };
   uint32_t a_ad[C::FM], b_ad[C::B_TR ? C::FN : C::KPW];
-  const int kr0 = ks * C::KPW * 16;  // first k row of this wave in a stage
 #pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm)
-    a_ad[fm] = lds0 + 2u * (uint32_t)((kr0 + 8 * hi + r4) * C::BM + 8 * (((wave_m0 + 32 * fm) / 8) ^ (4 * r4)) +
-                                      16 * half + 4 * c4);
+  for (int fm = 0; fm < C::FM; ++fm) a_ad[fm] = tr_addr(C::a_base(0), C::ROWA, C::A_CPR, wave_m0 + 32 * fm);
   if constexpr (C::B_TR) {
 #pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn)
-      b_ad[fn] = lds0 + 2u * (uint32_t)(C::b_base(0) + (kr0 + 8 * hi + r4) * C::BN +
-                                        8 * (((wave_n0 + 32 * fn) / 8) ^ (4 * r4)) + 16 * half + 4 * c4);
+    for (int fn = 0; fn < C::FN; ++fn) b_ad[fn] = tr_addr(C::b_base(0), C::ROWB, C::B_CPR, wave_n0 + 32 * fn);
   } else {
 #pragma unroll
     for (int kk = 0; kk < C::KPW; ++kk)
-      b_ad[kk] = lds0 + 2u * (uint32_t)(C::b_base(0) + (wave_n0 + l32) * C::BK +
-                                        8 * ((2 * (ks * C::KPW + kk) + hi) ^ ((l32 / C::KW) % C::B_CPR)));
+      b_ad[kk] = lds0 + (uint32_t)(C::b_base(0) + (wave_n0 + l32) * C::ROWB +
+                                   16 * ((2 * (ks * C::KPW + kk) + hi) ^ C::swz_b(l32)));
   }
 
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
@@ -278,75 +341,107 @@ void gemm_kernel(GArgs g, OptArgs a) {
     // Only the k range is checked per load: a chunk past the M or N edge feeds
     // accumulator rows or columns that are never stored (the buffer resource still
     // bounds every access), while a k past the end must read as zero.
-    const uint32_t a_base0 = (uint32_t)((a_row0 * g.lda + m0 + a_col) * 2);
+    const uint32_t a_base0 = (uint32_t)((a_row0 * g.lda + m0) * C::EB + a_colb);
     uint32_t b_base0;
     if constexpr (C::B_TR)
-      b_base0 = (uint32_t)((b_row0 * g.ldb + n0 + b_col) * 2);
+      b_base0 = (uint32_t)((b_row0 * g.ldb + n0) * C::EB + b_colb);
     else
-      b_base0 = (uint32_t)(((int64_t)(n0 + b_row0) * g.ldb + b_col) * 2);
+      b_base0 = (uint32_t)((int64_t)(n0 + b_row0) * g.ldb * C::EB + b_colb);
     auto dma = [&](auto buf_c, int s) {
       constexpr int buf = decltype(buf_c)::value;
       const int k0 = s * C::BK;
 #pragma unroll
       for (int j = 0; j < C::PA; ++j) {
         const uint32_t off = (k0 + a_row0 + j * A_RSTEP < g.K) ? a_base0 + (uint32_t)s * a_stageb + (uint32_t)j * a_rowb : kOOB;
-        dma16(rA, smem + C::a_base(buf) + (j * C::NT + wave_u * 64) * 8, off);
+        dma16(rA, smem + C::a_base(buf) + (j * C::NT + wave_u * 64) * 16, off);
       }
 #pragma unroll
       for (int j = 0; j < C::PB; ++j) {
-        const int kb = C::B_TR ? k0 + b_row0 + j * B_RSTEP : k0 + b_col;
+        const int kb = C::B_TR ? k0 + b_row0 + j * B_RSTEP : k0 + b_colb / C::EB;
         const uint32_t off = (kb < g.K) ? b_base0 + (uint32_t)s * b_stageb + (uint32_t)j * b_rowb : kOOB;
-        dma16(rB, smem + C::b_base(buf) + (j * C::NT + wave_u * 64) * 8, off);
+        dma16(rB, smem + C::b_base(buf) + (j * C::NT + wave_u * 64) * 16, off);
       }
     };
-    // Operand fragments of one k-step as the LDS reads return them: two 4-deep
-    // halves per transposed operand, one 16-byte read per k-fast B operand.
-    struct Frag {
-      u32x2 a[C::FM][2];
-      u32x2 bt[C::B_TR ? C::FN : 1][2];
+    // Operand fragments of one k-step as the LDS reads return them: RA pieces of 8 bytes
+    // per transposed operand, one 16-byte read per k-fast B operand.
+    struct FragBf16 {
+      u32x2 a[C::FM][C::RA];
+      u32x2 bt[C::B_TR ? C::FN : 1][C::RA];
       u32x4 bk[C::B_TR ? 1 : C::FN];
     };
+    // FP8: one 8-register operand vector per fragment, filled read by read
+    struct FragF8 {
+      i32x8 a[C::FM];
+      i32x8 bt[C::FN];
+    };
+    using Frag = std::conditional_t<C::F8, FragF8, FragBf16>;
     // The r-th of the NR reads of a k-step's fragments.
     auto read_one = [&](Frag& F, auto buf_c, auto kk_c, auto r_c) {
       constexpr int buf = decltype(buf_c)::value, kk = decltype(kk_c)::value, r = decltype(r_c)::value;
-      if constexpr (r < 2 * C::FM) {
-        constexpr int fm = r / 2, h = r % 2;
-        F.a[fm][h] = ds_tr_asm<2 * (C::a_base(buf) + kk * 16 * C::BM + 4 * h * C::BM)>(a_ad[fm]);
+      if constexpr (r < NRA) {
+        constexpr int fm = r / C::RA, h = r % C::RA;
+        constexpr int off = C::a_base(buf) + (kk * C::KSTEP + h * C::RSTEP) * C::ROWA;
+        if constexpr (C::F8) {
+          const u32x2 x = ds_tr8_asm<off>(a_ad[fm]);
+          F.a[fm][2 * h] = (int)x.x;
+          F.a[fm][2 * h + 1] = (int)x.y;
+        } else {
+          F.a[fm][h] = ds_tr_asm<off>(a_ad[fm]);
+        }
       } else if constexpr (C::B_TR) {
-        constexpr int fn = (r - 2 * C::FM) / 2, h = (r - 2 * C::FM) % 2;
-        F.bt[fn][h] = ds_tr_asm<2 * (buf * C::B_ELEMS + kk * 16 * C::BN + 4 * h * C::BN)>(b_ad[fn]);
+        constexpr int fn = (r - NRA) / C::RA, h = (r - NRA) % C::RA;
+        constexpr int off = buf * C::B_BYTES + (kk * C::KSTEP + h * C::RSTEP) * C::ROWB;
+        if constexpr (C::F8) {
+          const u32x2 x = ds_tr8_asm<off>(b_ad[fn]);
+          F.bt[fn][2 * h] = (int)x.x;
+          F.bt[fn][2 * h + 1] = (int)x.y;
+        } else {
+          F.bt[fn][h] = ds_tr_asm<off>(b_ad[fn]);
+        }
       } else {
-        constexpr int fn = r - 2 * C::FM;
-        F.bk[fn] = ds_b128_asm<2 * (buf * C::B_ELEMS + 32 * fn * C::BK)>(b_ad[kk]);
+        constexpr int fn = r - NRA;
+        F.bk[fn] = ds_b128_asm<buf * C::B_BYTES + 32 * fn * C::ROWB>(b_ad[kk]);
       }
     };
     // Orders every later use of F's registers after the wait that precedes this.
     auto settle = [&](Frag& F) {
+      if constexpr (C::F8) {
 #pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm) {
-        pin_reg(F.a[fm][0]);
-        pin_reg(F.a[fm][1]);
-      }
-      if constexpr (C::B_TR) {
+        for (int fm = 0; fm < C::FM; ++fm) pin_reg(F.a[fm]);
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) {
-          pin_reg(F.bt[fn][0]);
-          pin_reg(F.bt[fn][1]);
-        }
+        for (int fn = 0; fn < C::FN; ++fn) pin_reg(F.bt[fn]);
+        return;
       } else {
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int h = 0; h < C::RA; ++h) pin_reg(F.a[fm][h]);
+      }
+      if constexpr (C::B_TR && !C::F8) {
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+          for (int h = 0; h < C::RA; ++h) pin_reg(F.bt[fn][h]);
+      } else if constexpr (!C::F8) {
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn) pin_reg(F.bk[fn]);
       }
     };
     auto mfma_one = [&](const Frag& F, auto i_c) {
       constexpr int fm = decltype(i_c)::value / C::FN, fn = decltype(i_c)::value % C::FN;
-      const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{F.a[fm][0].x, F.a[fm][0].y, F.a[fm][1].x, F.a[fm][1].y});
-      bf16x8 bv;
-      if constexpr (C::B_TR)
-        bv = __builtin_bit_cast(bf16x8, u32x4{F.bt[fn][0].x, F.bt[fn][0].y, F.bt[fn][1].x, F.bt[fn][1].y});
-      else
-        bv = __builtin_bit_cast(bf16x8, F.bk[fn]);
-      acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[fm][fn], 0, 0, 0);
+      if constexpr (C::F8) {
+        // block scales of 2^0 (E8M0 code 127): the tensor scales are applied to the sum
+        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[fm], F.bt[fn], acc[fm][fn], C::FA, C::FB, 0, 127,
+                                                                      0, 127);
+      } else {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{F.a[fm][0].x, F.a[fm][0].y, F.a[fm][1].x, F.a[fm][1].y});
+        bf16x8 bv;
+        if constexpr (C::B_TR)
+          bv = __builtin_bit_cast(bf16x8, u32x4{F.bt[fn][0].x, F.bt[fn][0].y, F.bt[fn][1].x, F.bt[fn][1].y});
+        else
+          bv = __builtin_bit_cast(bf16x8, F.bk[fn]);
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[fm][fn], 0, 0, 0);
+      }
     };
     // The MFMAs of fragment set F, with the reads of the next set G spread over the
     // first half of them and `after_first` run after the first; sched_barrier keeps
@@ -364,11 +459,12 @@ void gemm_kernel(GArgs g, OptArgs a) {
     };
 
     // ---- mainloop ----
-    // Stage st sits in ring buffer st % NSTAGE. Within a stage the k-steps' MFMAs run
-    // back to back, each set reading the next set's fragments. Between the last two
-    // sets every wave waits for its own loads of stage st+1 and for its LDS reads, the
-    // barrier then makes stage st+1 visible and frees buffer st % NSTAGE (all its reads
-    // are done), and the loads of stage st+4 into that buffer are issued.
+    // Stage st sits in ring buffer st % NSTAGE. The k-steps' MFMAs run back to back,
+    // each set reading the next set's fragments (two register sets alternate). Before
+    // the last k-step of a stage every wave waits for its own loads of stage st+1 and
+    // for its LDS reads, the barrier then makes stage st+1 visible and frees buffer
+    // st % NSTAGE (all its reads are done), and the loads of stage st + NSTAGE into
+    // that buffer are issued.
     Frag F0, F1;
     __syncthreads();  // the previous tile's epilogue is done with LDS
     static_for<0, C::NSTAGE>([&](auto b_c) { dma(b_c, decltype(b_c)::value); });
@@ -376,21 +472,22 @@ void gemm_kernel(GArgs g, OptArgs a) {
     static_for<0, NR>([&](auto r_c) {
       read_one(F0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, r_c);
     });
+    static_assert((C::NSTAGE * C::KPW) % 2 == 0, "register sets alternate evenly over a round of the ring");
     auto stage = [&](auto R_c, int st) {
       constexpr int R = decltype(R_c)::value;
-      static_for<0, C::KPW / 2>([&](auto p_c) {
-        constexpr int kk = 2 * decltype(p_c)::value;
-        lgkm_wait<0>();
-        settle(F0);
-        mma_reading(F0, F1, R_c, std::integral_constant<int, kk + 1>{}, [] {});
-        if constexpr (kk + 2 < C::KPW) {
+      static_for<0, C::KPW>([&](auto kk_c) {
+        constexpr int kk = decltype(kk_c)::value;
+        constexpr int cur = (R * C::KPW + kk) % 2;
+        Frag& Fc = pick2<cur>(F0, F1);
+        Frag& Fn = pick2<1 - cur>(F0, F1);
+        if constexpr (kk + 1 < C::KPW) {
           lgkm_wait<0>();
-          settle(F1);
-          mma_reading(F1, F0, R_c, std::integral_constant<int, kk + 2>{}, [] {});
+          settle(Fc);
+          mma_reading(Fc, Fn, R_c, std::integral_constant<int, kk + 1>{}, [] {});
         } else {
           vm_wait_barrier<(C::NSTAGE - 2) * LPS>();
-          settle(F1);
-          mma_reading(F1, F0, std::integral_constant<int, (R + 1) % C::NSTAGE>{}, std::integral_constant<int, 0>{},
+          settle(Fc);
+          mma_reading(Fc, Fn, std::integral_constant<int, (R + 1) % C::NSTAGE>{}, std::integral_constant<int, 0>{},
                       [&] { dma(R_c, st + C::NSTAGE); });
         }
       });
@@ -440,7 +537,8 @@ void gemm_kernel(GArgs g, OptArgs a) {
         for (int k = 0; k < NV; ++k) {
           const int vi = tid + k * C::NT, row = vi / VPR, col = (vi % VPR) * 4;
           const int n = nrow0 + row, m = m0 + col;
-          const f32x4 x = *reinterpret_cast<const f32x4*>(E + row * LDE + col);
+          f32x4 x = *reinterpret_cast<const f32x4*>(E + row * LDE + col);
+          if constexpr (C::F8) x = x * gscale;
           const bool ok = n < g.N && m < g.M;
           if constexpr (EPI == G_EPI_STORE) {
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rO,
@@ -495,7 +593,8 @@ void gemm_kernel(GArgs g, OptArgs a) {
         for (int k = 0; k < KB; ++k) {
           const int vi = tid + (kb + k) * C::NT, row = vi / VPR, col = (vi % VPR) * 4;
           const int o = nrow0 + row, i = m0 + col;
-          const f32x4 gx = *reinterpret_cast<const f32x4*>(E + row * LDE + col);
+          f32x4 gx = *reinterpret_cast<const f32x4*>(E + row * LDE + col);
+          if constexpr (C::F8) gx = gx * gscale;
           const float gg[4] = {gx.x, gx.y, gx.z, gx.w};
           float w[4] = {bits_f32(wb[k].x << 16), bits_f32(wb[k].x & 0xFFFF0000u), bits_f32(wb[k].y << 16),
                         bits_f32(wb[k].y & 0xFFFF0000u)};
@@ -588,6 +687,19 @@ void gemm_kernel(GArgs g, OptArgs a) {
 #ifndef FORGE_DGRAD_SPLIT_CFG
 #define FORGE_DGRAD_SPLIT_CFG 128, 128, 64, 2, 2, false, 2, 4, 2
 #endif
+// FP8 operands (X in E4M3, dY in format FB): 64-token stages, one MFMA k-step each. The
+// large tile runs 4 waves of 128x128 (one per SIMD, 512 registers each): two sets of
+// 8-register FP8 fragments would not fit next to 128 accumulators at two waves per SIMD.
+#ifndef FORGE_WGRAD_F8_BIG_CFG
+#define FORGE_WGRAD_F8_BIG_CFG 256, 256, 64, 2, 2, true, 1, 4, 1
+#endif
+#ifndef FORGE_WGRAD_F8_SMALL_CFG
+#define FORGE_WGRAD_F8_SMALL_CFG 128, 128, 64, 2, 2, true, 2, 4, 1
+#endif
+template <int FB>
+using WgradF8Big = GCfg<FORGE_WGRAD_F8_BIG_CFG, G_FP8, 0, FB>;
+template <int FB>
+using WgradF8Small = GCfg<FORGE_WGRAD_F8_SMALL_CFG, G_FP8, 0, FB>;
 using WgradBig = GCfg<FORGE_WGRAD_BIG_CFG>;
 using WgradSmall = GCfg<FORGE_WGRAD_SMALL_CFG>;
 using WgradSplit = GCfg<FORGE_WGRAD_SPLIT_CFG>;
@@ -643,7 +755,7 @@ static uint32_t extent(int64_t rows, int64_t ld, int64_t es) { return (uint32_t)
 
 hipError_t launch_wgrad_fused_bf16(int state_q8, int opt, int sr, const void* X, const void* dY, const GemmDims& d,
                                    const OptArgs& a, hipStream_t st) {
-  GArgs g{reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(dY), d.ldx, d.lddy,
+  GArgs g{X, dY, d.ldx, d.lddy,
           d.in, d.out, d.T, nullptr, 0, extent(d.T, d.ldx, 2), extent(d.T, d.lddy, 2), 0};
   switch (opt) {
     case FORGE_ADAMW: return wgrad_opt_v2<FORGE_ADAMW>(state_q8, sr, g, a, st);
@@ -660,16 +772,61 @@ hipError_t launch_wgrad_fused_bf16(int state_q8, int opt, int sr, const void* X,
 
 hipError_t launch_wgrad_store_bf16(const void* X, const void* dY, const GemmDims& d, float* dW, int64_t ld_dw,
                                    hipStream_t st) {
-  GArgs g{reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(dY), d.ldx, d.lddy,
+  GArgs g{X, dY, d.ldx, d.lddy,
           d.in, d.out, d.T, dW, ld_dw, extent(d.T, d.ldx, 2), extent(d.T, d.lddy, 2), extent(d.out, ld_dw, 4)};
   OptArgs a{};
   return g_pick<WgradBig, WgradSmall, WgradSplit>(
       g, [&](auto c) { return g_launch<decltype(c), G_EPI_STORE, FORGE_SGD, false, false>(g, a, st); });
 }
 
+template <int OPT, int FB>
+static hipError_t wgrad_opt_f8(int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
+  if (g_tiles<WgradF8Big<FB>>(g) >= g_num_cus())
+    return sr ? g_launch<WgradF8Big<FB>, G_EPI_OPT, OPT, false, true>(g, a, st)
+              : g_launch<WgradF8Big<FB>, G_EPI_OPT, OPT, false, false>(g, a, st);
+  return sr ? g_launch<WgradF8Small<FB>, G_EPI_OPT, OPT, false, true>(g, a, st)
+            : g_launch<WgradF8Small<FB>, G_EPI_OPT, OPT, false, false>(g, a, st);
+}
+
+template <int FB>
+static hipError_t wgrad_fused_f8(int opt, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
+  switch (opt) {
+    case FORGE_ADAMW: return wgrad_opt_f8<FORGE_ADAMW, FB>(sr, g, a, st);
+    case FORGE_SGD: return wgrad_opt_f8<FORGE_SGD, FB>(sr, g, a, st);
+    case FORGE_SGD_MOMENTUM: return wgrad_opt_f8<FORGE_SGD_MOMENTUM, FB>(sr, g, a, st);
+    case FORGE_LION: return wgrad_opt_f8<FORGE_LION, FB>(sr, g, a, st);
+    case FORGE_RMSPROP: return wgrad_opt_f8<FORGE_RMSPROP, FB>(sr, g, a, st);
+    case FORGE_ADAGRAD: return wgrad_opt_f8<FORGE_ADAGRAD, FB>(sr, g, a, st);
+    case FORGE_NADAM: return wgrad_opt_f8<FORGE_NADAM, FB>(sr, g, a, st);
+    case FORGE_RADAM: return wgrad_opt_f8<FORGE_RADAM, FB>(sr, g, a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_wgrad_fused_f8(int dy_e5m2, int opt, int sr, const void* X, const float* x_scale, const void* dY,
+                                 const float* dy_scale, const GemmDims& d, const OptArgs& a, hipStream_t st) {
+  GArgs g{X, dY, d.ldx, d.lddy, d.in, d.out, d.T, nullptr, 0, extent(d.T, d.ldx, 1), extent(d.T, d.lddy, 1), 0,
+          x_scale, dy_scale};
+  return dy_e5m2 ? wgrad_fused_f8<1>(opt, sr, g, a, st) : wgrad_fused_f8<0>(opt, sr, g, a, st);
+}
+
+hipError_t launch_wgrad_store_f8(int dy_e5m2, const void* X, const float* x_scale, const void* dY,
+                                 const float* dy_scale, const GemmDims& d, float* dW, int64_t ld_dw, hipStream_t st) {
+  GArgs g{X, dY, d.ldx, d.lddy, d.in, d.out, d.T, dW, ld_dw, extent(d.T, d.ldx, 1), extent(d.T, d.lddy, 1),
+          extent(d.out, ld_dw, 4), x_scale, dy_scale};
+  OptArgs a{};
+  auto run = [&](auto big, auto small) -> hipError_t {
+    using Big = decltype(big);
+    using Small = decltype(small);
+    return g_tiles<Big>(g) >= g_num_cus() ? g_launch<Big, G_EPI_STORE, FORGE_SGD, false, false>(g, a, st)
+                                          : g_launch<Small, G_EPI_STORE, FORGE_SGD, false, false>(g, a, st);
+  };
+  return dy_e5m2 ? run(WgradF8Big<1>{}, WgradF8Small<1>{}) : run(WgradF8Big<0>{}, WgradF8Small<0>{});
+}
+
 hipError_t launch_dgrad_bf16(const void* dY, int64_t lddy, const void* W, int64_t ldw, void* dX, int64_t lddx,
                              int32_t T, int32_t n_out, int32_t n_in, hipStream_t st) {
-  GArgs g{reinterpret_cast<const uint16_t*>(W), reinterpret_cast<const uint16_t*>(dY), ldw, lddy,
+  GArgs g{W, dY, ldw, lddy,
           n_in, T, n_out, dX, lddx, extent(n_out, ldw, 2), extent(T, lddy, 2), extent(T, lddx, 2)};
   OptArgs a{};
   return g_pick<DgradBig, DgradSmall, DgradSplit>(

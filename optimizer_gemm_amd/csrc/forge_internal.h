@@ -254,6 +254,10 @@ hipError_t launch_wgrad_fused_bf16(int state_q8, int opt, int sr, const void* X,
                                    const OptArgs& a, hipStream_t stream);
 hipError_t launch_wgrad_store_bf16(const void* X, const void* dY, const GemmDims& d, float* dW, int64_t ld_dw,
                                    hipStream_t stream);
+hipError_t launch_wgrad_fused_f8(int dy_e5m2, int opt, int sr, const void* X, const float* x_scale, const void* dY,
+                                 const float* dy_scale, const GemmDims& d, const OptArgs& a, hipStream_t st);
+hipError_t launch_wgrad_store_f8(int dy_e5m2, const void* X, const float* x_scale, const void* dY,
+                                 const float* dy_scale, const GemmDims& d, float* dW, int64_t ld_dw, hipStream_t st);
 hipError_t launch_dgrad_bf16(const void* dY, int64_t lddy, const void* W, int64_t ldw, void* dX, int64_t lddx,
                              int32_t T, int32_t out, int32_t in, hipStream_t stream);
 

@@ -16,7 +16,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("FORGE_LIB", os.path.join(_PKG, "_lib", "libforge.so"))
 
-F32, BF16, I8, U8 = 0, 1, 2, 3
+F32, BF16, I8, U8, E4M3, E5M2 = 0, 1, 2, 3, 4, 5
 OPTIMIZERS = ("adamw", "sgd", "sgd_momentum", "lion", "rmsprop", "adagrad", "nadam", "radam")
 OPT_ID = {name: k for k, name in enumerate(OPTIMIZERS)}
 # slot usage per optimizer: (uses m, uses v)
@@ -100,7 +100,9 @@ def version() -> int:
 # ---------------------------------------------------------------------------
 # marshalling helpers
 # ---------------------------------------------------------------------------
-_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8, torch.uint8: U8}
+_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8, torch.uint8: U8,
+       torch.float8_e4m3fn: E4M3, torch.float8_e5m2: E5M2}
+_FP8 = (torch.float8_e4m3fn, torch.float8_e5m2)
 
 
 def describe(t: Optional[torch.Tensor], scale: Optional[torch.Tensor] = None, *, device: bool = True):
@@ -123,9 +125,14 @@ def describe(t: Optional[torch.Tensor], scale: Optional[torch.Tensor] = None, *,
         if device and not scale.is_cuda:
             raise ValueError("scales must be device tensors")
         if scale.dtype != torch.float32 or not scale.is_contiguous():
-            raise ValueError("scales are contiguous float32 [rows, cols/64]")
-        if tuple(scale.shape) != (t.shape[0], t.shape[1] // 64):
-            raise ValueError("scale shape must be [rows, cols/64]")
+            raise ValueError("scales are contiguous float32")
+        if t.dtype in _FP8:
+            if scale.numel() != 1:
+                raise ValueError("an FP8 tensor has one float32 scale")
+        elif tuple(scale.shape) != (t.shape[0], t.shape[1] // 64):
+            raise ValueError("block scale shape must be [rows, cols/64]")
+    elif t.dtype in _FP8:
+        raise ValueError("an FP8 tensor needs its float32 scale")
     return ForgeTensor(t.data_ptr(), _DT[t.dtype], 0, t.shape[0], t.shape[1], ld,
                        scale.data_ptr() if scale is not None else None)
 
@@ -189,10 +196,15 @@ def _stream(stream) -> Optional[int]:
 # ---------------------------------------------------------------------------
 def wgrad_step(X: torch.Tensor, dY: torch.Tensor, W: torch.Tensor, m: Optional[torch.Tensor],
                v: Optional[torch.Tensor], opt: str = "adamw", hyper=None, step: int = 1, seed: int = 0,
-               m_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Fused dW = dY^T X + optimizer step; W, m, v (and scales) updated in place."""
+               m_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None, stream=None,
+               x_scale: Optional[torch.Tensor] = None, dy_scale: Optional[torch.Tensor] = None) -> None:
+    """Fused dW = dY^T X + optimizer step; W, m, v (and scales) updated in place.
+
+    FP8 inputs (X float8_e4m3fn, dY float8_e4m3fn or float8_e5m2) carry their
+    dequantisation scales as one-element float32 device tensors x_scale, dy_scale.
+    """
     h = _hyper(opt, hyper)
-    st = _lib.forge_linear_wgrad_step(_ref(describe(X)), _ref(describe(dY)), _ref(describe(W)),
+    st = _lib.forge_linear_wgrad_step(_ref(describe(X, x_scale)), _ref(describe(dY, dy_scale)), _ref(describe(W)),
                                       _ref(describe(m, m_scale)), _ref(describe(v, v_scale)), OPT_ID[opt],
                                       ctypes.byref(h), int(step), seed & (2 ** 64 - 1), _stream(stream))
     if st:
@@ -209,14 +221,15 @@ def dgrad(dY: torch.Tensor, W: torch.Tensor, dX: Optional[torch.Tensor] = None, 
     return dX
 
 
-def wgrad(X: torch.Tensor, dY: torch.Tensor, dW: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Unfused baseline part 1: float32 dW = dY^T X written to device memory."""
+def wgrad(X: torch.Tensor, dY: torch.Tensor, dW: Optional[torch.Tensor] = None, stream=None,
+          x_scale: Optional[torch.Tensor] = None, dy_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Unfused baseline part 1: float32 dW = dY^T X written to device memory (FP8 inputs as in wgrad_step)."""
     if dW is None:
         dW = torch.empty((dY.shape[1], X.shape[1]), dtype=torch.float32, device=X.device)
     if dW.dtype != torch.float32 or dW.dim() != 2 or (dW.shape[1] > 1 and dW.stride(1) != 1) or not dW.is_cuda:
         raise ValueError("dW must be a row-major float32 device tensor")
-    st = _lib.forge_linear_wgrad(_ref(describe(X)), _ref(describe(dY)), dW.data_ptr(), dW.stride(0),
-                                 _stream(stream))
+    st = _lib.forge_linear_wgrad(_ref(describe(X, x_scale)), _ref(describe(dY, dy_scale)), dW.data_ptr(),
+                                 dW.stride(0), _stream(stream))
     if st:
         raise ForgeError(st, "forge_linear_wgrad")
     return dW
@@ -238,9 +251,10 @@ def optimizer_step(dW: torch.Tensor, W: torch.Tensor, m: Optional[torch.Tensor],
 
 
 def wgrad_unfused(X, dY, W, m, v, opt="adamw", hyper=None, step=1, seed=0, m_scale=None, v_scale=None,
-                  dW_workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                  dW_workspace: Optional[torch.Tensor] = None, stream=None, x_scale=None,
+                  dy_scale=None) -> torch.Tensor:
     """The two-phase baseline: store dW (float32), then a separate optimizer pass. Returns dW."""
-    dW = wgrad(X, dY, dW_workspace, stream)
+    dW = wgrad(X, dY, dW_workspace, stream, x_scale, dy_scale)
     optimizer_step(dW, W, m, v, opt, hyper, step, seed, m_scale, v_scale, stream)
     return dW
 

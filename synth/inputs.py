@@ -162,6 +162,37 @@ def draw_layer_batch(config: int, layer: int, step: int, spec: LayerSpec) -> Tup
     return _to_io(x, spec.io), _to_io(dy, spec.io)
 
 
+FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+
+
+def fp8_codes(x: np.ndarray, fmt: str) -> Tuple[np.ndarray, float]:
+    """Per-tensor scaled OCP FP8 codes of float32 data: scale = absmax / largest finite
+    value of the format (1 for an all-zero tensor), codes = round-to-nearest-even of
+    x / scale (PyTorch's conversion). Returns (uint8 codes, float32 scale)."""
+    import torch
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    scale = np.float32(amax / FP8_MAX[fmt]) if amax > 0 else np.float32(1.0)
+    dt = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
+    q = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32) / scale).to(dt)
+    return q.view(torch.uint8).numpy().copy(), float(scale)
+
+
+def draw_layer_batch_fp8(config: int, layer: int, step: int, spec: LayerSpec, x_fmt: str = "e4m3",
+                         dy_fmt: str = "e5m2") -> Tuple[np.ndarray, np.ndarray, float, float]:
+    """The same (X, dY) draw as draw_layer_batch, as FP8 codes with per-tensor scales:
+    (X codes, dY codes, x scale, dY scale)."""
+    x = draw_normal((config, layer, step, TID_X), (spec.T, spec.inn), spec.x_std)
+    dy = draw_normal((config, layer, step, TID_DY), (spec.T, spec.out), spec.dy_std)
+    if spec.outlier_frac > 0.0:
+        rx = outlier_rows(config, layer, step, TID_X_OUT, spec.T, spec.outlier_frac)
+        rd = outlier_rows(config, layer, step, TID_DY_OUT, spec.T, spec.outlier_frac)
+        x[rx, :] *= np.float32(spec.outlier_scale)
+        dy[rd, :] *= np.float32(spec.outlier_scale)
+    xq, sx = fp8_codes(x, x_fmt)
+    dq, sd = fp8_codes(dy, dy_fmt)
+    return xq, dq, sx, sd
+
+
 def _llama8b_layers(T: int) -> List[LayerSpec]:
     h, kv, ff = 4096, 1024, 14336
     return [

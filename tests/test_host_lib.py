@@ -238,6 +238,39 @@ def test_validation_errors(f):
     assert E.STATUS[-7] == "FORGE_ERR_HIP"
 
 
+@cpu_only
+def test_fp8_validation_errors(f):
+    """FP8 inputs: X E4M3, dY E4M3 or E5M2, each with a one-float device scale, bf16 W, fp32 moments."""
+    F32, BF16, I8, U8, E4M3, E5M2 = 0, 1, 2, 3, 4, 5
+    A, B, C, Mp, Vp = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+    SX, SD, S1, S2 = 0x60000000, 0x60000004, 0x70000000, 0x78000000
+    X = _t(f, A, E4M3, 64, 256, scale=SX)
+    dY = _t(f, B, E5M2, 64, 128, scale=SD)
+    W = _t(f, C, BF16, 128, 256)
+    m = _t(f, Mp, F32, 128, 256)
+    v = _t(f, Vp, F32, 128, 256)
+    assert _call_step(f, _t(f, A, E4M3, 64, 256), dY, W, m, v) == -1            # X without its scale
+    assert _call_step(f, X, _t(f, B, E5M2, 64, 128), W, m, v) == -1             # dY without its scale
+    assert _call_step(f, _t(f, A, E5M2, 64, 256, scale=SX), dY, W, m, v) == -3  # X must be E4M3
+    assert _call_step(f, X, dY, _t(f, C, F32, 128, 256), m, v) == -3            # W must be bf16
+    assert _call_step(f, X, _t(f, B, BF16, 64, 128), W, m, v) == -3             # mixed FP8 / bf16 inputs
+    assert _call_step(f, _t(f, A, E4M3, 64, 264, scale=SX), dY, _t(f, C, BF16, 128, 264), m, v) == -4  # cols % 16
+    assert _call_step(f, _t(f, A, E4M3, 64, 256, ld=264, scale=SX), dY, W, m, v) == -4  # ld % 16
+    assert _call_step(f, _t(f, A + 8, E4M3, 64, 256, scale=SX), dY, W, m, v) == -4      # 16-byte base
+    assert _call_step(f, _t(f, A, E4M3, 64, 256, scale=SX + 2), dY, W, m, v) == -4      # float scale alignment
+    assert _call_step(f, X, _t(f, B, E5M2, 63, 128, scale=SD), W, m, v) == -2   # T mismatch
+    assert _call_step(f, X, dY, W, _t(f, Mp, I8, 128, 256, scale=S1),
+                      _t(f, Vp, U8, 128, 256, scale=S2)) == -5                   # no INT8 states with FP8
+    r = lambda x: ctypes.byref(x)  # noqa: E731
+    lib = f.lib()
+    assert lib.forge_linear_dgrad(r(_t(f, B, E4M3, 64, 128, scale=SD)), r(W), r(_t(f, A, BF16, 64, 256)),
+                                  None) == -5                                    # no FP8 dgrad
+    assert lib.forge_linear_wgrad(r(_t(f, A, E4M3, 64, 256)), r(dY), ctypes.c_void_p(0x80000000), 256,
+                                  None) == -1
+    assert lib.forge_linear_wgrad(r(X), r(_t(f, B, E5M2, 64, 120, scale=SD)), ctypes.c_void_p(0x80000000), 256,
+                                  None) == -4
+
+
 def test_step_scalars_errors(f):
     s = f.forge.ForgeScalars()
     h = f.make_hyper("adamw")
