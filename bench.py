@@ -37,8 +37,11 @@ HBM_GBS = 8000.0
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in ("forge_internal.h", "forge_gemm.hip", "forge_wgrad.hip"):
-        with open(os.path.join(ROOT, "optimizer_gemm_amd", "csrc", name), "rb") as f:
+    csrc = os.path.join(ROOT, "optimizer_gemm_amd", "csrc")
+    names = ["forge_internal.h", "forge_gemm_kernel.h", "forge_wgrad.hip"]
+    names += sorted(f for f in os.listdir(csrc) if f.startswith("forge_gemm") and f.endswith(".hip"))
+    for name in names:
+        with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 

@@ -20,7 +20,9 @@ LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libforge.so")
 ARCH = os.environ.get("FORGE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["forge_gemm.hip", "forge_wgrad.hip", "forge_dgrad.hip", "forge_api.hip"]
+# every HIP source of csrc/ (the fused-step instantiations are split over several
+# files so they compile in parallel)
+SOURCES = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -1,6 +1,6 @@
 // float32 input gradient dX = dY W of a linear layer (FORGE explainer, §5
 // limitations: the input gradient is read from the old weights, before the
-// update; the bfloat16 kernel lives in forge_gemm.hip), and the stand-alone
+// update; the bfloat16 kernel lives in forge_gemm_kernel.h), and the stand-alone
 // element-wise optimizer pass of the two-phase baseline (§1).
 //
 // dgrad mapping: the MFMA (v_mfma_f32_16x16x4_f32) computes

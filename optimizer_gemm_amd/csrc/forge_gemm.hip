@@ -1,771 +1,44 @@
-// bfloat16 GEMM core of the library on gfx950, with three epilogues:
-//   * fused weight-gradient + optimizer step (FORGE, §2 Method, "Core mechanism":
-//     each weight tile is accumulated over all tokens in FP32 accumulators, the
-//     optimizer update runs on those registers, only W and the moments are
-//     written back; the gradient tile never reaches device memory),
-//   * float32 dW store (the two-phase baseline of §1),
-//   * input gradient dX = dY W in bfloat16 (§5: computed from the old W).
-//
-// Mapping. C[m][n] = sum_k A[m][k] B[k][n] with
-//   wgrad: m = in (i), n = out (o), k = tokens; A[i][t] = X[t][i], B[t][o] = dY[t][o]
-//   dgrad: m = in (i), n = tokens (t), k = out;  A[i][o] = W[o][i], B[o][t] = dY[t][o]
-// so each lane's accumulator rows are consecutive `in` elements of one W (or dX)
-// row: the epilogue moves W/m/v/dX as 8- and 16-byte vectors.
-// A is always stored with k as the slow index (rows of X or W), B either the same
-// way (wgrad: rows of dY) or with k fast (dgrad: rows of dY).
-//
-// Mainloop. Operand stages of BK tokens go from global memory straight into LDS:
-// buffer loads with the LDS bit write one wave's 64 x 16 bytes to 1 KiB of
-// consecutive LDS, and out-of-range offsets write zeros (ragged k needs no other
-// masking). Four stages are in flight in a ring, so a stage's loads are issued three
-// stages before it is multiplied. Rows are kept as they sit in memory; the matrix
-// cores get them K-major through the LDS transpose read ds_read_b64_tr_b16 (k-fast B
-// rows through 16-byte reads), and XOR swizzles of the 16-byte chunks keep those
-// reads free of bank conflicts. Matrix instruction: v_mfma_f32_32x32x16_bf16 (the
-// 16x16x32 form issues at half the rate on this part). Each workgroup has WM x WN
-// waves; a wave owns a (BM/WM) x (BN/WN) block of C. The fragments of the next
-// k-step are read between the MFMAs of the current one. Tiles are walked by a
-// persistent grid in an XCD-aware order so the workgroups that run at the same time
-// on one XCD share the X/dY panels in that XCD's L2.
-#include <type_traits>
-
-#include "forge_internal.h"
+// Launch entry points of the GEMM core (kernel and configurations in
+// forge_gemm_kernel.h): the fused weight-gradient + optimizer step on bf16 / fp32
+// or FP8 operands, the float32 dW store of the two-phase baseline, and dgrad.
+#include "forge_gemm_kernel.h"
 
 namespace forge {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-
-// Compile-time loop: f(std::integral_constant<int, 0>) ... f(<N-1>), always unrolled,
-// so small per-lane arrays indexed by it stay in registers.
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
-enum { G_EPI_STORE = 0, G_EPI_OPT = 1, G_EPI_DX = 2 };
-
-// Operand formats of the GEMM core: bfloat16, or OCP FP8 (E4M3 / E5M2 per operand).
-enum { G_BF16 = 0, G_FP8 = 1 };
-
-template <int BM_, int BN_, int BK_, int WM_, int WN_, bool B_TR_, int OCC_, int NSTAGE_ = 4, int KS_ = 1,
-          int IN_ = G_BF16, int FA_ = 0, int FB_ = 0>
-struct GCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
-  static constexpr int OCC = OCC_;  // waves per SIMD
-  static constexpr bool B_TR = B_TR_;
-  // IN = G_FP8: both operands are OCP 8-bit codes, A in format FA and B in format FB
-  // (0 = E4M3, 1 = E5M2), multiplied by v_mfma_f32_32x32x64_f8f6f4 (64 tokens per
-  // instruction) instead of v_mfma_f32_32x32x16_bf16 (16 tokens).
-  static constexpr bool F8 = IN_ == G_FP8;
-  static constexpr int FA = FA_, FB = FB_;
-  static constexpr int EB = F8 ? 1 : 2;        // bytes per operand element
-  static constexpr int KSTEP = F8 ? 64 : 16;   // tokens per MFMA
-  static_assert(!F8 || B_TR, "FP8 operands are token-major on both sides");
-  // KS > 1: in-workgroup split-K. KS groups of WM x WN waves each take their own
-  // k-steps of every stage; the partial tiles are summed through LDS in the epilogue.
-  static constexpr int KS = KS_;
-  static constexpr int NW = WM * WN * KS, NT = 64 * NW;
-  static constexpr int TM = BM / WM, TN = BN / WN;
-  static constexpr int FM = TM / 32, FN = TN / 32;
-  static constexpr int KSTEPS = BK / KSTEP;
-  static constexpr int KPW = KSTEPS / KS;  // k-steps of a stage per wave
-  // One LDS stage (bytes): A as BK rows of BM; B as BK rows of BN (B_TR) or BN rows of BK.
-  static constexpr int ROWA = BM * EB, ROWB = (B_TR ? BN : BK) * EB;
-  static constexpr int A_BYTES = BK * ROWA, B_BYTES = BK * BN * EB;
-  // LDS: a ring of NSTAGE stages (the A parts of all stages first, then the B parts,
-  // so every fragment read reaches its stage through an immediate offset below 64 KiB),
-  // reused after the mainloop for one TN-row chunk of the finished tile as float rows
-  // of BM + 4.
-  static constexpr int NSTAGE = NSTAGE_;
-  static_assert(NSTAGE >= 2, "ring");
-  static constexpr int a_base(int buf) { return buf * A_BYTES; }
-  static constexpr int b_base(int buf) { return NSTAGE * A_BYTES + buf * B_BYTES; }
-  static constexpr int EPI_BYTES = TN * (BM + 4) * 4;
-  static constexpr int RING_BYTES = NSTAGE * (A_BYTES + B_BYTES);
-  static constexpr int SMEM_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
-  static constexpr int A_CPR = ROWA / 16, B_CPR = ROWB / 16;  // 16-byte chunks per row
-  static constexpr int PA = A_BYTES / 16 / NT, PB = B_BYTES / 16 / NT;  // chunks per thread per stage
-  static_assert((A_BYTES / 16) % NT == 0 && (B_BYTES / 16) % NT == 0, "stage must split evenly over threads");
-  static_assert(NT % A_CPR == 0 && NT % B_CPR == 0, "a thread's chunks share a column");
-  static_assert(TM % 32 == 0 && TN % 32 == 0 && BK % KSTEP == 0 && KSTEPS % KS == 0 && KPW >= 1, "tile shape");
-  static_assert(F8 || KPW % 2 == 0, "bf16 stages hold an even number of k-steps per wave");
-  // Chunk swizzles (XOR of the 16-byte chunk index of a row):
-  //  * rows read with the 16-bit transpose read: 4 * (row % 4), so the four rows one read
-  //    touches land in four different 64-byte bank groups (16 or more chunks per row);
-  //  * rows read with the 8-bit transpose read (8 rows x 32 bytes per half-wave): with
-  //    16 or more chunks per row 2 * (row % 8), with 8 chunks 2 * ((row / 2) % 4), so the
-  //    eight 32-byte pieces fall in eight different 32-byte bank groups;
-  //  * k-fast bf16 B rows of 4 or 8 chunks (KW = 4 or 2 rows per 256 bytes):
-  //    (row / KW) % chunks, so 16 consecutive rows cover all 16 bank groups.
-  // A thread's chunks are NT / chunks-per-row rows apart, a multiple of the swizzle
-  // period, so they all share one swizzled column.
-  static constexpr int KW = B_TR ? 1 : 16 / B_CPR;
-  static constexpr int TR_PERIOD = F8 ? 8 : 4;
-  __host__ __device__ static constexpr int swz_tr(int row, int cpr) {
-    return F8 ? (cpr >= 16 ? 2 * (row & 7) : 2 * ((row >> 1) & 3)) : 4 * (row & 3);
-  }
-  __host__ __device__ static constexpr int swz_b(int row) { return B_TR ? swz_tr(row, B_CPR) : (row / KW) % B_CPR; }
-  static_assert((F8 ? A_CPR >= 8 : A_CPR >= 16) && (NT / A_CPR) % TR_PERIOD == 0, "A swizzle");
-  static_assert(B_TR ? ((F8 ? B_CPR >= 8 : B_CPR >= 16) && (NT / B_CPR) % TR_PERIOD == 0)
-                     : ((B_CPR == 4 || B_CPR == 8) && (NT / B_CPR) % 16 == 0), "B swizzle");
-  // transpose reads per operand fragment and the k rows one read covers
-  static constexpr int RA = F8 ? 4 : 2, RSTEP = F8 ? 8 : 4;
-  // the 16-bit offset field of the LDS reads
-  static_assert((NSTAGE - 1) * A_BYTES + ((KPW - 1) * KSTEP + (RA - 1) * RSTEP) * ROWA < 65536, "A read offsets");
-  static_assert((NSTAGE - 1) * B_BYTES +
-                (B_TR ? ((KPW - 1) * KSTEP + (RA - 1) * RSTEP) * ROWB : 32 * (FN - 1) * ROWB) < 65536,
-                "B read offsets");
-};
-
-struct GArgs {
-  const void* A;      // wgrad: X; dgrad: W
-  const void* B;      // dY
-  int64_t lda, ldb;   // row pitches in elements
-  int32_t M, N, K;
-  void* out;          // dW (float) or dX (bf16)
-  int64_t ldo;
-  uint32_t a_bytes, b_bytes, out_bytes;  // extents addressed through buffer resources
-  const float* a_scale;  // FP8 operands: dequantisation scale of A and of B (one float each)
-  const float* b_scale;
-};
-
-// A byte offset that no buffer resource here covers: loads through it return 0,
-// stores through it are dropped.
-constexpr uint32_t kOOB = 0x80000000u;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-
-// Fragment reads, written as inline assembly with explicit lgkmcnt waits: an LDS read
-// the compiler can see makes it wait for every outstanding global->LDS load first
-// (vmcnt(0)), which would drain the ring at every k-step. Target builtins and LDS
-// address casts stay in these __device__ helpers: in a kernel body the host pass
-// rejects them and silently drops the kernel's launch stub.
-template <int OFF>
-__device__ __forceinline__ u32x2 ds_tr_asm(uint32_t addr) {
-  u32x2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
-  return r;
-}
-template <int OFF>
-__device__ __forceinline__ u32x2 ds_tr8_asm(uint32_t addr) {
-  u32x2 r;
-  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
-  return r;
-}
-template <int OFF>
-__device__ __forceinline__ u32x4 ds_b128_asm(uint32_t addr) {
-  u32x4 r;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
-  return r;
-}
-// 32-bit LDS byte address of a __shared__ location.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Wold-style-cast"
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
-#pragma clang diagnostic pop
-}
-// 16 bytes per lane from buffer offset off into LDS at dst + 16 * lane (zeros where
-// off is out of range).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* dst, uint32_t off) {
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Wold-style-cast"
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
-#pragma clang diagnostic pop
-}
-// The first or second of two objects, chosen at compile time (keeps two register sets
-// as separate variables, which the compiler keeps in registers, unlike an array).
-template <int I, class T>
-__device__ __forceinline__ T& pick2(T& a, T& b) {
-  if constexpr (I == 0)
-    return a;
-  else
-    return b;
-}
-// An empty asm that claims to rewrite v: any use of v after it is ordered after the
-// wait that precedes it.
-__device__ __forceinline__ void pin_reg(u32x2& v) { asm volatile("" : "+v"(v)); }
-__device__ __forceinline__ void pin_reg(u32x4& v) { asm volatile("" : "+v"(v)); }
-__device__ __forceinline__ void pin_reg(i32x8& v) { asm volatile("" : "+v"(v)); }
-// Waits until at most N LDS reads of this wave are outstanding (they complete in order).
-template <int N>
-__device__ __forceinline__ void lgkm_wait() {
-  asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N) : "memory");
-}
-// Waits until at most N global loads of this wave are outstanding and no LDS read is,
-// then joins the workgroup barrier.
-template <int N>
-__device__ __forceinline__ void vm_wait_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(N) : "memory");
-}
-
-// Persistent tile order: tile ids a workgroup takes are blockIdx.x + r*gridDim.x.
-// Workgroups are dealt to the 8 XCDs round-robin, so within a full round the ids of
-// one XCD are made contiguous, and contiguous ids walk GROUP tile-rows at a time.
-__device__ __forceinline__ void g_tile(int tile, int ntm, int ntn, int& tm, int& tn) {
-  const int G = gridDim.x;
-  const int ntiles = ntm * ntn;
-  int L = tile;
-  const int round0 = (tile / G) * G;
-  if ((G & 7) == 0 && round0 + G <= ntiles) {
-    const int w = tile - round0;
-    L = round0 + (w & 7) * (G >> 3) + (w >> 3);
-  }
-  constexpr int GROUP = 4;
-  const int per = GROUP * ntn;
-  const int g = L / per;
-  const int first = g * GROUP;
-  const int gs = min(ntm - first, GROUP);
-  const int r = L - g * per;
-  tm = first + r % gs;
-  tn = r / gs;
-}
-
-// Epilogue memory access through buffer resources (32-bit offsets; an out-of-range
-// offset turns loads into zeros and drops stores).
-struct EpiRes {
-  __amdgpu_buffer_rsrc_t W, m, v, ms, vs;
-};
-
-template <int OPT, bool Q8>
-__device__ __forceinline__ EpiRes epi_res(const OptArgs& a) {
-  EpiRes r;
-  const uint32_t n = (uint32_t)a.out;
-  r.W = make_rsrc(a.W, n * (uint32_t)a.ldw * 2u);
-  constexpr int SL = opt_slots(OPT);
-  const uint32_t es = Q8 ? 1u : 4u;
-  r.m = make_rsrc((SL & 1) ? a.m : a.W, (SL & 1) ? n * (uint32_t)a.ldm * es : 0u);
-  r.v = make_rsrc((SL & 2) ? a.v : a.W, (SL & 2) ? n * (uint32_t)a.ldv * es : 0u);
-  const uint32_t sb = Q8 ? n * (uint32_t)(a.in >> 6) * 4u : 0u;
-  r.ms = make_rsrc(((SL & 1) && Q8) ? (const void*)a.m_scale : a.W, ((SL & 1) && Q8) ? sb : 0u);
-  r.vs = make_rsrc(((SL & 2) && Q8) ? (const void*)a.v_scale : a.W, ((SL & 2) && Q8) ? sb : 0u);
-  return r;
-}
-
-template <class C, int EPI, int OPT, bool Q8, bool SR>
-__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
-void gemm_kernel(GArgs g, OptArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[C::SMEM_BYTES];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int ks = wave / (C::WM * C::WN), wsp = wave % (C::WM * C::WN);
-  const int wm = wsp % C::WM, wn = wsp / C::WM;
-  const int wave_m0 = wm * C::TM, wave_n0 = wn * C::TN;
-  const int l32 = lane & 31, hi = lane >> 5;
-
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A, g.a_bytes);
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.B, g.b_bytes);
-  // FP8 operands: the gradient is the product of the two dequantisation scales times
-  // the sum of code products
-  const float gscale = C::F8 ? g.a_scale[0] * g.b_scale[0] : 1.f;
-
-  const int ntm = (g.M + C::BM - 1) / C::BM, ntn = (g.N + C::BN - 1) / C::BN;
-  const int ntiles = ntm * ntn;
-  const int nst = (g.K + C::BK - 1) / C::BK;
-  // Stages are issued in groups of the ring size; stages past the last one, like rows
-  // past the last token, load through out-of-range offsets and so hold zeros.
-  const int nstr = ((nst + C::NSTAGE - 1) / C::NSTAGE) * C::NSTAGE;
-  constexpr int LPS = C::PA + C::PB;                                     // loads per stage and wave
-  constexpr int NRA = C::RA * C::FM, NRB = C::B_TR ? C::RA * C::FN : C::FN;
-  constexpr int NR = NRA + NRB;                                           // LDS reads per k-step and wave
-  static_assert((C::NSTAGE - 1) * LPS <= 63, "vmcnt range");
-
-  // Staging: the LDS slot of this thread's chunk j in a stage is tid + j*NT (a wave's
-  // load fills 64 consecutive 16-byte slots); the swizzle picks the global chunk that
-  // lands there. Chunk j is A_RSTEP (B_RSTEP) rows below chunk 0.
-  const int a_row0 = tid / C::A_CPR, b_row0 = tid / C::B_CPR;
-  const int a_colb = ((tid % C::A_CPR) ^ C::swz_tr(a_row0, C::A_CPR)) * 16;  // byte column in the row
-  const int b_colb = ((tid % C::B_CPR) ^ C::swz_b(b_row0)) * 16;
-  constexpr int A_RSTEP = C::NT / C::A_CPR, B_RSTEP = C::NT / C::B_CPR;
-  const uint32_t a_rowb = (uint32_t)(A_RSTEP * g.lda * C::EB), a_stageb = (uint32_t)(C::BK * g.lda * C::EB);
-  const uint32_t b_rowb = (uint32_t)(B_RSTEP * g.ldb * C::EB);
-  const uint32_t b_stageb = C::B_TR ? (uint32_t)(C::BK * g.ldb * C::EB) : (uint32_t)(C::BK * C::EB);
-
-  // Byte addresses of this lane's fragment reads in stage buffer 0, k-step 0, with the
-  // chunk index swizzled as the loads placed it; buffers, k-steps and the reads of one
-  // fragment are immediates.
-  //  * 16-bit transpose read: lane (r4, c4, half, hi) reads row 8 hi + r4, elements
-  //    16 half + 4 c4 .. +3 of the 32-wide fragment; the lane receives 4 k of column l32.
-  //  * 8-bit transpose read: lane pair p = (lane % 16) / 2 reads row 32 hi + p, bytes
-  //    16 mh + 8 (lane % 2) .. +7 (mh = (lane / 16) % 2); the lane receives 8 k of
-  //    column l32. Operand byte b of lane l then holds k = 32 (l / 32) + b in both A and B.
-  const uint32_t lds0 = lds_addr(smem);
-  // A wave of k-split group ks reads k-steps ks*KPW .. ks*KPW + KPW-1 of each stage.
-  const int kr0 = ks * C::KPW * C::KSTEP;  // first k row of this wave in a stage
-  auto tr_addr = [&](int base, int rowbytes, int cpr, int col0) -> uint32_t {
-    int row, chunk, byte;
-    if constexpr (C::F8) {
-      row = kr0 + 32 * hi + ((lane & 15) >> 1);
-      chunk = col0 / 16 + ((lane >> 4) & 1);
-      byte = 8 * (lane & 1);
-    } else {
-      const int r4 = (lane & 15) >> 2, c4 = lane & 3;
-      row = kr0 + 8 * hi + r4;
-      chunk = col0 * 2 / 16 + 2 * ((lane >> 4) & 1) + (c4 >> 1);
-      byte = 8 * (c4 & 1);
-    }
-    return lds0 + (uint32_t)(base + row * rowbytes + 16 * (chunk ^ C::swz_tr(row, cpr)) + byte);
-  };
-  uint32_t a_ad[C::FM], b_ad[C::B_TR ? C::FN : C::KPW];
-#pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) a_ad[fm] = tr_addr(C::a_base(0), C::ROWA, C::A_CPR, wave_m0 + 32 * fm);
-  if constexpr (C::B_TR) {
-#pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn) b_ad[fn] = tr_addr(C::b_base(0), C::ROWB, C::B_CPR, wave_n0 + 32 * fn);
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < C::KPW; ++kk)
-      b_ad[kk] = lds0 + (uint32_t)(C::b_base(0) + (wave_n0 + l32) * C::ROWB +
-                                   16 * ((2 * (ks * C::KPW + kk) + hi) ^ C::swz_b(l32)));
-  }
-
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    int tm, tn;
-    g_tile(tile, ntm, ntn, tm, tn);
-    const int m0 = tm * C::BM, n0 = tn * C::BN;
-
-    f32x16 acc[C::FM][C::FN];
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[fm][fn][e] = 0.f;
-
-    // Only the k range is checked per load: a chunk past the M or N edge feeds
-    // accumulator rows or columns that are never stored (the buffer resource still
-    // bounds every access), while a k past the end must read as zero.
-    const uint32_t a_base0 = (uint32_t)((a_row0 * g.lda + m0) * C::EB + a_colb);
-    uint32_t b_base0;
-    if constexpr (C::B_TR)
-      b_base0 = (uint32_t)((b_row0 * g.ldb + n0) * C::EB + b_colb);
-    else
-      b_base0 = (uint32_t)((int64_t)(n0 + b_row0) * g.ldb * C::EB + b_colb);
-    auto dma = [&](auto buf_c, int s) {
-      constexpr int buf = decltype(buf_c)::value;
-      const int k0 = s * C::BK;
-#pragma unroll
-      for (int j = 0; j < C::PA; ++j) {
-        const uint32_t off = (k0 + a_row0 + j * A_RSTEP < g.K) ? a_base0 + (uint32_t)s * a_stageb + (uint32_t)j * a_rowb : kOOB;
-        dma16(rA, smem + C::a_base(buf) + (j * C::NT + wave_u * 64) * 16, off);
-      }
-#pragma unroll
-      for (int j = 0; j < C::PB; ++j) {
-        const int kb = C::B_TR ? k0 + b_row0 + j * B_RSTEP : k0 + b_colb / C::EB;
-        const uint32_t off = (kb < g.K) ? b_base0 + (uint32_t)s * b_stageb + (uint32_t)j * b_rowb : kOOB;
-        dma16(rB, smem + C::b_base(buf) + (j * C::NT + wave_u * 64) * 16, off);
-      }
-    };
-    // Operand fragments of one k-step as the LDS reads return them: RA pieces of 8 bytes
-    // per transposed operand, one 16-byte read per k-fast B operand.
-    struct FragBf16 {
-      u32x2 a[C::FM][C::RA];
-      u32x2 bt[C::B_TR ? C::FN : 1][C::RA];
-      u32x4 bk[C::B_TR ? 1 : C::FN];
-    };
-    // FP8: one 8-register operand vector per fragment, filled read by read
-    struct FragF8 {
-      i32x8 a[C::FM];
-      i32x8 bt[C::FN];
-    };
-    using Frag = std::conditional_t<C::F8, FragF8, FragBf16>;
-    // The r-th of the NR reads of a k-step's fragments.
-    auto read_one = [&](Frag& F, auto buf_c, auto kk_c, auto r_c) {
-      constexpr int buf = decltype(buf_c)::value, kk = decltype(kk_c)::value, r = decltype(r_c)::value;
-      if constexpr (r < NRA) {
-        constexpr int fm = r / C::RA, h = r % C::RA;
-        constexpr int off = C::a_base(buf) + (kk * C::KSTEP + h * C::RSTEP) * C::ROWA;
-        if constexpr (C::F8) {
-          const u32x2 x = ds_tr8_asm<off>(a_ad[fm]);
-          F.a[fm][2 * h] = (int)x.x;
-          F.a[fm][2 * h + 1] = (int)x.y;
-        } else {
-          F.a[fm][h] = ds_tr_asm<off>(a_ad[fm]);
-        }
-      } else if constexpr (C::B_TR) {
-        constexpr int fn = (r - NRA) / C::RA, h = (r - NRA) % C::RA;
-        constexpr int off = buf * C::B_BYTES + (kk * C::KSTEP + h * C::RSTEP) * C::ROWB;
-        if constexpr (C::F8) {
-          const u32x2 x = ds_tr8_asm<off>(b_ad[fn]);
-          F.bt[fn][2 * h] = (int)x.x;
-          F.bt[fn][2 * h + 1] = (int)x.y;
-        } else {
-          F.bt[fn][h] = ds_tr_asm<off>(b_ad[fn]);
-        }
-      } else {
-        constexpr int fn = r - NRA;
-        F.bk[fn] = ds_b128_asm<buf * C::B_BYTES + 32 * fn * C::ROWB>(b_ad[kk]);
-      }
-    };
-    // Orders every later use of F's registers after the wait that precedes this.
-    auto settle = [&](Frag& F) {
-      if constexpr (C::F8) {
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) pin_reg(F.a[fm]);
-#pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) pin_reg(F.bt[fn]);
-        return;
-      } else {
-#pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-        for (int h = 0; h < C::RA; ++h) pin_reg(F.a[fm][h]);
-      }
-      if constexpr (C::B_TR && !C::F8) {
-#pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-          for (int h = 0; h < C::RA; ++h) pin_reg(F.bt[fn][h]);
-      } else if constexpr (!C::F8) {
-#pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) pin_reg(F.bk[fn]);
-      }
-    };
-    auto mfma_one = [&](const Frag& F, auto i_c) {
-      constexpr int fm = decltype(i_c)::value / C::FN, fn = decltype(i_c)::value % C::FN;
-      if constexpr (C::F8) {
-        // block scales of 2^0 (E8M0 code 127): the tensor scales are applied to the sum
-        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[fm], F.bt[fn], acc[fm][fn], C::FA, C::FB, 0, 127,
-                                                                      0, 127);
-      } else {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{F.a[fm][0].x, F.a[fm][0].y, F.a[fm][1].x, F.a[fm][1].y});
-        bf16x8 bv;
-        if constexpr (C::B_TR)
-          bv = __builtin_bit_cast(bf16x8, u32x4{F.bt[fn][0].x, F.bt[fn][0].y, F.bt[fn][1].x, F.bt[fn][1].y});
-        else
-          bv = __builtin_bit_cast(bf16x8, F.bk[fn]);
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[fm][fn], 0, 0, 0);
-      }
-    };
-    // The MFMAs of fragment set F, with the reads of the next set G spread over the
-    // first half of them and `after_first` run after the first; sched_barrier keeps
-    // this order.
-    constexpr int NM = C::FM * C::FN;
-    constexpr int RPM = (NR + NM / 2 - 1) / (NM / 2);
-    auto mma_reading = [&](const Frag& F, Frag& G, auto buf_c, auto kk_c, auto&& after_first) {
-      static_for<0, NM>([&](auto i_c) {
-        constexpr int i = decltype(i_c)::value;
-        mfma_one(F, i_c);
-        if constexpr (i == 0) after_first();
-        static_for<i * RPM, (i + 1) * RPM < NR ? (i + 1) * RPM : NR>([&](auto r_c) { read_one(G, buf_c, kk_c, r_c); });
-        __builtin_amdgcn_sched_barrier(0);
-      });
-    };
-
-    // ---- mainloop ----
-    // Stage st sits in ring buffer st % NSTAGE. The k-steps' MFMAs run back to back,
-    // each set reading the next set's fragments (two register sets alternate). Before
-    // the last k-step of a stage every wave waits for its own loads of stage st+1 and
-    // for its LDS reads, the barrier then makes stage st+1 visible and frees buffer
-    // st % NSTAGE (all its reads are done), and the loads of stage st + NSTAGE into
-    // that buffer are issued.
-    Frag F0, F1;
-    __syncthreads();  // the previous tile's epilogue is done with LDS
-    static_for<0, C::NSTAGE>([&](auto b_c) { dma(b_c, decltype(b_c)::value); });
-    vm_wait_barrier<(C::NSTAGE - 1) * LPS>();
-    static_for<0, NR>([&](auto r_c) {
-      read_one(F0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, r_c);
-    });
-    static_assert((C::NSTAGE * C::KPW) % 2 == 0, "register sets alternate evenly over a round of the ring");
-    auto stage = [&](auto R_c, int st) {
-      constexpr int R = decltype(R_c)::value;
-      static_for<0, C::KPW>([&](auto kk_c) {
-        constexpr int kk = decltype(kk_c)::value;
-        constexpr int cur = (R * C::KPW + kk) % 2;
-        Frag& Fc = pick2<cur>(F0, F1);
-        Frag& Fn = pick2<1 - cur>(F0, F1);
-        if constexpr (kk + 1 < C::KPW) {
-          lgkm_wait<0>();
-          settle(Fc);
-          mma_reading(Fc, Fn, R_c, std::integral_constant<int, kk + 1>{}, [] {});
-        } else {
-          vm_wait_barrier<(C::NSTAGE - 2) * LPS>();
-          settle(Fc);
-          mma_reading(Fc, Fn, std::integral_constant<int, (R + 1) % C::NSTAGE>{}, std::integral_constant<int, 0>{},
-                      [&] { dma(R_c, st + C::NSTAGE); });
-        }
-      });
-    };
-    for (int st = 0; st < nstr; st += C::NSTAGE)
-      static_for<0, C::NSTAGE>([&](auto r_c) { stage(r_c, st + decltype(r_c)::value); });
-    // the loads issued past the end still write LDS: let them land before it is reused
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-
-    // ---- epilogue ----
-    // The finished tile is handed through LDS one wave-column (TN rows of n) at a
-    // time: the waves that own those rows write their accumulators (lane holds
-    // C[m = 8q + 4*hi + j][n = l32] of each 32x32 block) as float rows, then every
-    // thread takes 4 consecutive m of a row, so each wave reads and writes whole
-    // contiguous row segments of W / m / v / dW / dX.
-    float* E = reinterpret_cast<float*>(smem);
-    constexpr int LDE = C::BM + 4;
-    constexpr int VPR = C::BM / 4;                   // 4-element vectors per row
-    constexpr int NV = C::TN * VPR / C::NT;          // vectors per thread per chunk
-    static_assert((C::TN * VPR) % C::NT == 0, "chunk must split evenly over threads");
-    static_assert(VPR % 16 == 0, "an INT8 block of 64 must be 16 adjacent lanes");
-    __syncthreads();  // every wave is done reading the operand stages
-#pragma unroll 1
-    for (int c = 0; c < C::WN; ++c) {
-      // k-split group 0 writes its partial tile, groups 1.. add theirs in order
-#pragma unroll 1
-      for (int kg = 0; kg < C::KS; ++kg) {
-        if (wn == c && ks == kg) {
-#pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-            for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                f32x4* e = reinterpret_cast<f32x4*>(E + (32 * fn + l32) * LDE + wave_m0 + 32 * fm + 8 * q + 4 * hi);
-                f32x4 x{acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3]};
-                if (kg > 0) x = *e + x;
-                *e = x;
-              }
-        }
-        __syncthreads();
-      }
-      const int nrow0 = n0 + c * C::TN;
-      if constexpr (EPI == G_EPI_STORE || EPI == G_EPI_DX) {
-        const __amdgpu_buffer_rsrc_t rO = make_rsrc(g.out, g.out_bytes);
-#pragma unroll
-        for (int k = 0; k < NV; ++k) {
-          const int vi = tid + k * C::NT, row = vi / VPR, col = (vi % VPR) * 4;
-          const int n = nrow0 + row, m = m0 + col;
-          f32x4 x = *reinterpret_cast<const f32x4*>(E + row * LDE + col);
-          if constexpr (C::F8) x = x * gscale;
-          const bool ok = n < g.N && m < g.M;
-          if constexpr (EPI == G_EPI_STORE) {
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rO,
-                                                   ok ? (uint32_t)((n * g.ldo + m) * 4) : kOOB, 0, 0);
-          } else {
-            const u32x2 r{rne_bf16_bits(x.x) | (rne_bf16_bits(x.y) << 16), rne_bf16_bits(x.z) | (rne_bf16_bits(x.w) << 16)};
-            __builtin_amdgcn_raw_buffer_store_b64(r, rO, ok ? (uint32_t)((n * g.ldo + m) * 2) : kOOB, 0, 0);
-          }
-        }
-      } else {
-        constexpr int SL = opt_slots(OPT);
-        constexpr bool HAS_M = SL & 1, HAS_V = SL & 2;
-        const EpiRes R = epi_res<OPT, Q8>(a);
-        // loads of KB vectors are issued before any of them is consumed; KB bounds the
-        // registers a batch holds next to the accumulators still to be written out
-        constexpr int KB_MAX = C::OCC >= 2 ? 2 : (Q8 ? 4 : 8);
-        constexpr int KB = NV > KB_MAX ? KB_MAX : NV;
-#pragma unroll
-        for (int kb = 0; kb < NV; kb += KB) {
-        uint32_t ow[KB], om[KB], ov_[KB], osc[KB];
-        u32x2 wb[KB];
-        f32x4 mv[KB], vv[KB];
-        uint32_t qm[KB], qv[KB];
-        float msc[KB], vsc[KB];
-#pragma unroll
-        for (int k = 0; k < KB; ++k) {
-          const int vi = tid + (kb + k) * C::NT, row = vi / VPR, col = (vi % VPR) * 4;
-          const int o = nrow0 + row, i = m0 + col;
-          const bool ok = o < g.N && i < g.M;
-          ow[k] = ok ? (uint32_t)(o * a.ldw + i) * 2u : kOOB;
-          wb[k] = __builtin_amdgcn_raw_buffer_load_b64(R.W, ow[k], 0, 0);
-          if constexpr (!Q8) {
-            om[k] = ok ? (uint32_t)(o * a.ldm + i) * 4u : kOOB;
-            ov_[k] = ok ? (uint32_t)(o * a.ldv + i) * 4u : kOOB;
-            if constexpr (HAS_M) mv[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(R.m, om[k], 0, 0));
-            if constexpr (HAS_V) vv[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(R.v, ov_[k], 0, 0));
-          } else {
-            om[k] = ok ? (uint32_t)(o * a.ldm + i) : kOOB;
-            ov_[k] = ok ? (uint32_t)(o * a.ldv + i) : kOOB;
-            osc[k] = ok ? (uint32_t)(o * (a.in >> 6) + (i >> 6)) * 4u : kOOB;
-            if constexpr (HAS_M) {
-              qm[k] = __builtin_amdgcn_raw_buffer_load_b32(R.m, om[k], 0, 0);
-              msc[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(R.ms, osc[k], 0, 0));
-            }
-            if constexpr (HAS_V) {
-              qv[k] = __builtin_amdgcn_raw_buffer_load_b32(R.v, ov_[k], 0, 0);
-              vsc[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(R.vs, osc[k], 0, 0));
-            }
-          }
-        }
-#pragma unroll
-        for (int k = 0; k < KB; ++k) {
-          const int vi = tid + (kb + k) * C::NT, row = vi / VPR, col = (vi % VPR) * 4;
-          const int o = nrow0 + row, i = m0 + col;
-          f32x4 gx = *reinterpret_cast<const f32x4*>(E + row * LDE + col);
-          if constexpr (C::F8) gx = gx * gscale;
-          const float gg[4] = {gx.x, gx.y, gx.z, gx.w};
-          float w[4] = {bits_f32(wb[k].x << 16), bits_f32(wb[k].x & 0xFFFF0000u), bits_f32(wb[k].y << 16),
-                        bits_f32(wb[k].y & 0xFFFF0000u)};
-          float m[4] = {0.f, 0.f, 0.f, 0.f}, v[4] = {0.f, 0.f, 0.f, 0.f};
-          if constexpr (!Q8) {
-            if constexpr (HAS_M) { m[0] = mv[k].x; m[1] = mv[k].y; m[2] = mv[k].z; m[3] = mv[k].w; }
-            if constexpr (HAS_V) { v[0] = vv[k].x; v[1] = vv[k].y; v[2] = vv[k].z; v[3] = vv[k].w; }
-          } else {
-            if constexpr (HAS_M) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) m[j] = (float)(int8_t)((qm[k] >> (8 * j)) & 0xFF) * msc[k];
-            }
-            if constexpr (HAS_V) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const float r = (float)((qv[k] >> (8 * j)) & 0xFF) * vsc[k];
-                v[j] = r * r;
-              }
-            }
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) opt_apply<OPT>(gg[j], w[j], m[j], v[j], a.s);
-          const uint32_t idx0 = (uint32_t)o * (uint32_t)a.in + (uint32_t)i;
-          uint32_t bb[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            bb[j] = SR ? sr_bf16_bits(w[j], rand16_from_base(a.rng_base, idx0 + j)) : rne_bf16_bits(w[j]);
-          __builtin_amdgcn_raw_buffer_store_b64(u32x2{bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16)}, R.W, ow[k], 0, 0);
-          if constexpr (!Q8) {
-            if constexpr (HAS_M)
-              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{m[0], m[1], m[2], m[3]}), R.m, om[k], 0, 0);
-            if constexpr (HAS_V)
-              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{v[0], v[1], v[2], v[3]}), R.v, ov_[k], 0, 0);
-          } else {
-            // block-64 absmax over the 16 adjacent lanes holding this row's block
-            float r[4], mmax = 0.f, vmax = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              r[j] = sqrtf(v[j]);
-              mmax = fmaxf(mmax, fabsf(m[j]));
-              vmax = fmaxf(vmax, r[j]);
-            }
-#pragma unroll
-            for (int sh = 1; sh < 16; sh <<= 1) {
-              mmax = fmaxf(mmax, __shfl_xor(mmax, sh));
-              vmax = fmaxf(vmax, __shfl_xor(vmax, sh));
-            }
-            const float sm = mmax / 127.f, sv = vmax / 255.f;
-            if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(quant_m4(m, sm), R.m, om[k], 0, 0);
-            if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(quant_v4(r, sv), R.v, ov_[k], 0, 0);
-            if ((col & 63) == 0) {
-              if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sm), R.ms, osc[k], 0, 0);
-              if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sv), R.vs, osc[k], 0, 0);
-            }
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      __syncthreads();  // the chunk's LDS rows are consumed before the next chunk overwrites them
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Launchers. Large problems use 256x256 workgroup tiles (8 waves of 128x64, two
-// per SIMD); problems with fewer such tiles than compute units use 128x128 tiles
-// (4 waves of 64x64, two workgroups per compute unit), and when even those are
-// scarce (fewer than two per compute unit) 128x128 tiles with a 2-way in-workgroup
-// split-K (8 waves of 64x64, one workgroup per compute unit), so a compute unit
-// that holds a single tile still runs two waves per SIMD.
-// ---------------------------------------------------------------------------
-// Tile configurations (BM, BN, BK, WM, WN, B_TR, OCC[, NSTAGE, KS]); FORGE_*_CFG
-// override them at build time for tuning sweeps.
-#ifndef FORGE_WGRAD_BIG_CFG
-#define FORGE_WGRAD_BIG_CFG 256, 256, 32, 2, 4, true, 2
-#endif
-#ifndef FORGE_WGRAD_SMALL_CFG
-#define FORGE_WGRAD_SMALL_CFG 128, 128, 32, 2, 2, true, 2
-#endif
-#ifndef FORGE_WGRAD_SPLIT_CFG
-#define FORGE_WGRAD_SPLIT_CFG 128, 128, 64, 2, 2, true, 2, 4, 2
-#endif
-#ifndef FORGE_DGRAD_BIG_CFG
-#define FORGE_DGRAD_BIG_CFG 256, 256, 32, 2, 4, false, 2
-#endif
-#ifndef FORGE_DGRAD_SMALL_CFG
-#define FORGE_DGRAD_SMALL_CFG 128, 128, 32, 2, 2, false, 2
-#endif
-#ifndef FORGE_DGRAD_SPLIT_CFG
-#define FORGE_DGRAD_SPLIT_CFG 128, 128, 64, 2, 2, false, 2, 4, 2
-#endif
-// FP8 operands (X in E4M3, dY in format FB): 64-token stages, one MFMA k-step each. The
-// large tile runs 4 waves of 128x128 (one per SIMD, 512 registers each): two sets of
-// 8-register FP8 fragments would not fit next to 128 accumulators at two waves per SIMD.
-#ifndef FORGE_WGRAD_F8_BIG_CFG
-#define FORGE_WGRAD_F8_BIG_CFG 256, 256, 64, 2, 2, true, 1, 4, 1
-#endif
-#ifndef FORGE_WGRAD_F8_SMALL_CFG
-#define FORGE_WGRAD_F8_SMALL_CFG 128, 128, 64, 2, 2, true, 2, 4, 1
-#endif
-template <int FB>
-using WgradF8Big = GCfg<FORGE_WGRAD_F8_BIG_CFG, G_FP8, 0, FB>;
-template <int FB>
-using WgradF8Small = GCfg<FORGE_WGRAD_F8_SMALL_CFG, G_FP8, 0, FB>;
-using WgradBig = GCfg<FORGE_WGRAD_BIG_CFG>;
-using WgradSmall = GCfg<FORGE_WGRAD_SMALL_CFG>;
-using WgradSplit = GCfg<FORGE_WGRAD_SPLIT_CFG>;
-using DgradBig = GCfg<FORGE_DGRAD_BIG_CFG>;
-using DgradSmall = GCfg<FORGE_DGRAD_SMALL_CFG>;
-using DgradSplit = GCfg<FORGE_DGRAD_SPLIT_CFG>;
-
-static int g_num_cus() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      n = v;
-    else
-      n = 256;
-  }
-  return n;
-}
-
-template <class C, int EPI, int OPT, bool Q8, bool SR>
-static hipError_t g_launch(const GArgs& g, const OptArgs& a, hipStream_t st) {
-  const int ntiles = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN);
-  if (ntiles == 0) return hipSuccess;
-  const int resident = C::OCC * 4 / C::NW * g_num_cus();  // OCC waves on each of 4 SIMDs
-  const int grid = ntiles < resident ? ntiles : resident;
-  hipLaunchKernelGGL((gemm_kernel<C, EPI, OPT, Q8, SR>), dim3(grid), dim3(C::NT), 0, st, g, a);
-  return hipGetLastError();
-}
-
-template <class C>
-static int g_tiles(const GArgs& g) {
-  return ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN);
-}
-
-// Calls f(C{}) with the tile configuration for this problem size.
-template <class Big, class Small, class Split, class F>
-static hipError_t g_pick(const GArgs& g, F&& f) {
-  if (g_tiles<Big>(g) >= g_num_cus()) return f(Big{});
-  if (g_tiles<Small>(g) >= 2 * g_num_cus()) return f(Small{});
-  return f(Split{});
-}
-
-template <int OPT>
-static hipError_t wgrad_opt_v2(int q8, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
-  return g_pick<WgradBig, WgradSmall, WgradSplit>(g, [&](auto c) {
-    using C = decltype(c);
-    if (q8) return sr ? g_launch<C, G_EPI_OPT, OPT, true, true>(g, a, st) : g_launch<C, G_EPI_OPT, OPT, true, false>(g, a, st);
-    return sr ? g_launch<C, G_EPI_OPT, OPT, false, true>(g, a, st) : g_launch<C, G_EPI_OPT, OPT, false, false>(g, a, st);
-  });
-}
-
-static uint32_t extent(int64_t rows, int64_t ld, int64_t es) { return (uint32_t)(rows * ld * es); }
+FORGE_EXTERN_BF16(FORGE_ADAMW)
+FORGE_EXTERN_BF16(FORGE_SGD)
+FORGE_EXTERN_BF16(FORGE_SGD_MOMENTUM)
+FORGE_EXTERN_BF16(FORGE_LION)
+FORGE_EXTERN_BF16(FORGE_RMSPROP)
+FORGE_EXTERN_BF16(FORGE_ADAGRAD)
+FORGE_EXTERN_BF16(FORGE_NADAM)
+FORGE_EXTERN_BF16(FORGE_RADAM)
+#define FORGE_EXTERN_F8_ALL(FB)             \
+  FORGE_EXTERN_F8(FORGE_ADAMW, FB)          \
+  FORGE_EXTERN_F8(FORGE_SGD, FB)            \
+  FORGE_EXTERN_F8(FORGE_SGD_MOMENTUM, FB)   \
+  FORGE_EXTERN_F8(FORGE_LION, FB)           \
+  FORGE_EXTERN_F8(FORGE_RMSPROP, FB)        \
+  FORGE_EXTERN_F8(FORGE_ADAGRAD, FB)        \
+  FORGE_EXTERN_F8(FORGE_NADAM, FB)          \
+  FORGE_EXTERN_F8(FORGE_RADAM, FB)          \
+  extern template hipError_t wgrad_store_f8<FB>(const GArgs&, hipStream_t);
+FORGE_EXTERN_F8_ALL(0)
+FORGE_EXTERN_F8_ALL(1)
 
 hipError_t launch_wgrad_fused_bf16(int state_q8, int opt, int sr, const void* X, const void* dY, const GemmDims& d,
                                    const OptArgs& a, hipStream_t st) {
   GArgs g{X, dY, d.ldx, d.lddy,
           d.in, d.out, d.T, nullptr, 0, extent(d.T, d.ldx, 2), extent(d.T, d.lddy, 2), 0};
   switch (opt) {
-    case FORGE_ADAMW: return wgrad_opt_v2<FORGE_ADAMW>(state_q8, sr, g, a, st);
-    case FORGE_SGD: return wgrad_opt_v2<FORGE_SGD>(state_q8, sr, g, a, st);
-    case FORGE_SGD_MOMENTUM: return wgrad_opt_v2<FORGE_SGD_MOMENTUM>(state_q8, sr, g, a, st);
-    case FORGE_LION: return wgrad_opt_v2<FORGE_LION>(state_q8, sr, g, a, st);
-    case FORGE_RMSPROP: return wgrad_opt_v2<FORGE_RMSPROP>(state_q8, sr, g, a, st);
-    case FORGE_ADAGRAD: return wgrad_opt_v2<FORGE_ADAGRAD>(state_q8, sr, g, a, st);
-    case FORGE_NADAM: return wgrad_opt_v2<FORGE_NADAM>(state_q8, sr, g, a, st);
-    case FORGE_RADAM: return wgrad_opt_v2<FORGE_RADAM>(state_q8, sr, g, a, st);
+    case FORGE_ADAMW: return wgrad_fused_bf16_opt<FORGE_ADAMW>(state_q8, sr, g, a, st);
+    case FORGE_SGD: return wgrad_fused_bf16_opt<FORGE_SGD>(state_q8, sr, g, a, st);
+    case FORGE_SGD_MOMENTUM: return wgrad_fused_bf16_opt<FORGE_SGD_MOMENTUM>(state_q8, sr, g, a, st);
+    case FORGE_LION: return wgrad_fused_bf16_opt<FORGE_LION>(state_q8, sr, g, a, st);
+    case FORGE_RMSPROP: return wgrad_fused_bf16_opt<FORGE_RMSPROP>(state_q8, sr, g, a, st);
+    case FORGE_ADAGRAD: return wgrad_fused_bf16_opt<FORGE_ADAGRAD>(state_q8, sr, g, a, st);
+    case FORGE_NADAM: return wgrad_fused_bf16_opt<FORGE_NADAM>(state_q8, sr, g, a, st);
+    case FORGE_RADAM: return wgrad_fused_bf16_opt<FORGE_RADAM>(state_q8, sr, g, a, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -779,26 +52,17 @@ hipError_t launch_wgrad_store_bf16(const void* X, const void* dY, const GemmDims
       g, [&](auto c) { return g_launch<decltype(c), G_EPI_STORE, FORGE_SGD, false, false>(g, a, st); });
 }
 
-template <int OPT, int FB>
-static hipError_t wgrad_opt_f8(int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
-  if (g_tiles<WgradF8Big<FB>>(g) >= g_num_cus())
-    return sr ? g_launch<WgradF8Big<FB>, G_EPI_OPT, OPT, false, true>(g, a, st)
-              : g_launch<WgradF8Big<FB>, G_EPI_OPT, OPT, false, false>(g, a, st);
-  return sr ? g_launch<WgradF8Small<FB>, G_EPI_OPT, OPT, false, true>(g, a, st)
-            : g_launch<WgradF8Small<FB>, G_EPI_OPT, OPT, false, false>(g, a, st);
-}
-
 template <int FB>
 static hipError_t wgrad_fused_f8(int opt, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
   switch (opt) {
-    case FORGE_ADAMW: return wgrad_opt_f8<FORGE_ADAMW, FB>(sr, g, a, st);
-    case FORGE_SGD: return wgrad_opt_f8<FORGE_SGD, FB>(sr, g, a, st);
-    case FORGE_SGD_MOMENTUM: return wgrad_opt_f8<FORGE_SGD_MOMENTUM, FB>(sr, g, a, st);
-    case FORGE_LION: return wgrad_opt_f8<FORGE_LION, FB>(sr, g, a, st);
-    case FORGE_RMSPROP: return wgrad_opt_f8<FORGE_RMSPROP, FB>(sr, g, a, st);
-    case FORGE_ADAGRAD: return wgrad_opt_f8<FORGE_ADAGRAD, FB>(sr, g, a, st);
-    case FORGE_NADAM: return wgrad_opt_f8<FORGE_NADAM, FB>(sr, g, a, st);
-    case FORGE_RADAM: return wgrad_opt_f8<FORGE_RADAM, FB>(sr, g, a, st);
+    case FORGE_ADAMW: return wgrad_fused_f8_opt<FORGE_ADAMW, FB>(sr, g, a, st);
+    case FORGE_SGD: return wgrad_fused_f8_opt<FORGE_SGD, FB>(sr, g, a, st);
+    case FORGE_SGD_MOMENTUM: return wgrad_fused_f8_opt<FORGE_SGD_MOMENTUM, FB>(sr, g, a, st);
+    case FORGE_LION: return wgrad_fused_f8_opt<FORGE_LION, FB>(sr, g, a, st);
+    case FORGE_RMSPROP: return wgrad_fused_f8_opt<FORGE_RMSPROP, FB>(sr, g, a, st);
+    case FORGE_ADAGRAD: return wgrad_fused_f8_opt<FORGE_ADAGRAD, FB>(sr, g, a, st);
+    case FORGE_NADAM: return wgrad_fused_f8_opt<FORGE_NADAM, FB>(sr, g, a, st);
+    case FORGE_RADAM: return wgrad_fused_f8_opt<FORGE_RADAM, FB>(sr, g, a, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -814,14 +78,7 @@ hipError_t launch_wgrad_store_f8(int dy_e5m2, const void* X, const float* x_scal
                                  const float* dy_scale, const GemmDims& d, float* dW, int64_t ld_dw, hipStream_t st) {
   GArgs g{X, dY, d.ldx, d.lddy, d.in, d.out, d.T, dW, ld_dw, extent(d.T, d.ldx, 1), extent(d.T, d.lddy, 1),
           extent(d.out, ld_dw, 4), x_scale, dy_scale};
-  OptArgs a{};
-  auto run = [&](auto big, auto small) -> hipError_t {
-    using Big = decltype(big);
-    using Small = decltype(small);
-    return g_tiles<Big>(g) >= g_num_cus() ? g_launch<Big, G_EPI_STORE, FORGE_SGD, false, false>(g, a, st)
-                                          : g_launch<Small, G_EPI_STORE, FORGE_SGD, false, false>(g, a, st);
-  };
-  return dy_e5m2 ? run(WgradF8Big<1>{}, WgradF8Small<1>{}) : run(WgradF8Big<0>{}, WgradF8Small<0>{});
+  return dy_e5m2 ? wgrad_store_f8<1>(g, st) : wgrad_store_f8<0>(g, st);
 }
 
 hipError_t launch_dgrad_bf16(const void* dY, int64_t lddy, const void* W, int64_t ldw, void* dX, int64_t lddx,

@@ -1,0 +1,8 @@
+// Fused weight-gradient + optimizer kernels on bf16 / fp32 operands for two of the
+// optimizers (one translation unit per pair, so the library builds in parallel).
+#include "forge_gemm_kernel.h"
+
+namespace forge {
+FORGE_INST_BF16(FORGE_NADAM)
+FORGE_INST_BF16(FORGE_RADAM)
+}  // namespace forge

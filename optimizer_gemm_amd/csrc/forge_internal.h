@@ -249,7 +249,7 @@ hipError_t launch_optimizer(int w_bf16, int state_q8, int opt, int sr, const flo
                             const OptArgs& a, hipStream_t stream);
 hipError_t launch_dgrad(int io_bf16, const void* dY, int64_t lddy, const void* W, int64_t ldw, void* dX,
                         int64_t lddx, int32_t T, int32_t out, int32_t in, hipStream_t stream);
-// bfloat16 kernels (forge_gemm.hip)
+// bfloat16 / FP8 kernels (forge_gemm.hip, forge_gemm_kernel.h)
 hipError_t launch_wgrad_fused_bf16(int state_q8, int opt, int sr, const void* X, const void* dY, const GemmDims& d,
                                    const OptArgs& a, hipStream_t stream);
 hipError_t launch_wgrad_store_bf16(const void* X, const void* dY, const GemmDims& d, float* dW, int64_t ld_dw,

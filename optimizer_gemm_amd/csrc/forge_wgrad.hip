@@ -2,7 +2,7 @@
 // fused optimizer epilogue (FORGE, §2 Method, "Core mechanism": accumulate the
 // tile in FP32 registers, update it in registers, write back only W and the
 // moments) or a plain float32 dW store (the two-phase baseline of §1). The
-// bfloat16 path lives in forge_gemm.hip; this kernel serves float32 layers.
+// bfloat16 path lives in forge_gemm_kernel.h; this kernel serves float32 layers.
 //
 // Mapping: a workgroup owns a BM x BN tile of dW^T (BM along `in`, BN along
 // `out`) with WM x WN wave tiles, replicated KS times to split the token range
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(C::NT) void wgrad_f32_kernel(const void* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Launchers (float32; bfloat16 goes to forge_gemm.hip).
+// Launchers (float32; bfloat16 goes to forge_gemm.hip and forge_gemm_kernel.h).
 // ---------------------------------------------------------------------------
 using CfgF32 = TileCfg<64, 64, 16, 2, 2, 2>;  // 8 waves: 2x2 wave tiles of 32x32, 2-way token split
 
