@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--cold-calls", type=int, default=10,
                    help="fused calls of the first layer timed after a 1 GiB write that evicts the memory-side cache")
     p.add_argument("--opt", default="adamw")
+    p.add_argument("--states", default=None, choices=("f32", "bf16", "q8"),
+                   help="moment storage format (default: the workload's)")
     p.add_argument("--inputs", default="native", choices=("native", "fp8"),
                    help="fp8: the fused step reads X as E4M3 and dY as E5M2 codes with per-tensor scales "
                         "(W and dgrad stay bf16)")
@@ -84,7 +86,7 @@ def _counter_means(db: str, counter: str) -> dict:
 
 
 def _traffic_name(args) -> str:
-    return args.workload + ("_fp8" if args.inputs == "fp8" else "")
+    return args.workload + ("_fp8" if args.inputs == "fp8" else "") + (f"_{args.states}" if args.states else "")
 
 
 def record_traffic(args) -> int:
@@ -155,13 +157,15 @@ def main() -> int:
     else:
         wl = WORKLOADS[args.workload]
         layers, wl_config, state, sr = wl.layers, wl.config, wl.state, wl.stochastic_round
+    if args.states:
+        state = args.states
     opt = args.opt
     dev = torch.device("cuda:0")
     io = layers[0].io
     tdt = torch.bfloat16 if io == "bf16" else torch.float32
     fp8 = args.inputs == "fp8"
-    if fp8 and (io != "bf16" or state != "f32"):
-        print("FP8 inputs need bf16 weights and float32 moments", file=sys.stderr)
+    if fp8 and (io != "bf16" or state == "q8"):
+        print("FP8 inputs need bf16 weights and float32 or bfloat16 moments", file=sys.stderr)
         return 2
 
     def to_dev(a):

@@ -123,16 +123,21 @@ typedef struct {
  *   then the `opt` update of W, m, v in place, with step t = `step` (1-based).
  * X [T, in] and dY [T, out] are read only; W [out, in] is updated in place.
  * dtypes: X, dY, W all FORGE_F32, or all FORGE_BF16. m and v: FORGE_F32, or
- * FORGE_I8 (m) and FORGE_U8 (v) with block scales (requires in % 64 == 0).
+ * FORGE_I8 (m) and FORGE_U8 (v) with block scales (requires in % 64 == 0), or
+ * FORGE_BF16 (with bf16 W; ld a multiple of 8; step < 2^30).
  * Slots an optimizer does not use may be NULL and are never touched:
  *   SGD: none; SGD-momentum, Lion: m; RMSprop, AdaGrad: v; others: m and v.
  * bfloat16 W is written with stochastic rounding (hyper->stochastic_round)
  * driven by a counter hash: r16 = top 16 bits of the SplitMix64 output number
  * ((step << 32) | (o*in + i)) + 1 from state `seed`; bf16 = (bits(w32) + r16) >> 16
- * (NaN -> quiet NaN). T == 0 is allowed (zero gradient). Requires out*in < 2^32.
+ * (NaN -> quiet NaN). bfloat16 m and v are rounded the same way from their float32
+ * update (the weight update uses the unrounded moments), with their own streams:
+ * the seed is seed + 2^62 for m and seed + 2^63 for v (W: seed); with
+ * stochastic_round = 0 all three round to nearest-even.
+ * T == 0 is allowed (zero gradient). Requires out*in < 2^32.
  * FP8 inputs (the pages' outlook, §5): X FORGE_E4M3 and dY FORGE_E4M3 or
  * FORGE_E5M2, each with its scale (see forge_tensor), with W FORGE_BF16 and
- * float32 m, v; cols and ld of X and dY must be multiples of 16 (else
+ * float32 or bfloat16 m, v; cols and ld of X and dY must be multiples of 16 (else
  * FORGE_ERR_ALIGN); INT8 moments with FP8 inputs return FORGE_ERR_UNSUPPORTED. The
  * gradient is (sum over tokens of the decoded code products) * scale_X * scale_dY.
  * Must be enqueued after forge_linear_dgrad of the same layer (which reads the old W).

@@ -96,7 +96,7 @@ int check_hyper(int opt, const forge_hyper* h, int64_t step) {
   return FORGE_OK;
 }
 
-// Moment slots: returns the state format (ST_F32 / ST_Q8) or a negative status.
+// Moment slots: returns the state format (ST_F32 / ST_Q8 / ST_BF16) or a negative status.
 int check_states(int opt, int io_dtype, const forge_tensor* W, const forge_tensor* m, const forge_tensor* v) {
   const int sl = opt_slots(opt);
   const forge_tensor* slot[2] = {m, v};
@@ -112,6 +112,10 @@ int check_states(int opt, int io_dtype, const forge_tensor* W, const forge_tenso
     if (t->dtype == FORGE_F32) {
       f = ST_F32;
       if (!aligned16(t->data) || t->ld % 4) return FORGE_ERR_ALIGN;
+    } else if (t->dtype == FORGE_BF16) {
+      f = ST_BF16;
+      if (io_dtype != FORGE_BF16) return FORGE_ERR_DTYPE;
+      if (!aligned16(t->data) || t->ld % 8) return FORGE_ERR_ALIGN;
     } else if ((k == 0 && t->dtype == FORGE_I8) || (k == 1 && t->dtype == FORGE_U8)) {
       f = ST_Q8;
       if (io_dtype != FORGE_BF16) return FORGE_ERR_DTYPE;
@@ -307,6 +311,7 @@ int forge_linear_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge
   if (X->rows != dY->rows || X->cols != W->cols || dY->cols != W->rows) return FORGE_ERR_SHAPE;
   const int fmt = check_states(opt, io, W, m, v);
   if (fmt < 0) return fmt;
+  if (fmt == ST_BF16 && step >= ((int64_t)1 << 30)) return FORGE_ERR_HYPER;
   if (f8 && fmt == ST_Q8) return FORGE_ERR_UNSUPPORTED;
   if (W->rows * W->cols >= ((int64_t)1 << 32)) return FORGE_ERR_UNSUPPORTED;
   const int sl = opt_slots(opt);
@@ -321,10 +326,9 @@ int forge_linear_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge
   const OptArgs a = make_args(W, m, v, opt, s, seed, step);
   const GemmDims d{(int32_t)X->rows, (int32_t)W->rows, (int32_t)W->cols, X->ld, dY->ld};
   const int sr = (io == FORGE_BF16 && hyper->stochastic_round) ? 1 : 0;
-  hipError_t e = f8 ? launch_wgrad_fused_f8(dY->dtype == FORGE_E5M2, opt, sr, X->data, X->scale, dY->data, dY->scale,
-                                            d, a, (hipStream_t)stream)
-                    : launch_wgrad_fused(io == FORGE_BF16, fmt == ST_Q8, opt, sr, X->data, dY->data, d, a,
-                                         (hipStream_t)stream);
+  hipError_t e = f8 ? launch_wgrad_fused_f8(dY->dtype == FORGE_E5M2, fmt, opt, sr, X->data, X->scale, dY->data,
+                                            dY->scale, d, a, (hipStream_t)stream)
+                    : launch_wgrad_fused(io == FORGE_BF16, fmt, opt, sr, X->data, dY->data, d, a, (hipStream_t)stream);
   return e == hipSuccess ? FORGE_OK : FORGE_ERR_HIP;
 }
 
@@ -386,6 +390,7 @@ int forge_optimizer_step(const float* dW, int64_t ld_dw, forge_tensor* W, forge_
   if (!aligned16(dW) || ld_dw % 4) return FORGE_ERR_ALIGN;
   const int fmt = check_states(opt, io, W, m, v);
   if (fmt < 0) return fmt;
+  if (fmt == ST_BF16 && step >= ((int64_t)1 << 30)) return FORGE_ERR_HYPER;
   if (W->rows * W->cols >= ((int64_t)1 << 32)) return FORGE_ERR_UNSUPPORTED;
   const int sl = opt_slots(opt);
   const forge_tensor dWt{const_cast<float*>(dW), FORGE_F32, 0, W->rows, W->cols, ld_dw, nullptr};
@@ -397,7 +402,7 @@ int forge_optimizer_step(const float* dW, int64_t ld_dw, forge_tensor* W, forge_
   if (W->rows == 0 || W->cols == 0) return FORGE_OK;
   const OptArgs a = make_args(W, m, v, opt, s, seed, step);
   const int sr = (io == FORGE_BF16 && hyper->stochastic_round) ? 1 : 0;
-  hipError_t e = launch_optimizer(io == FORGE_BF16, fmt == ST_Q8, opt, sr, dW, ld_dw, a, (hipStream_t)stream);
+  hipError_t e = launch_optimizer(io == FORGE_BF16, fmt, opt, sr, dW, ld_dw, a, (hipStream_t)stream);
   return e == hipSuccess ? FORGE_OK : FORGE_ERR_HIP;
 }
 

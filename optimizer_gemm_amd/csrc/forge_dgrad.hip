@@ -160,8 +160,9 @@ hipError_t launch_dgrad(int io_bf16, const void* dY, int64_t lddy, const void* W
 // consecutive elements of one row; 16 consecutive threads cover one INT8 block
 // of 64 (rows are multiples of 64 long in that mode).
 // ---------------------------------------------------------------------------
-template <bool W_BF16, int OPT, bool Q8, bool SR>
+template <bool W_BF16, int OPT, int SF, bool SR>
 __global__ __launch_bounds__(256) void optimizer_kernel(const float* __restrict__ dW, int64_t ld_dw, OptArgs a) {
+  constexpr bool Q8 = SF == ST_Q8, B16S = SF == ST_BF16;
   constexpr int SL = opt_slots(OPT);
   constexpr bool HAS_M = SL & 1, HAS_V = SL & 2;
   const int64_t vec_per_row = a.in >> 2;
@@ -177,6 +178,9 @@ __global__ __launch_bounds__(256) void optimizer_kernel(const float* __restrict_
     if constexpr (Q8) {
       if constexpr (HAS_M) dequant_m4(a, o, i, m);
       if constexpr (HAS_V) dequant_v4(a, o, i, v);
+    } else if constexpr (B16S) {
+      if constexpr (HAS_M) bf16x4_to_f32(*reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.m) + (int64_t)o * a.ldm + i), m);
+      if constexpr (HAS_V) bf16x4_to_f32(*reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.v) + (int64_t)o * a.ldv + i), v);
     } else {
       if constexpr (HAS_M) load_f4(a.m, a.ldm, o, i, m);
       if constexpr (HAS_V) load_f4(a.v, a.ldv, o, i, v);
@@ -210,6 +214,16 @@ __global__ __launch_bounds__(256) void optimizer_kernel(const float* __restrict_
         if constexpr (HAS_V) a.v_scale[si] = sv;
       }
     }
+  } else if constexpr (B16S) {
+    if (valid) {
+      const uint32_t idx0 = (uint32_t)o * (uint32_t)a.in + (uint32_t)i;
+      if constexpr (HAS_M)
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.m) + (int64_t)o * a.ldm + i) =
+            pack_bf16x4<SR>(m, rng_stream_base(a.rng_base, 1), idx0);
+      if constexpr (HAS_V)
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.v) + (int64_t)o * a.ldv + i) =
+            pack_bf16x4<SR>(v, rng_stream_base(a.rng_base, 2), idx0);
+    }
   } else {
     if (valid) {
       if constexpr (HAS_M) store_f4(a.m, a.ldm, o, i, m);
@@ -218,35 +232,40 @@ __global__ __launch_bounds__(256) void optimizer_kernel(const float* __restrict_
   }
 }
 
+template <int OPT, int SF>
+static void launch_opt_sf(int sr, dim3 grid, const float* dW, int64_t ld_dw, const OptArgs& a, hipStream_t st) {
+  if (sr) hipLaunchKernelGGL((optimizer_kernel<true, OPT, SF, true>), grid, dim3(256), 0, st, dW, ld_dw, a);
+  else hipLaunchKernelGGL((optimizer_kernel<true, OPT, SF, false>), grid, dim3(256), 0, st, dW, ld_dw, a);
+}
+
 template <int OPT>
-static hipError_t launch_opt_t(int w_bf16, int q8, int sr, const float* dW, int64_t ld_dw, const OptArgs& a,
+static hipError_t launch_opt_t(int w_bf16, int sf, int sr, const float* dW, int64_t ld_dw, const OptArgs& a,
                                hipStream_t st) {
   const int64_t total = (int64_t)a.out * (a.in >> 2);
   if (total == 0) return hipSuccess;
-  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
-  if (!w_bf16) {
-    hipLaunchKernelGGL((optimizer_kernel<false, OPT, false, false>), grid, block, 0, st, dW, ld_dw, a);
-  } else if (q8) {
-    if (sr) hipLaunchKernelGGL((optimizer_kernel<true, OPT, true, true>), grid, block, 0, st, dW, ld_dw, a);
-    else hipLaunchKernelGGL((optimizer_kernel<true, OPT, true, false>), grid, block, 0, st, dW, ld_dw, a);
-  } else {
-    if (sr) hipLaunchKernelGGL((optimizer_kernel<true, OPT, false, true>), grid, block, 0, st, dW, ld_dw, a);
-    else hipLaunchKernelGGL((optimizer_kernel<true, OPT, false, false>), grid, block, 0, st, dW, ld_dw, a);
-  }
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (!w_bf16)
+    hipLaunchKernelGGL((optimizer_kernel<false, OPT, ST_F32, false>), grid, dim3(256), 0, st, dW, ld_dw, a);
+  else if (sf == ST_Q8)
+    launch_opt_sf<OPT, ST_Q8>(sr, grid, dW, ld_dw, a, st);
+  else if (sf == ST_BF16)
+    launch_opt_sf<OPT, ST_BF16>(sr, grid, dW, ld_dw, a, st);
+  else
+    launch_opt_sf<OPT, ST_F32>(sr, grid, dW, ld_dw, a, st);
   return hipGetLastError();
 }
 
-hipError_t launch_optimizer(int w_bf16, int state_q8, int opt, int sr, const float* dW, int64_t ld_dw,
+hipError_t launch_optimizer(int w_bf16, int state_fmt, int opt, int sr, const float* dW, int64_t ld_dw,
                             const OptArgs& a, hipStream_t stream) {
   switch (opt) {
-    case FORGE_ADAMW: return launch_opt_t<FORGE_ADAMW>(w_bf16, state_q8, sr, dW, ld_dw, a, stream);
-    case FORGE_SGD: return launch_opt_t<FORGE_SGD>(w_bf16, state_q8, sr, dW, ld_dw, a, stream);
-    case FORGE_SGD_MOMENTUM: return launch_opt_t<FORGE_SGD_MOMENTUM>(w_bf16, state_q8, sr, dW, ld_dw, a, stream);
-    case FORGE_LION: return launch_opt_t<FORGE_LION>(w_bf16, state_q8, sr, dW, ld_dw, a, stream);
-    case FORGE_RMSPROP: return launch_opt_t<FORGE_RMSPROP>(w_bf16, state_q8, sr, dW, ld_dw, a, stream);
-    case FORGE_ADAGRAD: return launch_opt_t<FORGE_ADAGRAD>(w_bf16, state_q8, sr, dW, ld_dw, a, stream);
-    case FORGE_NADAM: return launch_opt_t<FORGE_NADAM>(w_bf16, state_q8, sr, dW, ld_dw, a, stream);
-    case FORGE_RADAM: return launch_opt_t<FORGE_RADAM>(w_bf16, state_q8, sr, dW, ld_dw, a, stream);
+    case FORGE_ADAMW: return launch_opt_t<FORGE_ADAMW>(w_bf16, state_fmt, sr, dW, ld_dw, a, stream);
+    case FORGE_SGD: return launch_opt_t<FORGE_SGD>(w_bf16, state_fmt, sr, dW, ld_dw, a, stream);
+    case FORGE_SGD_MOMENTUM: return launch_opt_t<FORGE_SGD_MOMENTUM>(w_bf16, state_fmt, sr, dW, ld_dw, a, stream);
+    case FORGE_LION: return launch_opt_t<FORGE_LION>(w_bf16, state_fmt, sr, dW, ld_dw, a, stream);
+    case FORGE_RMSPROP: return launch_opt_t<FORGE_RMSPROP>(w_bf16, state_fmt, sr, dW, ld_dw, a, stream);
+    case FORGE_ADAGRAD: return launch_opt_t<FORGE_ADAGRAD>(w_bf16, state_fmt, sr, dW, ld_dw, a, stream);
+    case FORGE_NADAM: return launch_opt_t<FORGE_NADAM>(w_bf16, state_fmt, sr, dW, ld_dw, a, stream);
+    case FORGE_RADAM: return launch_opt_t<FORGE_RADAM>(w_bf16, state_fmt, sr, dW, ld_dw, a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -26,19 +26,19 @@ FORGE_EXTERN_BF16(FORGE_RADAM)
 FORGE_EXTERN_F8_ALL(0)
 FORGE_EXTERN_F8_ALL(1)
 
-hipError_t launch_wgrad_fused_bf16(int state_q8, int opt, int sr, const void* X, const void* dY, const GemmDims& d,
+hipError_t launch_wgrad_fused_bf16(int state_fmt, int opt, int sr, const void* X, const void* dY, const GemmDims& d,
                                    const OptArgs& a, hipStream_t st) {
   GArgs g{X, dY, d.ldx, d.lddy,
           d.in, d.out, d.T, nullptr, 0, extent(d.T, d.ldx, 2), extent(d.T, d.lddy, 2), 0};
   switch (opt) {
-    case FORGE_ADAMW: return wgrad_fused_bf16_opt<FORGE_ADAMW>(state_q8, sr, g, a, st);
-    case FORGE_SGD: return wgrad_fused_bf16_opt<FORGE_SGD>(state_q8, sr, g, a, st);
-    case FORGE_SGD_MOMENTUM: return wgrad_fused_bf16_opt<FORGE_SGD_MOMENTUM>(state_q8, sr, g, a, st);
-    case FORGE_LION: return wgrad_fused_bf16_opt<FORGE_LION>(state_q8, sr, g, a, st);
-    case FORGE_RMSPROP: return wgrad_fused_bf16_opt<FORGE_RMSPROP>(state_q8, sr, g, a, st);
-    case FORGE_ADAGRAD: return wgrad_fused_bf16_opt<FORGE_ADAGRAD>(state_q8, sr, g, a, st);
-    case FORGE_NADAM: return wgrad_fused_bf16_opt<FORGE_NADAM>(state_q8, sr, g, a, st);
-    case FORGE_RADAM: return wgrad_fused_bf16_opt<FORGE_RADAM>(state_q8, sr, g, a, st);
+    case FORGE_ADAMW: return wgrad_fused_bf16_opt<FORGE_ADAMW>(state_fmt, sr, g, a, st);
+    case FORGE_SGD: return wgrad_fused_bf16_opt<FORGE_SGD>(state_fmt, sr, g, a, st);
+    case FORGE_SGD_MOMENTUM: return wgrad_fused_bf16_opt<FORGE_SGD_MOMENTUM>(state_fmt, sr, g, a, st);
+    case FORGE_LION: return wgrad_fused_bf16_opt<FORGE_LION>(state_fmt, sr, g, a, st);
+    case FORGE_RMSPROP: return wgrad_fused_bf16_opt<FORGE_RMSPROP>(state_fmt, sr, g, a, st);
+    case FORGE_ADAGRAD: return wgrad_fused_bf16_opt<FORGE_ADAGRAD>(state_fmt, sr, g, a, st);
+    case FORGE_NADAM: return wgrad_fused_bf16_opt<FORGE_NADAM>(state_fmt, sr, g, a, st);
+    case FORGE_RADAM: return wgrad_fused_bf16_opt<FORGE_RADAM>(state_fmt, sr, g, a, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -49,29 +49,29 @@ hipError_t launch_wgrad_store_bf16(const void* X, const void* dY, const GemmDims
           d.in, d.out, d.T, dW, ld_dw, extent(d.T, d.ldx, 2), extent(d.T, d.lddy, 2), extent(d.out, ld_dw, 4)};
   OptArgs a{};
   return g_pick<WgradBig, WgradSmall, WgradSplit>(
-      g, [&](auto c) { return g_launch<decltype(c), G_EPI_STORE, FORGE_SGD, false, false>(g, a, st); });
+      g, [&](auto c) { return g_launch<decltype(c), G_EPI_STORE, FORGE_SGD, ST_F32, false>(g, a, st); });
 }
 
 template <int FB>
-static hipError_t wgrad_fused_f8(int opt, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
+static hipError_t wgrad_fused_f8(int sf, int opt, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
   switch (opt) {
-    case FORGE_ADAMW: return wgrad_fused_f8_opt<FORGE_ADAMW, FB>(sr, g, a, st);
-    case FORGE_SGD: return wgrad_fused_f8_opt<FORGE_SGD, FB>(sr, g, a, st);
-    case FORGE_SGD_MOMENTUM: return wgrad_fused_f8_opt<FORGE_SGD_MOMENTUM, FB>(sr, g, a, st);
-    case FORGE_LION: return wgrad_fused_f8_opt<FORGE_LION, FB>(sr, g, a, st);
-    case FORGE_RMSPROP: return wgrad_fused_f8_opt<FORGE_RMSPROP, FB>(sr, g, a, st);
-    case FORGE_ADAGRAD: return wgrad_fused_f8_opt<FORGE_ADAGRAD, FB>(sr, g, a, st);
-    case FORGE_NADAM: return wgrad_fused_f8_opt<FORGE_NADAM, FB>(sr, g, a, st);
-    case FORGE_RADAM: return wgrad_fused_f8_opt<FORGE_RADAM, FB>(sr, g, a, st);
+    case FORGE_ADAMW: return wgrad_fused_f8_opt<FORGE_ADAMW, FB>(sf, sr, g, a, st);
+    case FORGE_SGD: return wgrad_fused_f8_opt<FORGE_SGD, FB>(sf, sr, g, a, st);
+    case FORGE_SGD_MOMENTUM: return wgrad_fused_f8_opt<FORGE_SGD_MOMENTUM, FB>(sf, sr, g, a, st);
+    case FORGE_LION: return wgrad_fused_f8_opt<FORGE_LION, FB>(sf, sr, g, a, st);
+    case FORGE_RMSPROP: return wgrad_fused_f8_opt<FORGE_RMSPROP, FB>(sf, sr, g, a, st);
+    case FORGE_ADAGRAD: return wgrad_fused_f8_opt<FORGE_ADAGRAD, FB>(sf, sr, g, a, st);
+    case FORGE_NADAM: return wgrad_fused_f8_opt<FORGE_NADAM, FB>(sf, sr, g, a, st);
+    case FORGE_RADAM: return wgrad_fused_f8_opt<FORGE_RADAM, FB>(sf, sr, g, a, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_wgrad_fused_f8(int dy_e5m2, int opt, int sr, const void* X, const float* x_scale, const void* dY,
+hipError_t launch_wgrad_fused_f8(int dy_e5m2, int state_fmt, int opt, int sr, const void* X, const float* x_scale, const void* dY,
                                  const float* dy_scale, const GemmDims& d, const OptArgs& a, hipStream_t st) {
   GArgs g{X, dY, d.ldx, d.lddy, d.in, d.out, d.T, nullptr, 0, extent(d.T, d.ldx, 1), extent(d.T, d.lddy, 1), 0,
           x_scale, dy_scale};
-  return dy_e5m2 ? wgrad_fused_f8<1>(opt, sr, g, a, st) : wgrad_fused_f8<0>(opt, sr, g, a, st);
+  return dy_e5m2 ? wgrad_fused_f8<1>(state_fmt, opt, sr, g, a, st) : wgrad_fused_f8<0>(state_fmt, opt, sr, g, a, st);
 }
 
 hipError_t launch_wgrad_store_f8(int dy_e5m2, const void* X, const float* x_scale, const void* dY,
@@ -87,7 +87,7 @@ hipError_t launch_dgrad_bf16(const void* dY, int64_t lddy, const void* W, int64_
           n_in, T, n_out, dX, lddx, extent(n_out, ldw, 2), extent(T, lddy, 2), extent(T, lddx, 2)};
   OptArgs a{};
   return g_pick<DgradBig, DgradSmall, DgradSplit>(
-      g, [&](auto c) { return g_launch<decltype(c), G_EPI_DX, FORGE_SGD, false, false>(g, a, st); });
+      g, [&](auto c) { return g_launch<decltype(c), G_EPI_DX, FORGE_SGD, ST_F32, false>(g, a, st); });
 }
 
 }  // namespace forge

@@ -238,13 +238,14 @@ struct EpiRes {
   __amdgpu_buffer_rsrc_t W, m, v, ms, vs;
 };
 
-template <int OPT, bool Q8>
+template <int OPT, int SF>
 __device__ __forceinline__ EpiRes epi_res(const OptArgs& a) {
   EpiRes r;
+  constexpr bool Q8 = SF == ST_Q8;
   const uint32_t n = (uint32_t)a.out;
   r.W = make_rsrc(a.W, n * (uint32_t)a.ldw * 2u);
   constexpr int SL = opt_slots(OPT);
-  const uint32_t es = Q8 ? 1u : 4u;
+  const uint32_t es = Q8 ? 1u : (SF == ST_BF16 ? 2u : 4u);
   r.m = make_rsrc((SL & 1) ? a.m : a.W, (SL & 1) ? n * (uint32_t)a.ldm * es : 0u);
   r.v = make_rsrc((SL & 2) ? a.v : a.W, (SL & 2) ? n * (uint32_t)a.ldv * es : 0u);
   const uint32_t sb = Q8 ? n * (uint32_t)(a.in >> 6) * 4u : 0u;
@@ -253,9 +254,11 @@ __device__ __forceinline__ EpiRes epi_res(const OptArgs& a) {
   return r;
 }
 
-template <class C, int EPI, int OPT, bool Q8, bool SR>
+// SF: moment storage format (StateFmt: float32, INT8 block-64, or bfloat16).
+template <class C, int EPI, int OPT, int SF, bool SR>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
 void gemm_kernel(GArgs g, OptArgs a) {
+  constexpr bool Q8 = SF == ST_Q8, B16S = SF == ST_BF16;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::SMEM_BYTES];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -556,7 +559,7 @@ void gemm_kernel(GArgs g, OptArgs a) {
       } else {
         constexpr int SL = opt_slots(OPT);
         constexpr bool HAS_M = SL & 1, HAS_V = SL & 2;
-        const EpiRes R = epi_res<OPT, Q8>(a);
+        const EpiRes R = epi_res<OPT, SF>(a);
         // loads of KB vectors are issued before any of them is consumed; KB bounds the
         // registers a batch holds next to the accumulators still to be written out
         constexpr int KB_MAX = C::OCC >= 2 ? 2 : (Q8 ? 4 : 8);
@@ -564,7 +567,7 @@ void gemm_kernel(GArgs g, OptArgs a) {
 #pragma unroll
         for (int kb = 0; kb < NV; kb += KB) {
         uint32_t ow[KB], om[KB], ov_[KB], osc[KB];
-        u32x2 wb[KB];
+        u32x2 wb[KB], mb[KB], vb[KB];
         f32x4 mv[KB], vv[KB];
         uint32_t qm[KB], qv[KB];
         float msc[KB], vsc[KB];
@@ -575,7 +578,12 @@ void gemm_kernel(GArgs g, OptArgs a) {
           const bool ok = o < g.N && i < g.M;
           ow[k] = ok ? (uint32_t)(o * a.ldw + i) * 2u : kOOB;
           wb[k] = __builtin_amdgcn_raw_buffer_load_b64(R.W, ow[k], 0, 0);
-          if constexpr (!Q8) {
+          if constexpr (B16S) {
+            om[k] = ok ? (uint32_t)(o * a.ldm + i) * 2u : kOOB;
+            ov_[k] = ok ? (uint32_t)(o * a.ldv + i) * 2u : kOOB;
+            if constexpr (HAS_M) mb[k] = __builtin_amdgcn_raw_buffer_load_b64(R.m, om[k], 0, 0);
+            if constexpr (HAS_V) vb[k] = __builtin_amdgcn_raw_buffer_load_b64(R.v, ov_[k], 0, 0);
+          } else if constexpr (!Q8) {
             om[k] = ok ? (uint32_t)(o * a.ldm + i) * 4u : kOOB;
             ov_[k] = ok ? (uint32_t)(o * a.ldv + i) * 4u : kOOB;
             if constexpr (HAS_M) mv[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(R.m, om[k], 0, 0));
@@ -604,7 +612,10 @@ void gemm_kernel(GArgs g, OptArgs a) {
           float w[4] = {bits_f32(wb[k].x << 16), bits_f32(wb[k].x & 0xFFFF0000u), bits_f32(wb[k].y << 16),
                         bits_f32(wb[k].y & 0xFFFF0000u)};
           float m[4] = {0.f, 0.f, 0.f, 0.f}, v[4] = {0.f, 0.f, 0.f, 0.f};
-          if constexpr (!Q8) {
+          if constexpr (B16S) {
+            if constexpr (HAS_M) bf16x4_to_f32(mb[k], m);
+            if constexpr (HAS_V) bf16x4_to_f32(vb[k], v);
+          } else if constexpr (!Q8) {
             if constexpr (HAS_M) { m[0] = mv[k].x; m[1] = mv[k].y; m[2] = mv[k].z; m[3] = mv[k].w; }
             if constexpr (HAS_V) { v[0] = vv[k].x; v[1] = vv[k].y; v[2] = vv[k].z; v[3] = vv[k].w; }
           } else {
@@ -628,7 +639,14 @@ void gemm_kernel(GArgs g, OptArgs a) {
           for (int j = 0; j < 4; ++j)
             bb[j] = SR ? sr_bf16_bits(w[j], rand16_from_base(a.rng_base, idx0 + j)) : rne_bf16_bits(w[j]);
           __builtin_amdgcn_raw_buffer_store_b64(u32x2{bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16)}, R.W, ow[k], 0, 0);
-          if constexpr (!Q8) {
+          if constexpr (B16S) {
+            if constexpr (HAS_M)
+              __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4<SR>(m, rng_stream_base(a.rng_base, 1), idx0), R.m, om[k],
+                                                    0, 0);
+            if constexpr (HAS_V)
+              __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4<SR>(v, rng_stream_base(a.rng_base, 2), idx0), R.v,
+                                                    ov_[k], 0, 0);
+          } else if constexpr (!Q8) {
             if constexpr (HAS_M)
               __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{m[0], m[1], m[2], m[3]}), R.m, om[k], 0, 0);
             if constexpr (HAS_V)
@@ -724,13 +742,13 @@ static int g_num_cus() {
   return n;
 }
 
-template <class C, int EPI, int OPT, bool Q8, bool SR>
+template <class C, int EPI, int OPT, int SF, bool SR>
 static hipError_t g_launch(const GArgs& g, const OptArgs& a, hipStream_t st) {
   const int ntiles = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN);
   if (ntiles == 0) return hipSuccess;
   const int resident = C::OCC * 4 / C::NW * g_num_cus();  // OCC waves on each of 4 SIMDs
   const int grid = ntiles < resident ? ntiles : resident;
-  hipLaunchKernelGGL((gemm_kernel<C, EPI, OPT, Q8, SR>), dim3(grid), dim3(C::NT), 0, st, g, a);
+  hipLaunchKernelGGL((gemm_kernel<C, EPI, OPT, SF, SR>), dim3(grid), dim3(C::NT), 0, st, g, a);
   return hipGetLastError();
 }
 
@@ -751,32 +769,47 @@ static uint32_t extent(int64_t rows, int64_t ld, int64_t es) { return (uint32_t)
 
 // Fused step for one optimizer on bf16 / fp32 operands (instantiated per optimizer
 // in the forge_gemm_bf16_*.hip sources).
+template <class C, int OPT>
+static hipError_t g_launch_opt(int sf, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
+  switch (sf) {
+    case ST_Q8:
+      return sr ? g_launch<C, G_EPI_OPT, OPT, ST_Q8, true>(g, a, st) : g_launch<C, G_EPI_OPT, OPT, ST_Q8, false>(g, a, st);
+    case ST_BF16:
+      return sr ? g_launch<C, G_EPI_OPT, OPT, ST_BF16, true>(g, a, st)
+                : g_launch<C, G_EPI_OPT, OPT, ST_BF16, false>(g, a, st);
+    default:
+      return sr ? g_launch<C, G_EPI_OPT, OPT, ST_F32, true>(g, a, st) : g_launch<C, G_EPI_OPT, OPT, ST_F32, false>(g, a, st);
+  }
+}
+
 template <int OPT>
-hipError_t wgrad_fused_bf16_opt(int q8, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
-  return g_pick<WgradBig, WgradSmall, WgradSplit>(g, [&](auto c) {
-    using C = decltype(c);
-    if (q8) return sr ? g_launch<C, G_EPI_OPT, OPT, true, true>(g, a, st) : g_launch<C, G_EPI_OPT, OPT, true, false>(g, a, st);
-    return sr ? g_launch<C, G_EPI_OPT, OPT, false, true>(g, a, st) : g_launch<C, G_EPI_OPT, OPT, false, false>(g, a, st);
-  });
+hipError_t wgrad_fused_bf16_opt(int sf, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
+  return g_pick<WgradBig, WgradSmall, WgradSplit>(
+      g, [&](auto c) { return g_launch_opt<decltype(c), OPT>(sf, sr, g, a, st); });
 }
 
 // FP8 operands, dY in format FB (0 = E4M3, 1 = E5M2): the fused step of one
 // optimizer, and the float32 dW store (instantiated in forge_gemm_f8_*.hip).
+template <class C, int OPT>
+static hipError_t g_launch_opt_f8(int sf, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
+  if (sf == ST_BF16)
+    return sr ? g_launch<C, G_EPI_OPT, OPT, ST_BF16, true>(g, a, st) : g_launch<C, G_EPI_OPT, OPT, ST_BF16, false>(g, a, st);
+  return sr ? g_launch<C, G_EPI_OPT, OPT, ST_F32, true>(g, a, st) : g_launch<C, G_EPI_OPT, OPT, ST_F32, false>(g, a, st);
+}
+
+// sf: ST_F32 or ST_BF16 (INT8 moments are not offered with FP8 inputs)
 template <int OPT, int FB>
-hipError_t wgrad_fused_f8_opt(int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
-  if (g_tiles<WgradF8Big<FB>>(g) >= g_num_cus())
-    return sr ? g_launch<WgradF8Big<FB>, G_EPI_OPT, OPT, false, true>(g, a, st)
-              : g_launch<WgradF8Big<FB>, G_EPI_OPT, OPT, false, false>(g, a, st);
-  return sr ? g_launch<WgradF8Small<FB>, G_EPI_OPT, OPT, false, true>(g, a, st)
-            : g_launch<WgradF8Small<FB>, G_EPI_OPT, OPT, false, false>(g, a, st);
+hipError_t wgrad_fused_f8_opt(int sf, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
+  if (g_tiles<WgradF8Big<FB>>(g) >= g_num_cus()) return g_launch_opt_f8<WgradF8Big<FB>, OPT>(sf, sr, g, a, st);
+  return g_launch_opt_f8<WgradF8Small<FB>, OPT>(sf, sr, g, a, st);
 }
 
 template <int FB>
 hipError_t wgrad_store_f8(const GArgs& g, hipStream_t st) {
   OptArgs a{};
   if (g_tiles<WgradF8Big<FB>>(g) >= g_num_cus())
-    return g_launch<WgradF8Big<FB>, G_EPI_STORE, FORGE_SGD, false, false>(g, a, st);
-  return g_launch<WgradF8Small<FB>, G_EPI_STORE, FORGE_SGD, false, false>(g, a, st);
+    return g_launch<WgradF8Big<FB>, G_EPI_STORE, FORGE_SGD, ST_F32, false>(g, a, st);
+  return g_launch<WgradF8Small<FB>, G_EPI_STORE, FORGE_SGD, ST_F32, false>(g, a, st);
 }
 
 #define FORGE_EXTERN_BF16(OPT) \
@@ -784,8 +817,8 @@ hipError_t wgrad_store_f8(const GArgs& g, hipStream_t st) {
 #define FORGE_INST_BF16(OPT) \
   template hipError_t wgrad_fused_bf16_opt<OPT>(int, int, const GArgs&, const OptArgs&, hipStream_t);
 #define FORGE_EXTERN_F8(OPT, FB) \
-  extern template hipError_t wgrad_fused_f8_opt<OPT, FB>(int, const GArgs&, const OptArgs&, hipStream_t);
+  extern template hipError_t wgrad_fused_f8_opt<OPT, FB>(int, int, const GArgs&, const OptArgs&, hipStream_t);
 #define FORGE_INST_F8(OPT, FB) \
-  template hipError_t wgrad_fused_f8_opt<OPT, FB>(int, const GArgs&, const OptArgs&, hipStream_t);
+  template hipError_t wgrad_fused_f8_opt<OPT, FB>(int, int, const GArgs&, const OptArgs&, hipStream_t);
 
 }  // namespace forge

@@ -22,7 +22,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // State formats of the moment slots.
-enum StateFmt { ST_F32 = 0, ST_Q8 = 1 };
+enum StateFmt { ST_F32 = 0, ST_Q8 = 1, ST_BF16 = 2 };
 // Which slots an optimizer keeps (bit 0: m, bit 1: v).
 __host__ __device__ constexpr int opt_slots(int opt) {
   return opt == FORGE_ADAMW ? 3 : opt == FORGE_SGD ? 0 : opt == FORGE_SGD_MOMENTUM ? 1
@@ -47,6 +47,12 @@ __host__ __device__ __forceinline__ uint64_t splitmix64_mix(uint64_t z) {
 // is computed once per launch: base = seed + gamma*(step<<32).
 __host__ __device__ __forceinline__ uint64_t rng_base(uint64_t seed, uint64_t step) {
   return seed + 0x9E3779B97F4A7C15ull * (step << 32);
+}
+// Independent streams for the bfloat16 write-backs of one element: stream s uses
+// the seed seed + s * 2^62 (W: 0, m: 1, v: 2). For steps below 2^30 the counters of
+// different streams never reach the same SplitMix64 state.
+__host__ __device__ __forceinline__ uint64_t rng_stream_base(uint64_t base, int s) {
+  return base + ((uint64_t)s << 62);
 }
 __host__ __device__ __forceinline__ uint32_t rand16_from_base(uint64_t base, uint32_t idx) {
   uint64_t z = base + 0x9E3779B97F4A7C15ull * ((uint64_t)idx + 1ull);
@@ -134,8 +140,8 @@ __device__ __forceinline__ void opt_apply(float g, float& w, float& m, float& v,
 // stand-alone element-wise kernel of the unfused baseline.
 struct OptArgs {
   void* W;            // [out, ldw] bf16 or f32
-  void* m;            // [out, ldm] f32 or int8
-  void* v;            // [out, ldv] f32 or uint8
+  void* m;            // [out, ldm] f32, bf16 or int8
+  void* v;            // [out, ldv] f32, bf16 or uint8
   float* m_scale;     // [out, in/64]  (Q8 only)
   float* v_scale;     // [out, in/64]  (Q8 only)
   int64_t ldw, ldm, ldv;
@@ -162,6 +168,23 @@ __device__ __forceinline__ void load_w4(const OptArgs& a, int o, int i, float w[
 }
 
 // Stores 4 consecutive weights; bfloat16 with stochastic rounding or nearest-even.
+// Four consecutive bfloat16 values (8 bytes) <-> float.
+__device__ __forceinline__ void bf16x4_to_f32(u32x2 r, float x[4]) {
+  x[0] = bits_f32(r.x << 16);
+  x[1] = bits_f32(r.x & 0xFFFF0000u);
+  x[2] = bits_f32(r.y << 16);
+  x[3] = bits_f32(r.y & 0xFFFF0000u);
+}
+// Rounds four consecutive elements (flat index idx0..idx0+3) to bfloat16:
+// stochastically with the r16 of the stream whose base is `base`, or to nearest-even.
+template <bool SR>
+__device__ __forceinline__ u32x2 pack_bf16x4(const float x[4], uint64_t base, uint32_t idx0) {
+  uint32_t b[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b[j] = SR ? sr_bf16_bits(x[j], rand16_from_base(base, idx0 + j)) : rne_bf16_bits(x[j]);
+  return u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+}
+
 template <bool W_BF16, bool SR>
 __device__ __forceinline__ void store_w4(const OptArgs& a, int o, int i, const float w[4]) {
   if constexpr (W_BF16) {
@@ -241,20 +264,20 @@ struct GemmDims {
   int64_t ldx, lddy;
 };
 
-hipError_t launch_wgrad_fused(int io_bf16, int state_q8, int opt, int sr, const void* X, const void* dY,
+hipError_t launch_wgrad_fused(int io_bf16, int state_fmt, int opt, int sr, const void* X, const void* dY,
                               const GemmDims& d, const OptArgs& a, hipStream_t stream);
 hipError_t launch_wgrad_store(int io_bf16, const void* X, const void* dY, const GemmDims& d, float* dW,
                               int64_t ld_dw, hipStream_t stream);
-hipError_t launch_optimizer(int w_bf16, int state_q8, int opt, int sr, const float* dW, int64_t ld_dw,
+hipError_t launch_optimizer(int w_bf16, int state_fmt, int opt, int sr, const float* dW, int64_t ld_dw,
                             const OptArgs& a, hipStream_t stream);
 hipError_t launch_dgrad(int io_bf16, const void* dY, int64_t lddy, const void* W, int64_t ldw, void* dX,
                         int64_t lddx, int32_t T, int32_t out, int32_t in, hipStream_t stream);
 // bfloat16 / FP8 kernels (forge_gemm.hip, forge_gemm_kernel.h)
-hipError_t launch_wgrad_fused_bf16(int state_q8, int opt, int sr, const void* X, const void* dY, const GemmDims& d,
+hipError_t launch_wgrad_fused_bf16(int state_fmt, int opt, int sr, const void* X, const void* dY, const GemmDims& d,
                                    const OptArgs& a, hipStream_t stream);
 hipError_t launch_wgrad_store_bf16(const void* X, const void* dY, const GemmDims& d, float* dW, int64_t ld_dw,
                                    hipStream_t stream);
-hipError_t launch_wgrad_fused_f8(int dy_e5m2, int opt, int sr, const void* X, const float* x_scale, const void* dY,
+hipError_t launch_wgrad_fused_f8(int dy_e5m2, int state_fmt, int opt, int sr, const void* X, const float* x_scale, const void* dY,
                                  const float* dy_scale, const GemmDims& d, const OptArgs& a, hipStream_t st);
 hipError_t launch_wgrad_store_f8(int dy_e5m2, const void* X, const float* x_scale, const void* dY,
                                  const float* dy_scale, const GemmDims& d, float* dW, int64_t ld_dw, hipStream_t st);

@@ -253,9 +253,9 @@ static hipError_t launch_f32(const void* X, const void* dY, const GemmDims& d, c
   return hipGetLastError();
 }
 
-hipError_t launch_wgrad_fused(int io_bf16, int state_q8, int opt, int sr, const void* X, const void* dY,
+hipError_t launch_wgrad_fused(int io_bf16, int state_fmt, int opt, int sr, const void* X, const void* dY,
                               const GemmDims& d, const OptArgs& a, hipStream_t stream) {
-  if (io_bf16) return launch_wgrad_fused_bf16(state_q8, opt, sr, X, dY, d, a, stream);
+  if (io_bf16) return launch_wgrad_fused_bf16(state_fmt, opt, sr, X, dY, d, a, stream);
   switch (opt) {
     case FORGE_ADAMW: return launch_f32<EPI_OPT, FORGE_ADAMW>(X, dY, d, a, nullptr, 0, stream);
     case FORGE_SGD: return launch_f32<EPI_OPT, FORGE_SGD>(X, dY, d, a, nullptr, 0, stream);

@@ -260,7 +260,7 @@ def wgrad_unfused(X, dY, W, m, v, opt="adamw", hyper=None, step=1, seed=0, m_sca
 
 
 def new_states(W: torch.Tensor, opt: str = "adamw", fmt: str = "f32"):
-    """Zero moment slots for `opt` in format f32 or q8: returns (m, v, m_scale, v_scale)."""
+    """Zero moment slots for `opt` in format f32, bf16 or q8: returns (m, v, m_scale, v_scale)."""
     use_m, use_v = SLOTS[opt]
     rows, cols = W.shape
     m = v = ms = vs = None
@@ -269,6 +269,11 @@ def new_states(W: torch.Tensor, opt: str = "adamw", fmt: str = "f32"):
             m = torch.zeros((rows, cols), dtype=torch.float32, device=W.device)
         if use_v:
             v = torch.zeros((rows, cols), dtype=torch.float32, device=W.device)
+    elif fmt == "bf16":
+        if use_m:
+            m = torch.zeros((rows, cols), dtype=torch.bfloat16, device=W.device)
+        if use_v:
+            v = torch.zeros((rows, cols), dtype=torch.bfloat16, device=W.device)
     elif fmt == "q8":
         if use_m:
             m = torch.zeros((rows, cols), dtype=torch.int8, device=W.device)

@@ -15,6 +15,10 @@ element-wise update, then the storage formats:
   round-to-nearest-even bfloat16 when stochastic rounding is off;
 * INT8 states: dequantise the stored codes, update in float64, quantise the new
   moments (see `q8`). The weight update uses the unquantised new moments.
+* bfloat16 states: widen the stored values, update in float64, then round like a
+  bfloat16 weight (nearest float32, then stochastic rounding with the moment's own
+  random stream, or nearest-even when stochastic rounding is off). The weight
+  update uses the unrounded new moments.
 
 Row-sampled mode computes the same thing for a subset of output rows only; the
 update is element-wise and INT8 blocks never cross rows, so it is the same
@@ -55,15 +59,25 @@ def load_state(slot: str, arr: Optional[np.ndarray], scale: Optional[np.ndarray]
         return np.asarray(arr, dtype=np.float32).astype(np.float64)
     if state == "q8":
         return q8.dequant_signed(arr, scale) if slot == "m" else q8.dequant_sqrt_unsigned(arr, scale)
+    if state == "bf16":
+        return rounding.bf16_to_f64(arr)
     raise ValueError(state)
 
 
-def store_state(slot: str, val: Optional[np.ndarray], state: str):
-    """float64 moment -> (stored array, scale or None)."""
+def store_state(slot: str, val: Optional[np.ndarray], state: str, *, seed: int = 0, t: int = 1,
+                idx: Optional[np.ndarray] = None, sr: bool = True):
+    """float64 moment -> (stored array, scale or None). bfloat16 states need the
+    element indices `idx`, the seed and step for their random stream."""
     if val is None:
         return None, None
     if state == "f32":
         return rounding.rne_f32(val), None
+    if state == "bf16":
+        x32 = rounding.rne_f32(val)
+        if not sr:
+            return _rne_bf16_from_f32(x32), None
+        stream = rounding.STREAM_M if slot == "m" else rounding.STREAM_V
+        return rounding.sr_bf16(x32, rounding.rand16(seed, t, idx, stream)), None
     if slot == "m":
         return q8.quant_signed(val)
     return q8.quant_sqrt_unsigned(val)
@@ -98,13 +112,14 @@ def wgrad_step(opt: str, X: np.ndarray, dY: np.ndarray, W: np.ndarray,
     m64 = load_state("m", m, m_scale, state) if "m" in slots else None
     v64 = load_state("v", v, v_scale, state) if "v" in slots else None
     theta, m64n, v64n = optim.update(opt, theta0, g, m64, v64, hp, t)
-    m_out, ms = store_state("m", m64n, state)
-    v_out, vs = store_state("v", v64n, state)
+    idx = rounding.element_index(rows, n_in)
+    m_out, ms = store_state("m", m64n, state, seed=seed, t=t, idx=idx, sr=sr)
+    v_out, vs = store_state("v", v64n, state, seed=seed, t=t, idx=idx, sr=sr)
     x32 = rounding.rne_f32(theta)
     if io == "f32":
         w_out = x32
     elif sr:
-        r16 = rounding.rand16(seed, t, rounding.element_index(rows, n_in))
+        r16 = rounding.rand16(seed, t, idx)
         w_out = rounding.sr_bf16(x32, r16)
     else:
         w_out = _rne_bf16_from_f32(x32)

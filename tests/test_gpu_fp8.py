@@ -39,13 +39,13 @@ def dev_scale(s: float) -> torch.Tensor:
 
 
 def run_fp8_case(spec, opt, steps, dy_fmt="e5m2", config=120, layer=0, sr=True, rows=None, hp_over=None,
-                 label=""):
+                 label="", state="f32"):
     f = _forge()
-    print(f"[case] {label} fp8 e4m3 x {dy_fmt} opt={opt} spec={spec} sr={sr} steps={steps}", flush=True)
+    print(f"[case] {label} fp8 e4m3 x {dy_fmt} opt={opt} spec={spec} sr={sr} steps={steps} state={state}", flush=True)
     hp = optim.hyper(opt, **(hp_over or {}))
     seed = (0x5EED0000 + config) ^ layer
     Wd = P.dev_bf16(draw_layer_init(config, layer, spec))
-    m, v, _, _ = f.new_states(Wd, opt, "f32")
+    m, v, _, _ = f.new_states(Wd, opt, state)
     sel = np.arange(spec.out) if rows is None else np.asarray(rows)
     for t in range(1, steps + 1):
         Xq, dYq, sx, sd = draw_layer_batch_fp8(config, layer, t, spec, "e4m3", dy_fmt)
@@ -54,7 +54,7 @@ def run_fp8_case(spec, opt, steps, dy_fmt="e5m2", config=120, layer=0, sr=True, 
                      x_scale=dev_scale(sx), dy_scale=dev_scale(sd))
         torch.cuda.synchronize()
         after = P.snapshot((Wd, m, v, None, None), sel)
-        P.verify_step(opt, Xq, dYq, before, after, hp, t, seed, "bf16", "f32", sr, sel,
+        P.verify_step(opt, Xq, dYq, before, after, hp, t, seed, "bf16", state, sr, sel,
                       fp8=("e4m3", dy_fmt, sx, sd))
     return Wd, m, v
 
@@ -69,6 +69,12 @@ def test_fp8_ragged_all_optimizers(opt):
 @pytest.mark.parametrize("opt", ["adamw", "lion", "sgd"])
 def test_fp8_e4m3_gradients(opt):
     run_fp8_case(LayerSpec("f8", 208, 336, 130), opt, 2, "e4m3", config=122, label="fp8 e4m3/e4m3")
+
+
+@pytest.mark.parametrize("opt", ["adamw", "lion", "rmsprop"])
+def test_fp8_with_bf16_states(opt):
+    run_fp8_case(LayerSpec("f8", 208, 336, 130), opt, 2, "e5m2", config=129, label="fp8 + bf16 states",
+                 state="bf16")
 
 
 def test_fp8_round_to_nearest_and_outliers():

@@ -102,6 +102,17 @@ def test_q8_states(opt):
     run_case(LayerSpec("q", 136, 320, 200, outlier_frac=0.01), opt, 3, config=98, state="q8", label="q8")
 
 
+# ---------------------------------------------------------------- bfloat16 states
+@pytest.mark.parametrize("opt", optim.OPTIMIZERS)
+def test_bf16_states_all_optimizers_sr(opt):
+    run_case(LayerSpec("r", 200, 328, 130), opt, 3, config=99, state="bf16", label="bf16 states")
+
+
+def test_bf16_states_round_to_nearest():
+    run_case(LayerSpec("r", 136, 264, 96), "adamw", 2, config=99, layer=1, state="bf16", sr=False,
+             label="bf16 states rne")
+
+
 # ---------------------------------------------------------------- tile configurations
 def _tile_config_shapes():
     """(rows, cols) of C = (in, out) for wgrad or (in, T) for dgrad that select each
@@ -120,7 +131,7 @@ def _tile_config_shapes():
 
 
 @pytest.mark.parametrize("cfg", ["big", "small", "split"])
-@pytest.mark.parametrize("state", ["f32", "q8"])
+@pytest.mark.parametrize("state", ["f32", "q8", "bf16"])
 def test_each_tile_configuration_fused(cfg, state):
     n_in, n_out = _tile_config_shapes()[cfg]
     rows = np.unique(np.concatenate([np.arange(0, n_out, max(1, n_out // 96)), [n_out - 1]]))
@@ -186,7 +197,7 @@ def test_dgrad_reads_old_weights_before_step():
 
 # ---------------------------------------------------------------- unfused baseline
 @pytest.mark.parametrize("opt,state", [("adamw", "f32"), ("lion", "f32"), ("radam", "f32"), ("adamw", "q8"),
-                                       ("rmsprop", "q8")])
+                                       ("rmsprop", "q8"), ("adamw", "bf16"), ("sgd_momentum", "bf16")])
 def test_unfused_matches_fused(opt, state):
     f = _forge()
     spec = LayerSpec("u", 200, 320, 300)

@@ -118,3 +118,77 @@ def test_q8_state_step_updates_with_unquantised_moments():
     np.testing.assert_array_equal(out["m"], q_m)
     np.testing.assert_array_equal(out["m_scale"], s_m)
     assert out["v"].dtype == np.uint8 and out["v_scale"].shape == (32, 2)
+
+
+# ---------------------------------------------------------------- bfloat16 moment states
+def test_moment_streams_follow_the_sequential_generator():
+    # stream s is SplitMix64 started from seed + s * 2^62: the c-th counter draws the
+    # (c+1)-th output of the sequential generator from that state
+    seed = 0x0123456789ABCDEF
+    for s in (1, 2):
+        seq = rounding.splitmix64_py((seed + (s << 62)) % (1 << 64), 40)
+        got = rounding.rand16(seed, 0, np.arange(40, dtype=np.uint64), stream=s)
+        np.testing.assert_array_equal(got, np.array([z >> 48 for z in seq], dtype=np.uint32))
+
+
+def test_moment_streams_are_uncorrelated_with_the_weight_stream():
+    idx = np.arange(200_000, dtype=np.uint64)
+    r = [rounding.rand16(77, 3, idx, stream=s).astype(np.float64) for s in (0, 1, 2)]
+    for a, b in ((0, 1), (0, 2), (1, 2)):
+        assert abs(np.corrcoef(r[a], r[b])[0, 1]) < 0.01
+        assert np.mean(r[a] == r[b]) < 1e-3
+
+
+def test_bf16_moments_exact_when_representable():
+    # integer-valued X and dY: g is an integer below 2^8, exact in bfloat16, so the
+    # SGD-momentum buffer of step 1 (m = g) is stored exactly whatever the random bits
+    rng = np.random.default_rng(5)
+    X = rng.integers(-2, 3, size=(16, 64)).astype(np.float32)
+    dY = rng.integers(-2, 3, size=(16, 8)).astype(np.float32)
+    Xb, dYb = inputs.bf16_bits_from_f32(X), inputs.bf16_bits_from_f32(dY)
+    W = inputs.bf16_bits_from_f32(np.zeros((8, 64), np.float32))
+    m0 = inputs.bf16_bits_from_f32(np.zeros((8, 64), np.float32))
+    hp = optim.hyper("sgd_momentum", weight_decay=0.0)
+    g = dY.astype(np.float64).T @ X.astype(np.float64)
+    for seed in (1, 2, 3):
+        out = step.wgrad_step("sgd_momentum", Xb, dYb, W, m0, None, hp, 1, seed, state="bf16")
+        np.testing.assert_array_equal(rounding.bf16_to_f64(out["m"]), g)
+
+
+def test_bf16_moments_round_to_a_neighbour_and_are_unbiased():
+    spec = inputs.LayerSpec("t", 8, 64, 32)
+    W = inputs.draw_layer_init(9, 3, spec)
+    X, dY = inputs.draw_layer_batch(9, 3, 1, spec)
+    hp = optim.hyper("adamw")
+    z = inputs.bf16_bits_from_f32(np.zeros(W.shape, np.float32))
+    ref = step.wgrad_step("adamw", X, dY, W, z, z, hp, 1, 0, state="f32")
+    n = 2000
+    acc = {"m": np.zeros(W.shape), "v": np.zeros(W.shape)}
+    for s in range(n):
+        out = step.wgrad_step("adamw", X, dY, W, z, z, hp, 1, s, state="bf16")
+        for k in acc:
+            val = rounding.bf16_to_f64(out[k])
+            x32 = ref[k].astype(np.float64)
+            ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(x32), 1e-38))) - 7)
+            assert np.all(np.abs(val - x32) < ulp)            # one of the two bfloat16 neighbours
+            acc[k] += val
+    for k in acc:
+        x32 = ref[k].astype(np.float64)
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(x32), 1e-38))) - 7)
+        assert np.max(np.abs(acc[k] / n - x32) / ulp) < 4.5 * 0.5 / np.sqrt(n) * 2
+    # the weight update does not see the rounding of the moments
+    np.testing.assert_array_equal(out["x32"], step.wgrad_step("adamw", X, dY, W, z, z, hp, 1, s, state="f32")["x32"])
+
+
+def test_bf16_moments_round_to_nearest_when_sr_is_off():
+    spec = inputs.LayerSpec("t", 8, 64, 32)
+    W = inputs.draw_layer_init(9, 4, spec)
+    X, dY = inputs.draw_layer_batch(9, 4, 1, spec)
+    hp = optim.hyper("adamw")
+    z = inputs.bf16_bits_from_f32(np.zeros(W.shape, np.float32))
+    ref = step.wgrad_step("adamw", X, dY, W, z, z, hp, 1, 0, state="f32", sr=False)
+    out = step.wgrad_step("adamw", X, dY, W, z, z, hp, 1, 0, state="bf16", sr=False)
+    t = __import__("torch")
+    for k in ("m", "v"):
+        want = t.from_numpy(ref[k]).to(t.bfloat16).view(t.int16).numpy().view(np.uint16)
+        np.testing.assert_array_equal(out[k], want)
