@@ -1,6 +1,7 @@
 """Builds libforge.so (the gfx950 HIP kernels + C ABI) in-tree with hipcc.
 
-Usage: python -m optimizer_gemm_amd.build   (or optimizer_gemm_amd.build.build())
+Usage: python optimizer_gemm_amd/build.py   (or __graft_entry__.build()); run by path,
+since importing the package loads the library this script builds.
 The library lands in optimizer_gemm_amd/_lib/libforge.so; object files in
 optimizer_gemm_amd/_build/. Every call recompiles.
 """

@@ -56,7 +56,7 @@ class ForgeError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"libforge.so not built at {LIB_PATH}; run `python -m optimizer_gemm_amd.build`")
+        raise ImportError(f"libforge.so not built at {LIB_PATH}; run `python optimizer_gemm_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     sigs = {
