@@ -48,8 +48,8 @@ hipError_t launch_wgrad_store_bf16(const void* X, const void* dY, const GemmDims
   GArgs g{X, dY, d.ldx, d.lddy,
           d.in, d.out, d.T, dW, ld_dw, extent(d.T, d.ldx, 2), extent(d.T, d.lddy, 2), extent(d.out, ld_dw, 4)};
   OptArgs a{};
-  return g_pick<WgradBig, WgradSmall, WgradSplit>(
-      g, [&](auto c) { return g_launch<decltype(c), G_EPI_STORE, FORGE_SGD, ST_F32, false>(g, a, st); });
+  return g_pick<WgradBig, WgradSmall, WgradSplit, WgradBand>(
+      g, [&](auto c, const GArgs& gc) { return g_launch<decltype(c), G_EPI_STORE, FORGE_SGD, ST_F32, false>(gc, a, st); });
 }
 
 template <int FB>
@@ -86,8 +86,8 @@ hipError_t launch_dgrad_bf16(const void* dY, int64_t lddy, const void* W, int64_
   GArgs g{W, dY, ldw, lddy,
           n_in, T, n_out, dX, lddx, extent(n_out, ldw, 2), extent(T, lddy, 2), extent(T, lddx, 2)};
   OptArgs a{};
-  return g_pick<DgradBig, DgradSmall, DgradSplit>(
-      g, [&](auto c) { return g_launch<decltype(c), G_EPI_DX, FORGE_SGD, ST_F32, false>(g, a, st); });
+  return g_pick<DgradBig, DgradSmall, DgradSplit, DgradBand>(
+      g, [&](auto c, const GArgs& gc) { return g_launch<decltype(c), G_EPI_DX, FORGE_SGD, ST_F32, false>(gc, a, st); });
 }
 
 }  // namespace forge

@@ -53,6 +53,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 enum { G_EPI_STORE = 0, G_EPI_OPT = 1, G_EPI_DX = 2 };
 
+
 // Operand formats of the GEMM core: bfloat16, or OCP FP8 (E4M3 / E5M2 per operand).
 enum { G_BF16 = 0, G_FP8 = 1 };
 
@@ -136,7 +137,15 @@ struct GArgs {
   uint32_t a_bytes, b_bytes, out_bytes;  // extents addressed through buffer resources
   const float* a_scale;  // FP8 operands: dequantisation scale of A and of B (one float each)
   const float* b_scale;
+  // Origin of this launch's tiles in C: the launch covers rows [m_off, M) and columns
+  // [n_off, N); all addressing (and the weight element index of the RNG) stays absolute.
+  int32_t m_off, n_off;
 };
+
+template <class C>
+__host__ __device__ inline int g_ntm(const GArgs& g) { return (g.M - g.m_off + C::BM - 1) / C::BM; }
+template <class C>
+__host__ __device__ inline int g_ntn(const GArgs& g) { return (g.N - g.n_off + C::BN - 1) / C::BN; }
 
 // A byte offset that no buffer resource here covers: loads through it return 0,
 // stores through it are dropped.
@@ -273,7 +282,7 @@ void gemm_kernel(GArgs g, OptArgs a) {
   // the sum of code products
   const float gscale = C::F8 ? g.a_scale[0] * g.b_scale[0] : 1.f;
 
-  const int ntm = (g.M + C::BM - 1) / C::BM, ntn = (g.N + C::BN - 1) / C::BN;
+  const int ntm = g_ntm<C>(g), ntn = g_ntn<C>(g);
   const int ntiles = ntm * ntn;
   const int nst = (g.K + C::BK - 1) / C::BK;
   // Stages are issued in groups of the ring size; stages past the last one, like rows
@@ -336,7 +345,7 @@ void gemm_kernel(GArgs g, OptArgs a) {
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     int tm, tn;
     g_tile(tile, ntm, ntn, tm, tn);
-    const int m0 = tm * C::BM, n0 = tn * C::BN;
+    const int m0 = g.m_off + tm * C::BM, n0 = g.n_off + tn * C::BN;
 
     f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -688,7 +697,9 @@ void gemm_kernel(GArgs g, OptArgs a) {
 // (4 waves of 64x64, two workgroups per compute unit), and when even those are
 // scarce (fewer than two per compute unit) 128x128 tiles with a 2-way in-workgroup
 // split-K (8 waves of 64x64, one workgroup per compute unit), so a compute unit
-// that holds a single tile still runs two waves per SIMD.
+// that holds a single tile still runs two waves per SIMD. A last round of 256x256
+// tiles that would be at most half full is replaced by a second launch of 256x128
+// tiles (8 waves of 128x64, 2-way in-workgroup split-K) over the rest of C.
 // ---------------------------------------------------------------------------
 // Tile configurations (BM, BN, BK, WM, WN, B_TR, OCC[, NSTAGE, KS]); FORGE_*_CFG
 // override them at build time for tuning sweeps.
@@ -700,6 +711,15 @@ void gemm_kernel(GArgs g, OptArgs a) {
 #endif
 #ifndef FORGE_WGRAD_SPLIT_CFG
 #define FORGE_WGRAD_SPLIT_CFG 128, 128, 64, 2, 2, true, 2, 4, 2
+#endif
+// the rest of a problem whose last round of 256x256 tiles would be at most half full:
+// 256x128 tiles (half a large tile each), 8 waves of 128x64 in two k-split groups,
+// a 2-deep ring of 64-token stages
+#ifndef FORGE_WGRAD_BAND_CFG
+#define FORGE_WGRAD_BAND_CFG 256, 128, 64, 2, 2, true, 2, 2, 2
+#endif
+#ifndef FORGE_DGRAD_BAND_CFG
+#define FORGE_DGRAD_BAND_CFG 256, 128, 64, 2, 2, false, 2, 2, 2
 #endif
 #ifndef FORGE_DGRAD_BIG_CFG
 #define FORGE_DGRAD_BIG_CFG 256, 256, 32, 2, 4, false, 2
@@ -726,6 +746,8 @@ using WgradF8Small = GCfg<FORGE_WGRAD_F8_SMALL_CFG, G_FP8, 0, FB>;
 using WgradBig = GCfg<FORGE_WGRAD_BIG_CFG>;
 using WgradSmall = GCfg<FORGE_WGRAD_SMALL_CFG>;
 using WgradSplit = GCfg<FORGE_WGRAD_SPLIT_CFG>;
+using WgradBand = GCfg<FORGE_WGRAD_BAND_CFG>;
+using DgradBand = GCfg<FORGE_DGRAD_BAND_CFG>;
 using DgradBig = GCfg<FORGE_DGRAD_BIG_CFG>;
 using DgradSmall = GCfg<FORGE_DGRAD_SMALL_CFG>;
 using DgradSplit = GCfg<FORGE_DGRAD_SPLIT_CFG>;
@@ -744,7 +766,7 @@ static int g_num_cus() {
 
 template <class C, int EPI, int OPT, int SF, bool SR>
 static hipError_t g_launch(const GArgs& g, const OptArgs& a, hipStream_t st) {
-  const int ntiles = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN);
+  const int ntiles = g_ntm<C>(g) * g_ntn<C>(g);
   if (ntiles == 0) return hipSuccess;
   const int resident = C::OCC * 4 / C::NW * g_num_cus();  // OCC waves on each of 4 SIMDs
   const int grid = ntiles < resident ? ntiles : resident;
@@ -754,15 +776,42 @@ static hipError_t g_launch(const GArgs& g, const OptArgs& a, hipStream_t st) {
 
 template <class C>
 static int g_tiles(const GArgs& g) {
-  return ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN);
+  return g_ntm<C>(g) * g_ntn<C>(g);
 }
 
-// Calls f(C{}) with the tile configuration for this problem size.
-template <class Big, class Small, class Split, class F>
+// Calls f(C{}, g') for each launch of the tile configuration C over the part g' of
+// the problem. Large tiles are used when there are at least as many as compute units.
+// When their last round would leave more than half of the compute units idle, the
+// whole rounds run as large tiles over a band of tile columns (or rows, whichever
+// band holds more of them), and the rest of C runs as a second launch on the same
+// stream: Band tiles (half a large tile) when they fit in one round, else 128x128
+// tiles. Each tile still owns its output elements outright.
+template <class Big, class Small, class Split, class Band, class F>
 static hipError_t g_pick(const GArgs& g, F&& f) {
-  if (g_tiles<Big>(g) >= g_num_cus()) return f(Big{});
-  if (g_tiles<Small>(g) >= 2 * g_num_cus()) return f(Small{});
-  return f(Split{});
+  const int cus = g_num_cus();
+  const int tiles = g_tiles<Big>(g);
+  if (tiles >= cus) {
+    const int full = (tiles / cus) * cus, rem = tiles - full;
+    const int ntm = g_ntm<Big>(g), ntn = g_ntn<Big>(g);
+    const int nb = full / ntm, mb = full / ntn;  // whole tile columns / rows the rounds hold
+    if (rem > 0 && 2 * rem <= cus && (nb > 0 || mb > 0)) {
+      GArgs g1 = g, g2 = g;
+      if (nb * ntm >= mb * ntn) {
+        g1.N = g.n_off + nb * Big::BN;
+        g2.n_off = g1.N;
+      } else {
+        g1.M = g.m_off + mb * Big::BM;
+        g2.m_off = g1.M;
+      }
+      hipError_t e = f(Big{}, g1);
+      if (e != hipSuccess) return e;
+      if (g_tiles<Band>(g2) <= cus) return f(Band{}, g2);
+      return g_tiles<Small>(g2) > cus ? f(Small{}, g2) : f(Split{}, g2);
+    }
+    return f(Big{}, g);
+  }
+  if (g_tiles<Small>(g) >= 2 * cus) return f(Small{}, g);
+  return f(Split{}, g);
 }
 
 static uint32_t extent(int64_t rows, int64_t ld, int64_t es) { return (uint32_t)(rows * ld * es); }
@@ -784,8 +833,8 @@ static hipError_t g_launch_opt(int sf, int sr, const GArgs& g, const OptArgs& a,
 
 template <int OPT>
 hipError_t wgrad_fused_bf16_opt(int sf, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
-  return g_pick<WgradBig, WgradSmall, WgradSplit>(
-      g, [&](auto c) { return g_launch_opt<decltype(c), OPT>(sf, sr, g, a, st); });
+  return g_pick<WgradBig, WgradSmall, WgradSplit, WgradBand>(
+      g, [&](auto c, const GArgs& gc) { return g_launch_opt<decltype(c), OPT>(sf, sr, gc, a, st); });
 }
 
 // FP8 operands, dY in format FB (0 = E4M3, 1 = E5M2): the fused step of one
@@ -800,16 +849,15 @@ static hipError_t g_launch_opt_f8(int sf, int sr, const GArgs& g, const OptArgs&
 // sf: ST_F32 or ST_BF16 (INT8 moments are not offered with FP8 inputs)
 template <int OPT, int FB>
 hipError_t wgrad_fused_f8_opt(int sf, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
-  if (g_tiles<WgradF8Big<FB>>(g) >= g_num_cus()) return g_launch_opt_f8<WgradF8Big<FB>, OPT>(sf, sr, g, a, st);
-  return g_launch_opt_f8<WgradF8Small<FB>, OPT>(sf, sr, g, a, st);
+  return g_pick<WgradF8Big<FB>, WgradF8Small<FB>, WgradF8Small<FB>, WgradF8Small<FB>>(
+      g, [&](auto c, const GArgs& gc) { return g_launch_opt_f8<decltype(c), OPT>(sf, sr, gc, a, st); });
 }
 
 template <int FB>
 hipError_t wgrad_store_f8(const GArgs& g, hipStream_t st) {
   OptArgs a{};
-  if (g_tiles<WgradF8Big<FB>>(g) >= g_num_cus())
-    return g_launch<WgradF8Big<FB>, G_EPI_STORE, FORGE_SGD, ST_F32, false>(g, a, st);
-  return g_launch<WgradF8Small<FB>, G_EPI_STORE, FORGE_SGD, ST_F32, false>(g, a, st);
+  return g_pick<WgradF8Big<FB>, WgradF8Small<FB>, WgradF8Small<FB>, WgradF8Small<FB>>(
+      g, [&](auto c, const GArgs& gc) { return g_launch<decltype(c), G_EPI_STORE, FORGE_SGD, ST_F32, false>(gc, a, st); });
 }
 
 #define FORGE_EXTERN_BF16(OPT) \

@@ -118,31 +118,52 @@ def _tile_config_shapes():
     """(rows, cols) of C = (in, out) for wgrad or (in, T) for dgrad that select each
     tile configuration of the launcher on this device: 256x256 tiles when there are
     at least as many as compute units, else 128x128 tiles when there are at least two
-    per compute unit, else 128x128 tiles with the in-workgroup split-K."""
+    per compute unit, else 128x128 tiles with the in-workgroup split-K.
+    The band_* shapes (256 compute units) leave a last round of 256x256 tiles at most
+    half full, so the launcher runs the whole rounds over a band of tile columns or rows
+    and the rest as a second launch: band_n (column band, ragged 256x128 rest), band_m
+    (row band, ragged 256x128 rest), band_full (a rest of exactly one round of 256x128
+    tiles) and band_small (a rest too large for one round of 256x128 tiles, so 128x128)."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     big = (4096, 256 * -(-cus // 16))
     small = (4096, 128 * -(-cus // 16))
     split = (1024, 520)
-    tiles = lambda mn, t: -(-mn[0] // t) * -(-mn[1] // t)
+    cdiv = lambda a, b: -(-a // b)
+    tiles = lambda mn, t: cdiv(mn[0], t) * cdiv(mn[1], t)
     assert tiles(big, 256) >= cus
     assert tiles(small, 256) < cus and tiles(small, 128) >= 2 * cus
     assert tiles(split, 256) < cus and tiles(split, 128) < 2 * cus
-    return {"big": big, "small": small, "split": split}
+    shapes = {"big": big, "small": small, "split": split}
+    if cus == 256:
+        shapes.update(band_n=(4096, 4416), band_m=(4416, 4096), band_full=(4096, 6144), band_small=(5120, 4864))
+        for k in ("band_n", "band_m", "band_full", "band_small"):
+            assert tiles(shapes[k], 256) > cus and 2 * (tiles(shapes[k], 256) % cus) <= cus
+    return shapes
 
 
-@pytest.mark.parametrize("cfg", ["big", "small", "split"])
+def _shape(cfg):
+    sh = _tile_config_shapes()
+    if cfg not in sh:
+        pytest.skip(f"{cfg}: shapes are laid out for 256 compute units")
+    return sh[cfg]
+
+
+CONFIGS = ["big", "small", "split", "band_n", "band_m", "band_full", "band_small"]
+
+
+@pytest.mark.parametrize("cfg", CONFIGS)
 @pytest.mark.parametrize("state", ["f32", "q8", "bf16"])
 def test_each_tile_configuration_fused(cfg, state):
-    n_in, n_out = _tile_config_shapes()[cfg]
+    n_in, n_out = _shape(cfg)
     rows = np.unique(np.concatenate([np.arange(0, n_out, max(1, n_out // 96)), [n_out - 1]]))
     run_case(LayerSpec("c", n_out, n_in, 72), "adamw", 2, config=88, state=state, rows=rows,
              label=f"tile config {cfg}")
 
 
-@pytest.mark.parametrize("cfg", ["big", "small", "split"])
+@pytest.mark.parametrize("cfg", CONFIGS)
 def test_each_tile_configuration_dgrad(cfg):
     f = _forge()
-    n_in, T = _tile_config_shapes()[cfg]
+    n_in, T = _shape(cfg)
     spec = LayerSpec("d", 136, n_in, T)
     print(f"[case] dgrad tile config {cfg}: T={T} out=136 in={n_in}", flush=True)
     W = draw_layer_init(87, 0, spec)
