@@ -13,8 +13,9 @@ element-wise update, then the storage formats:
 * bfloat16 weights: x32 = round-to-nearest float32 of the float64 result, then
   stochastic rounding with the counter-based r16 (see `rounding`), or
   round-to-nearest-even bfloat16 when stochastic rounding is off;
-* INT8 states: dequantise the stored codes, update in float64, quantise the new
-  moments (see `q8`). The weight update uses the unquantised new moments.
+* INT8 states (linear codes, or the dynamic 8-bit code): dequantise the stored
+  codes, update in float64, quantise the new moments (see `q8`). The weight
+  update uses the unquantised new moments.
 * bfloat16 states: widen the stored values, update in float64, then round like a
   bfloat16 weight (nearest float32, then stochastic rounding with the moment's own
   random stream, or nearest-even when stochastic rounding is off). The weight
@@ -61,6 +62,8 @@ def load_state(slot: str, arr: Optional[np.ndarray], scale: Optional[np.ndarray]
         return q8.dequant_signed(arr, scale) if slot == "m" else q8.dequant_sqrt_unsigned(arr, scale)
     if state == "bf16":
         return rounding.bf16_to_f64(arr)
+    if state == "q8dyn":
+        return q8.dequant_dyn_signed(arr, scale) if slot == "m" else q8.dequant_dyn_unsigned(arr, scale)
     raise ValueError(state)
 
 
@@ -78,6 +81,10 @@ def store_state(slot: str, val: Optional[np.ndarray], state: str, *, seed: int =
             return _rne_bf16_from_f32(x32), None
         stream = rounding.STREAM_M if slot == "m" else rounding.STREAM_V
         return rounding.sr_bf16(x32, rounding.rand16(seed, t, idx, stream)), None
+    if state == "q8dyn":
+        return q8.quant_dyn_signed(val) if slot == "m" else q8.quant_dyn_unsigned(val)
+    if state != "q8":
+        raise ValueError(state)
     if slot == "m":
         return q8.quant_signed(val)
     return q8.quant_sqrt_unsigned(val)
