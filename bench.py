@@ -21,6 +21,7 @@ Besides the JSON line's contract fields it reports:
 from __future__ import annotations
 
 import argparse
+import functools
 import hashlib
 import json
 import os
@@ -57,7 +58,7 @@ def parse():
     p.add_argument("--cold-calls", type=int, default=10,
                    help="fused calls of the first layer timed after a 1 GiB write that evicts the memory-side cache")
     p.add_argument("--opt", default="adamw")
-    p.add_argument("--states", default=None, choices=("f32", "bf16", "q8"),
+    p.add_argument("--states", default=None, choices=("f32", "bf16", "q8", "q8dyn"),
                    help="moment storage format (default: the workload's)")
     p.add_argument("--inputs", default="native", choices=("native", "fp8"),
                    help="fp8: the fused step reads X as E4M3 and dY as E5M2 codes with per-tensor scales "
@@ -160,11 +161,16 @@ def main() -> int:
     if args.states:
         state = args.states
     opt = args.opt
+    # int8 moments: linear codes ("q8") or the dynamic 8-bit code ("q8dyn")
+    code = "dynamic" if state == "q8dyn" else "linear"
+    wstep = functools.partial(forge.wgrad_step, code=code)
+    wunfused = functools.partial(forge.wgrad_unfused, code=code)
+    optstep = functools.partial(forge.optimizer_step, code=code)
     dev = torch.device("cuda:0")
     io = layers[0].io
     tdt = torch.bfloat16 if io == "bf16" else torch.float32
     fp8 = args.inputs == "fp8"
-    if fp8 and (io != "bf16" or state == "q8"):
+    if fp8 and (io != "bf16" or state in ("q8", "q8dyn")):
         print("FP8 inputs need bf16 weights and float32 or bfloat16 moments", file=sys.stderr)
         return 2
 
@@ -220,7 +226,7 @@ def main() -> int:
             forge.dgrad(dY, W, dX)
             if fused_events is not None:
                 fused_events[k][0].record()
-            forge.wgrad_step(X, dYf, W, m, v, opt, hyper, t, seed, ms, vs, x_scale=xs, dy_scale=ds)
+            wstep(X, dYf, W, m, v, opt, hyper, t, seed, ms, vs, x_scale=xs, dy_scale=ds)
             if fused_events is not None:
                 fused_events[k][1].record()
 
@@ -273,7 +279,7 @@ def main() -> int:
             flush.fill_(float(r))
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            forge.wgrad_step(X0, dY0, W0d, m0, v0, opt, hyper, 30_000 + r, seed0, ms0, vs0, x_scale=xs0,
+            wstep(X0, dY0, W0d, m0, v0, opt, hyper, 30_000 + r, seed0, ms0, vs0, x_scale=xs0,
                              dy_scale=ds0)
             e1.record()
             torch.cuda.synchronize()
@@ -300,12 +306,12 @@ def main() -> int:
         torch.cuda.synchronize()
         base = torch.cuda.memory_allocated()
         torch.cuda.reset_peak_memory_stats()
-        forge.wgrad_step(X, dY, W, m, v, opt, hyper, 10_000, seed, ms, vs, **sc)
+        wstep(X, dY, W, m, v, opt, hyper, 10_000, seed, ms, vs, **sc)
         torch.cuda.synchronize()
         fused_transient = torch.cuda.max_memory_allocated() - base
         torch.cuda.reset_peak_memory_stats()
         dW = torch.empty((spec.out, spec.inn), dtype=torch.float32, device=dev)
-        forge.wgrad_unfused(X, dY, W, m, v, opt, hyper, 10_001, seed, ms, vs, dW_workspace=dW, **sc)
+        wunfused(X, dY, W, m, v, opt, hyper, 10_001, seed, ms, vs, dW_workspace=dW, **sc)
         torch.cuda.synchronize()
         unfused_transient = torch.cuda.max_memory_allocated() - base
         e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
@@ -313,12 +319,12 @@ def main() -> int:
         f_e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_rep)]
         for r in range(n_rep):
             f_e[r][0].record()
-            forge.wgrad_step(X, dY, W, m, v, opt, hyper, 10_002 + r, seed, ms, vs, **sc)
+            wstep(X, dY, W, m, v, opt, hyper, 10_002 + r, seed, ms, vs, **sc)
             f_e[r][1].record()
             e[r][0].record()
             forge.wgrad(X, dY, dW, **sc)
             e[r][1].record()
-            forge.optimizer_step(dW, W, m, v, opt, hyper, 10_002 + r, seed, ms, vs)
+            optstep(dW, W, m, v, opt, hyper, 10_002 + r, seed, ms, vs)
             e[r][2].record()
         torch.cuda.synchronize()
         gemm_ms = float(np.median([a.elapsed_time(b) for a, b, _ in e]))
@@ -346,7 +352,7 @@ def main() -> int:
             forge.dgrad(dY, W, dX)
             dWs.append(forge.wgrad(X, dYf, x_scale=xs, dy_scale=ds))
         for (spec, W, m, v, ms, vs, seed), dW in zip(per_layer, dWs):
-            forge.optimizer_step(dW, W, m, v, opt, hyper, 20_000, seed, ms, vs)
+            optstep(dW, W, m, v, opt, hyper, 20_000, seed, ms, vs)
         e1.record()
         torch.cuda.synchronize()
         floor = torch.cuda.max_memory_allocated() - base

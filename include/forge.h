@@ -45,7 +45,9 @@ typedef enum {
   FORGE_I8 = 2,   /* int8 codes of a signed moment (block-64 absmax, scale/127) */
   FORGE_U8 = 3,   /* uint8 codes of sqrt(second moment) (block-64 absmax, scale/255) */
   FORGE_E4M3 = 4, /* OCP FP8 E4M3 input codes (value = decode(code) * scale[0]) */
-  FORGE_E5M2 = 5  /* OCP FP8 E5M2 input codes (value = decode(code) * scale[0]) */
+  FORGE_E5M2 = 5, /* OCP FP8 E5M2 input codes (value = decode(code) * scale[0]) */
+  FORGE_I8_DYN = 6, /* signed dynamic 8-bit codes of m (block-64 absmax; see forge_dyn_value) */
+  FORGE_U8_DYN = 7  /* unsigned dynamic 8-bit codes of v (block-64 max; see forge_dyn_value) */
 } forge_dtype;
 
 /* The eight element-wise optimizers the pages list (§3 Contributions, generality). */
@@ -63,7 +65,10 @@ typedef enum {
 /* A 2-D row-major device tensor. `scale` is used only for
  *   - FORGE_I8 / FORGE_U8 moments: float32 block scales, [rows, cols/64] with row
  *     pitch cols/64, one per 64 consecutive elements of a row (§2 "Precision and
- *     fidelity": INT8 states with blocks of 64);
+ *     fidelity": INT8 states with blocks of 64); the scale is absmax/127 (m) or
+ *     max sqrt(v)/255 (v);
+ *   - FORGE_I8_DYN / FORGE_U8_DYN moments: the same layout, the scale being the
+ *     block's absmax of m (or max of v);
  *   - FORGE_E4M3 / FORGE_E5M2 inputs: one float32 in device memory, the tensor's
  *     dequantisation scale (element value = decoded code * scale[0]). */
 typedef struct {
@@ -118,13 +123,33 @@ typedef struct {
 #define FORGE_ERR_ALIAS (-8)       /* output tensors overlap each other or an input */
 
 /*
+ * Dynamic 8-bit moment code (FORGE_I8_DYN / FORGE_U8_DYN; §2 "Precision and
+ * fidelity" compares the INT8 states' block of 64 with the 2048 of the standard
+ * 8-bit optimizers, whose states use a dynamic-exponent code). The n magnitude bits
+ * of a code (n = 7 signed, 8 unsigned) hold, from the top, E zeros, an indicator 1
+ * and F = n - 1 - E fraction bits f; the magnitude is 10^-E (0.1 + 0.9 (f+1)/2^F),
+ * computed as the double quotient (2^F + 9 (f+1)) / (2^F 10^(E+1)) rounded to float;
+ * magnitude index 0 is 0. A signed code is sign << 7 | magnitude index. Stored
+ * moment = code value * block scale; a new code is the nearest magnitude to
+ * |x| / scale in float32 (ties to the larger; x = 0 or a zero block -> code 0).
+ * Host-only helpers, no device work:
+ *   forge_dyn_value:  float value of a code (is_signed: 1 for m codes, 0 for v codes;
+ *                     code 0..255; NaN for other codes).
+ *   forge_dyn_encode: the code the kernels store for the normalised value y.
+ */
+float forge_dyn_value(int32_t is_signed, int32_t code);
+int32_t forge_dyn_encode(int32_t is_signed, float y);
+
+/*
  * Fused weight-gradient + optimizer step (§2 Method, "Core mechanism"):
  *   dW = dY^T X (FP32 accumulation over T tokens, tile by tile, never stored),
  *   then the `opt` update of W, m, v in place, with step t = `step` (1-based).
  * X [T, in] and dY [T, out] are read only; W [out, in] is updated in place.
  * dtypes: X, dY, W all FORGE_F32, or all FORGE_BF16. m and v: FORGE_F32, or
- * FORGE_I8 (m) and FORGE_U8 (v) with block scales (requires in % 64 == 0), or
- * FORGE_BF16 (with bf16 W; ld a multiple of 8; step < 2^30).
+ * FORGE_I8 (m) and FORGE_U8 (v) with block scales, or FORGE_I8_DYN (m) and
+ * FORGE_U8_DYN (v) with block scales (both INT8 forms: bf16 W, in % 64 == 0, ld a
+ * multiple of 16), or FORGE_BF16 (with bf16 W; ld a multiple of 8; step < 2^30);
+ * m and v must share one format.
  * Slots an optimizer does not use may be NULL and are never touched:
  *   SGD: none; SGD-momentum, Lion: m; RMSprop, AdaGrad: v; others: m and v.
  * bfloat16 W is written with stochastic rounding (hyper->stochastic_round)

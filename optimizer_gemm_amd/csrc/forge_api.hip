@@ -96,7 +96,7 @@ int check_hyper(int opt, const forge_hyper* h, int64_t step) {
   return FORGE_OK;
 }
 
-// Moment slots: returns the state format (ST_F32 / ST_Q8 / ST_BF16) or a negative status.
+// Moment slots: returns the state format (ST_F32 / ST_Q8 / ST_Q8D / ST_BF16) or a negative status.
 int check_states(int opt, int io_dtype, const forge_tensor* W, const forge_tensor* m, const forge_tensor* v) {
   const int sl = opt_slots(opt);
   const forge_tensor* slot[2] = {m, v};
@@ -116,8 +116,9 @@ int check_states(int opt, int io_dtype, const forge_tensor* W, const forge_tenso
       f = ST_BF16;
       if (io_dtype != FORGE_BF16) return FORGE_ERR_DTYPE;
       if (!aligned16(t->data) || t->ld % 8) return FORGE_ERR_ALIGN;
-    } else if ((k == 0 && t->dtype == FORGE_I8) || (k == 1 && t->dtype == FORGE_U8)) {
-      f = ST_Q8;
+    } else if ((k == 0 && (t->dtype == FORGE_I8 || t->dtype == FORGE_I8_DYN)) ||
+               (k == 1 && (t->dtype == FORGE_U8 || t->dtype == FORGE_U8_DYN))) {
+      f = (t->dtype == FORGE_I8 || t->dtype == FORGE_U8) ? ST_Q8 : ST_Q8D;
       if (io_dtype != FORGE_BF16) return FORGE_ERR_DTYPE;
       if (!t->scale) return FORGE_ERR_NULL;
       if (!aligned16(t->data) || t->ld % 16 || ((uintptr_t)t->scale & 3u)) return FORGE_ERR_ALIGN;
@@ -293,6 +294,19 @@ uint32_t forge_rand16(uint64_t seed, int64_t step, uint32_t idx) {
 
 uint16_t forge_sr_bf16(float x, uint32_t r16) { return (uint16_t)sr_bf16_bits(x, r16 & 0xFFFFu); }
 
+// Host copy of the dynamic-code tables (the same constexpr construction as the
+// kernels' constant-memory copy).
+static constexpr DynTables kDynHost = make_dyn_tables();
+
+float forge_dyn_value(int32_t is_signed, int32_t code) {
+  if (code < 0 || code > 255) return __builtin_nanf("");
+  return is_signed ? dyn_decode_s((uint32_t)code, kDynHost.vs) : kDynHost.vu[code];
+}
+
+int32_t forge_dyn_encode(int32_t is_signed, float y) {
+  return (int32_t)(is_signed ? dyn_encode_s(y, kDynHost.ms) : dyn_encode_u(y, kDynHost.mu));
+}
+
 int forge_linear_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge_tensor* W, forge_tensor* m,
                             forge_tensor* v, int32_t opt, const forge_hyper* hyper, int64_t step, uint64_t seed,
                             forge_stream_t stream) {
@@ -312,7 +326,7 @@ int forge_linear_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge
   const int fmt = check_states(opt, io, W, m, v);
   if (fmt < 0) return fmt;
   if (fmt == ST_BF16 && step >= ((int64_t)1 << 30)) return FORGE_ERR_HYPER;
-  if (f8 && fmt == ST_Q8) return FORGE_ERR_UNSUPPORTED;
+  if (f8 && (fmt == ST_Q8 || fmt == ST_Q8D)) return FORGE_ERR_UNSUPPORTED;
   if (W->rows * W->cols >= ((int64_t)1 << 32)) return FORGE_ERR_UNSUPPORTED;
   const int sl = opt_slots(opt);
   if (!fits_31(X) || !fits_31(dY) || !fits_31(W) || ((sl & 1) && !fits_31(m)) || ((sl & 2) && !fits_31(v)))

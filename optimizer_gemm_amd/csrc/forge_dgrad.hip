@@ -162,7 +162,7 @@ hipError_t launch_dgrad(int io_bf16, const void* dY, int64_t lddy, const void* W
 // ---------------------------------------------------------------------------
 template <bool W_BF16, int OPT, int SF, bool SR>
 __global__ __launch_bounds__(256) void optimizer_kernel(const float* __restrict__ dW, int64_t ld_dw, OptArgs a) {
-  constexpr bool Q8 = SF == ST_Q8, B16S = SF == ST_BF16;
+  constexpr bool Q8D = SF == ST_Q8D, Q8 = SF == ST_Q8 || Q8D, B16S = SF == ST_BF16;
   constexpr int SL = opt_slots(OPT);
   constexpr bool HAS_M = SL & 1, HAS_V = SL & 2;
   const int64_t vec_per_row = a.in >> 2;
@@ -175,7 +175,21 @@ __global__ __launch_bounds__(256) void optimizer_kernel(const float* __restrict_
   if (valid) {
     load_f4(dW, ld_dw, o, i, g);
     load_w4<W_BF16>(a, o, i, w);
-    if constexpr (Q8) {
+    if constexpr (Q8D) {
+      const int64_t si = (int64_t)o * (a.in >> 6) + (i >> 6);
+      if constexpr (HAS_M) {
+        const uint32_t q = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.m) + (int64_t)o * a.ldm + i);
+        const float sc = a.m_scale[si];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m[j] = dyn_decode_s((q >> (8 * j)) & 0xFFu, g_dyn.vs) * sc;
+      }
+      if constexpr (HAS_V) {
+        const uint32_t q = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.v) + (int64_t)o * a.ldv + i);
+        const float sc = a.v_scale[si];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = g_dyn.vu[(q >> (8 * j)) & 0xFFu] * sc;
+      }
+    } else if constexpr (Q8) {
       if constexpr (HAS_M) dequant_m4(a, o, i, m);
       if constexpr (HAS_V) dequant_v4(a, o, i, v);
     } else if constexpr (B16S) {
@@ -190,10 +204,11 @@ __global__ __launch_bounds__(256) void optimizer_kernel(const float* __restrict_
     store_w4<W_BF16, SR>(a, o, i, w);
   }
   if constexpr (Q8) {
+    // linear codes: absmax of m and sqrt(v); dynamic codes: of m and v
     float r[4], mmax = 0.f, vmax = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      r[j] = sqrtf(v[j]);
+      r[j] = Q8D ? v[j] : sqrtf(v[j]);
       mmax = fmaxf(mmax, fabsf(m[j]));
       vmax = fmaxf(vmax, r[j]);
     }
@@ -202,12 +217,14 @@ __global__ __launch_bounds__(256) void optimizer_kernel(const float* __restrict_
       mmax = fmaxf(mmax, __shfl_xor(mmax, sh));
       vmax = fmaxf(vmax, __shfl_xor(vmax, sh));
     }
-    const float sm = mmax / 127.f, sv = vmax / 255.f;
+    const float sm = Q8D ? mmax : mmax / 127.f, sv = Q8D ? vmax : vmax / 255.f;
     if (valid) {
       if constexpr (HAS_M)
-        *reinterpret_cast<uint32_t*>(reinterpret_cast<int8_t*>(a.m) + (int64_t)o * a.ldm + i) = quant_m4(m, sm);
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<int8_t*>(a.m) + (int64_t)o * a.ldm + i) =
+            Q8D ? quant_dyn_m4(m, sm, g_dyn.ms) : quant_m4(m, sm);
       if constexpr (HAS_V)
-        *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.v) + (int64_t)o * a.ldv + i) = quant_v4(r, sv);
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.v) + (int64_t)o * a.ldv + i) =
+            Q8D ? quant_dyn_v4(r, sv, g_dyn.mu) : quant_v4(r, sv);
       if ((i & 63) == 0) {
         const int64_t si = (int64_t)o * (a.in >> 6) + (i >> 6);
         if constexpr (HAS_M) a.m_scale[si] = sm;
@@ -248,6 +265,8 @@ static hipError_t launch_opt_t(int w_bf16, int sf, int sr, const float* dW, int6
     hipLaunchKernelGGL((optimizer_kernel<false, OPT, ST_F32, false>), grid, dim3(256), 0, st, dW, ld_dw, a);
   else if (sf == ST_Q8)
     launch_opt_sf<OPT, ST_Q8>(sr, grid, dW, ld_dw, a, st);
+  else if (sf == ST_Q8D)
+    launch_opt_sf<OPT, ST_Q8D>(sr, grid, dW, ld_dw, a, st);
   else if (sf == ST_BF16)
     launch_opt_sf<OPT, ST_BF16>(sr, grid, dW, ld_dw, a, st);
   else

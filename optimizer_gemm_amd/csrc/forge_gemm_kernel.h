@@ -250,7 +250,7 @@ struct EpiRes {
 template <int OPT, int SF>
 __device__ __forceinline__ EpiRes epi_res(const OptArgs& a) {
   EpiRes r;
-  constexpr bool Q8 = SF == ST_Q8;
+  constexpr bool Q8 = SF == ST_Q8 || SF == ST_Q8D;
   const uint32_t n = (uint32_t)a.out;
   r.W = make_rsrc(a.W, n * (uint32_t)a.ldw * 2u);
   constexpr int SL = opt_slots(OPT);
@@ -267,8 +267,18 @@ __device__ __forceinline__ EpiRes epi_res(const OptArgs& a) {
 template <class C, int EPI, int OPT, int SF, bool SR>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
 void gemm_kernel(GArgs g, OptArgs a) {
-  constexpr bool Q8 = SF == ST_Q8, B16S = SF == ST_BF16;
+  // Q8: INT8 codes with block scales, linear (ST_Q8) or the dynamic code (ST_Q8D)
+  constexpr bool Q8D = SF == ST_Q8D, Q8 = SF == ST_Q8 || Q8D, B16S = SF == ST_BF16;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::SMEM_BYTES];
+  // dynamic-code tables, copied to LDS once (the first tile's barrier publishes them)
+  const DynTables* dyn = nullptr;
+  if constexpr (Q8D) {
+    __shared__ DynTables dyn_lds;
+    float* dst = reinterpret_cast<float*>(&dyn_lds);
+    const float* src = reinterpret_cast<const float*>(&g_dyn);
+    for (int j = threadIdx.x; j < (int)(sizeof(DynTables) / 4); j += C::NT) dst[j] = src[j];
+    dyn = &dyn_lds;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int ks = wave / (C::WM * C::WN), wsp = wave % (C::WM * C::WN);
@@ -628,15 +638,26 @@ void gemm_kernel(GArgs g, OptArgs a) {
             if constexpr (HAS_M) { m[0] = mv[k].x; m[1] = mv[k].y; m[2] = mv[k].z; m[3] = mv[k].w; }
             if constexpr (HAS_V) { v[0] = vv[k].x; v[1] = vv[k].y; v[2] = vv[k].z; v[3] = vv[k].w; }
           } else {
-            if constexpr (HAS_M) {
+            if constexpr (Q8D) {
+              if constexpr (HAS_M) {
 #pragma unroll
-              for (int j = 0; j < 4; ++j) m[j] = (float)(int8_t)((qm[k] >> (8 * j)) & 0xFF) * msc[k];
-            }
-            if constexpr (HAS_V) {
+                for (int j = 0; j < 4; ++j) m[j] = dyn_decode_s((qm[k] >> (8 * j)) & 0xFFu, dyn->vs) * msc[k];
+              }
+              if constexpr (HAS_V) {
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const float r = (float)((qv[k] >> (8 * j)) & 0xFF) * vsc[k];
-                v[j] = r * r;
+                for (int j = 0; j < 4; ++j) v[j] = dyn->vu[(qv[k] >> (8 * j)) & 0xFFu] * vsc[k];
+              }
+            } else {
+              if constexpr (HAS_M) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) m[j] = (float)(int8_t)((qm[k] >> (8 * j)) & 0xFF) * msc[k];
+              }
+              if constexpr (HAS_V) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  const float r = (float)((qv[k] >> (8 * j)) & 0xFF) * vsc[k];
+                  v[j] = r * r;
+                }
               }
             }
           }
@@ -662,10 +683,11 @@ void gemm_kernel(GArgs g, OptArgs a) {
               __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{v[0], v[1], v[2], v[3]}), R.v, ov_[k], 0, 0);
           } else {
             // block-64 absmax over the 16 adjacent lanes holding this row's block
+            // (linear codes: of m and sqrt(v); dynamic codes: of m and v)
             float r[4], mmax = 0.f, vmax = 0.f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              r[j] = sqrtf(v[j]);
+              r[j] = Q8D ? v[j] : sqrtf(v[j]);
               mmax = fmaxf(mmax, fabsf(m[j]));
               vmax = fmaxf(vmax, r[j]);
             }
@@ -674,9 +696,14 @@ void gemm_kernel(GArgs g, OptArgs a) {
               mmax = fmaxf(mmax, __shfl_xor(mmax, sh));
               vmax = fmaxf(vmax, __shfl_xor(vmax, sh));
             }
-            const float sm = mmax / 127.f, sv = vmax / 255.f;
-            if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(quant_m4(m, sm), R.m, om[k], 0, 0);
-            if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(quant_v4(r, sv), R.v, ov_[k], 0, 0);
+            const float sm = Q8D ? mmax : mmax / 127.f, sv = Q8D ? vmax : vmax / 255.f;
+            if constexpr (Q8D) {
+              if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(quant_dyn_m4(m, sm, dyn->ms), R.m, om[k], 0, 0);
+              if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(quant_dyn_v4(r, sv, dyn->mu), R.v, ov_[k], 0, 0);
+            } else {
+              if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(quant_m4(m, sm), R.m, om[k], 0, 0);
+              if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(quant_v4(r, sv), R.v, ov_[k], 0, 0);
+            }
             if ((col & 63) == 0) {
               if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sm), R.ms, osc[k], 0, 0);
               if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sv), R.vs, osc[k], 0, 0);
@@ -823,6 +850,8 @@ static hipError_t g_launch_opt(int sf, int sr, const GArgs& g, const OptArgs& a,
   switch (sf) {
     case ST_Q8:
       return sr ? g_launch<C, G_EPI_OPT, OPT, ST_Q8, true>(g, a, st) : g_launch<C, G_EPI_OPT, OPT, ST_Q8, false>(g, a, st);
+    case ST_Q8D:
+      return sr ? g_launch<C, G_EPI_OPT, OPT, ST_Q8D, true>(g, a, st) : g_launch<C, G_EPI_OPT, OPT, ST_Q8D, false>(g, a, st);
     case ST_BF16:
       return sr ? g_launch<C, G_EPI_OPT, OPT, ST_BF16, true>(g, a, st)
                 : g_launch<C, G_EPI_OPT, OPT, ST_BF16, false>(g, a, st);

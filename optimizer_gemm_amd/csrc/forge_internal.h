@@ -22,7 +22,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // State formats of the moment slots.
-enum StateFmt { ST_F32 = 0, ST_Q8 = 1, ST_BF16 = 2 };
+enum StateFmt { ST_F32 = 0, ST_Q8 = 1, ST_BF16 = 2, ST_Q8D = 3 };
 // Which slots an optimizer keeps (bit 0: m, bit 1: v).
 __host__ __device__ constexpr int opt_slots(int opt) {
   return opt == FORGE_ADAMW ? 3 : opt == FORGE_SGD ? 0 : opt == FORGE_SGD_MOMENTUM ? 1
@@ -142,8 +142,8 @@ struct OptArgs {
   void* W;            // [out, ldw] bf16 or f32
   void* m;            // [out, ldm] f32, bf16 or int8
   void* v;            // [out, ldv] f32, bf16 or uint8
-  float* m_scale;     // [out, in/64]  (Q8 only)
-  float* v_scale;     // [out, in/64]  (Q8 only)
+  float* m_scale;     // [out, in/64]  (INT8 codes only)
+  float* v_scale;     // [out, in/64]  (INT8 codes only)
   int64_t ldw, ldm, ldv;
   int32_t out, in;
   uint64_t rng_base;  // rng_base(seed, step)
@@ -255,6 +255,78 @@ __device__ __forceinline__ uint32_t quant_v4(const float r[4], float s) {  // r 
     c = fminf(fmaxf(c, 0.f), 255.f);
     q |= ((uint32_t)c & 0xFFu) << (8 * j);
   }
+  return q;
+}
+
+// ---------------------------------------------------------------------------
+// Dynamic 8-bit moment code on blocks of 64 (normalised by the block absmax):
+// the code family of the standard 8-bit optimizers (dynamic tree quantization,
+// Dettmers et al., "8-bit Optimizers via Block-wise Quantization"), with values
+// of this library's own construction. A code's n magnitude bits hold, from the
+// top, E zeros (the decade), an indicator 1, then F = n - 1 - E fraction bits f;
+// its magnitude is 10^-E (0.1 + 0.9 (f + 1) / 2^F), i.e. the exact rational
+// (2^F + 9 (f + 1)) / (2^F 10^(E+1)), taken as float of its double quotient;
+// the all-zero magnitude is 0, the all-ones one exactly 1. Signed codes (m):
+// sign << 7 | 7-bit magnitude index; unsigned codes (v): 8-bit index. Encoding
+// takes the nearest magnitude: the index is the number of float midpoints of
+// neighbouring magnitudes that are <= |y|, ties going to the larger.
+// ---------------------------------------------------------------------------
+struct DynTables {
+  float vs[128];  // signed-code magnitudes
+  float ms[128];  // their 127 midpoints, then +inf
+  float vu[256];  // unsigned-code magnitudes
+  float mu[256];  // their 255 midpoints, then +inf
+};
+constexpr float dyn_magnitude(int k, int nbits) {
+  if (k == 0) return 0.f;
+  int F = 0;
+  while ((k >> (F + 1)) != 0) ++F;
+  const int E = nbits - 1 - F, f = k - (1 << F);
+  double den = (double)(1 << F);
+  for (int j = 0; j <= E; ++j) den *= 10.0;
+  return (float)((double)((1 << F) + 9 * (f + 1)) / den);
+}
+constexpr DynTables make_dyn_tables() {
+  DynTables t{};
+  for (int k = 0; k < 128; ++k) t.vs[k] = dyn_magnitude(k, 7);
+  for (int k = 0; k < 256; ++k) t.vu[k] = dyn_magnitude(k, 8);
+  for (int k = 0; k < 127; ++k) t.ms[k] = (float)(((double)t.vs[k] + (double)t.vs[k + 1]) * 0.5);
+  for (int k = 0; k < 255; ++k) t.mu[k] = (float)(((double)t.vu[k] + (double)t.vu[k + 1]) * 0.5);
+  t.ms[127] = __builtin_huge_valf();
+  t.mu[255] = __builtin_huge_valf();
+  return t;
+}
+// Device copy (one per translation unit that uses it; read-only).
+static __constant__ DynTables g_dyn = make_dyn_tables();
+
+// Number of the N sorted midpoints mid[0..N-1] (padded with +inf) that are <= a.
+template <int N>
+__host__ __device__ __forceinline__ uint32_t dyn_search(const float* mid, float a) {
+  uint32_t k = 0;
+#pragma unroll
+  for (int step = N / 2; step >= 1; step >>= 1) k += (mid[k + step - 1] <= a) ? (uint32_t)step : 0u;
+  return k;
+}
+__host__ __device__ __forceinline__ uint32_t dyn_encode_s(float y, const float* mid) {
+  const uint32_t k = dyn_search<128>(mid, fabsf(y));
+  return (y < 0.f && k != 0u) ? (k | 0x80u) : k;
+}
+__host__ __device__ __forceinline__ uint32_t dyn_encode_u(float y, const float* mid) { return dyn_search<256>(mid, y); }
+__host__ __device__ __forceinline__ float dyn_decode_s(uint32_t b, const float* vs) {
+  const float x = vs[b & 0x7Fu];
+  return (b & 0x80u) ? -x : x;
+}
+// 4 values with block absmax s (already reduced over the block) -> 4 codes.
+__host__ __device__ __forceinline__ uint32_t quant_dyn_m4(const float x[4], float s, const float* mid) {
+  uint32_t q = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) q |= dyn_encode_s(s > 0.f ? x[j] / s : 0.f, mid) << (8 * j);
+  return q;
+}
+__host__ __device__ __forceinline__ uint32_t quant_dyn_v4(const float x[4], float s, const float* mid) {
+  uint32_t q = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) q |= dyn_encode_u(s > 0.f ? x[j] / s : 0.f, mid) << (8 * j);
   return q;
 }
 

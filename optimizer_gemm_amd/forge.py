@@ -16,7 +16,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("FORGE_LIB", os.path.join(_PKG, "_lib", "libforge.so"))
 
-F32, BF16, I8, U8, E4M3, E5M2 = 0, 1, 2, 3, 4, 5
+F32, BF16, I8, U8, E4M3, E5M2, I8_DYN, U8_DYN = 0, 1, 2, 3, 4, 5, 6, 7
 OPTIMIZERS = ("adamw", "sgd", "sgd_momentum", "lion", "rmsprop", "adagrad", "nadam", "radam")
 OPT_ID = {name: k for k, name in enumerate(OPTIMIZERS)}
 # slot usage per optimizer: (uses m, uses v)
@@ -73,6 +73,8 @@ def _load() -> ctypes.CDLL:
         "forge_rand16": ([ctypes.c_uint64, ctypes.c_int64, ctypes.c_uint32], ctypes.c_uint32),
         "forge_sr_bf16": ([ctypes.c_float, ctypes.c_uint32], ctypes.c_uint16),
         "forge_status_str": ([ctypes.c_int], ctypes.c_char_p),
+        "forge_dyn_value": ([ctypes.c_int32, ctypes.c_int32], ctypes.c_float),
+        "forge_dyn_encode": ([ctypes.c_int32, ctypes.c_float], ctypes.c_int32),
         "forge_version": ([], ctypes.c_int),
     }
     for name, (argt, rest) in sigs.items():
@@ -105,10 +107,14 @@ _DT = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8, torch.uint8: U8
 _FP8 = (torch.float8_e4m3fn, torch.float8_e5m2)
 
 
-def describe(t: Optional[torch.Tensor], scale: Optional[torch.Tensor] = None, *, device: bool = True):
-    """forge_tensor for a 2-D row-major tensor (None -> None)."""
+def describe(t: Optional[torch.Tensor], scale: Optional[torch.Tensor] = None, *, device: bool = True,
+             code: str = "linear"):
+    """forge_tensor for a 2-D row-major tensor (None -> None). int8 / uint8 moments
+    hold linear codes (code="linear") or the dynamic 8-bit code (code="dynamic")."""
     if t is None:
         return None
+    if code not in ("linear", "dynamic"):
+        raise ValueError(f"unknown moment code {code!r}")
     if t.dim() != 2:
         raise ValueError("forge tensors are 2-D")
     if device and not t.is_cuda:
@@ -133,7 +139,10 @@ def describe(t: Optional[torch.Tensor], scale: Optional[torch.Tensor] = None, *,
             raise ValueError("block scale shape must be [rows, cols/64]")
     elif t.dtype in _FP8:
         raise ValueError("an FP8 tensor needs its float32 scale")
-    return ForgeTensor(t.data_ptr(), _DT[t.dtype], 0, t.shape[0], t.shape[1], ld,
+    dt = _DT[t.dtype]
+    if code == "dynamic" and dt in (I8, U8):
+        dt = I8_DYN if dt == I8 else U8_DYN
+    return ForgeTensor(t.data_ptr(), dt, 0, t.shape[0], t.shape[1], ld,
                        scale.data_ptr() if scale is not None else None)
 
 
@@ -183,6 +192,16 @@ def sr_bf16(x: float, r16: int) -> int:
     return int(_lib.forge_sr_bf16(float(x), int(r16)))
 
 
+def dyn_value(is_signed: bool, code: int) -> float:
+    """Value of a dynamic 8-bit moment code (host helper of the library)."""
+    return float(_lib.forge_dyn_value(int(bool(is_signed)), int(code)))
+
+
+def dyn_encode(is_signed: bool, y: float) -> int:
+    """The dynamic code the kernels store for a normalised value y (host helper)."""
+    return int(_lib.forge_dyn_encode(int(bool(is_signed)), float(y)))
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -197,15 +216,18 @@ def _stream(stream) -> Optional[int]:
 def wgrad_step(X: torch.Tensor, dY: torch.Tensor, W: torch.Tensor, m: Optional[torch.Tensor],
                v: Optional[torch.Tensor], opt: str = "adamw", hyper=None, step: int = 1, seed: int = 0,
                m_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None, stream=None,
-               x_scale: Optional[torch.Tensor] = None, dy_scale: Optional[torch.Tensor] = None) -> None:
+               x_scale: Optional[torch.Tensor] = None, dy_scale: Optional[torch.Tensor] = None,
+               code: str = "linear") -> None:
     """Fused dW = dY^T X + optimizer step; W, m, v (and scales) updated in place.
 
     FP8 inputs (X float8_e4m3fn, dY float8_e4m3fn or float8_e5m2) carry their
     dequantisation scales as one-element float32 device tensors x_scale, dy_scale.
+    int8 / uint8 moments hold linear codes, or the dynamic 8-bit code with code="dynamic".
     """
     h = _hyper(opt, hyper)
     st = _lib.forge_linear_wgrad_step(_ref(describe(X, x_scale)), _ref(describe(dY, dy_scale)), _ref(describe(W)),
-                                      _ref(describe(m, m_scale)), _ref(describe(v, v_scale)), OPT_ID[opt],
+                                      _ref(describe(m, m_scale, code=code)), _ref(describe(v, v_scale, code=code)),
+                                      OPT_ID[opt],
                                       ctypes.byref(h), int(step), seed & (2 ** 64 - 1), _stream(stream))
     if st:
         raise ForgeError(st, "forge_linear_wgrad_step")
@@ -238,13 +260,14 @@ def wgrad(X: torch.Tensor, dY: torch.Tensor, dW: Optional[torch.Tensor] = None, 
 def optimizer_step(dW: torch.Tensor, W: torch.Tensor, m: Optional[torch.Tensor], v: Optional[torch.Tensor],
                    opt: str = "adamw", hyper=None, step: int = 1, seed: int = 0,
                    m_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
-                   stream=None) -> None:
+                   stream=None, code: str = "linear") -> None:
     """Unfused baseline part 2: element-wise optimizer pass reading the stored dW."""
     if dW.dtype != torch.float32 or not dW.is_cuda or (dW.shape[1] > 1 and dW.stride(1) != 1):
         raise ValueError("dW must be a row-major float32 device tensor")
     h = _hyper(opt, hyper)
-    st = _lib.forge_optimizer_step(dW.data_ptr(), dW.stride(0), _ref(describe(W)), _ref(describe(m, m_scale)),
-                                   _ref(describe(v, v_scale)), OPT_ID[opt], ctypes.byref(h), int(step),
+    st = _lib.forge_optimizer_step(dW.data_ptr(), dW.stride(0), _ref(describe(W)),
+                                   _ref(describe(m, m_scale, code=code)), _ref(describe(v, v_scale, code=code)),
+                                   OPT_ID[opt], ctypes.byref(h), int(step),
                                    seed & (2 ** 64 - 1), _stream(stream))
     if st:
         raise ForgeError(st, "forge_optimizer_step")
@@ -252,15 +275,16 @@ def optimizer_step(dW: torch.Tensor, W: torch.Tensor, m: Optional[torch.Tensor],
 
 def wgrad_unfused(X, dY, W, m, v, opt="adamw", hyper=None, step=1, seed=0, m_scale=None, v_scale=None,
                   dW_workspace: Optional[torch.Tensor] = None, stream=None, x_scale=None,
-                  dy_scale=None) -> torch.Tensor:
+                  dy_scale=None, code: str = "linear") -> torch.Tensor:
     """The two-phase baseline: store dW (float32), then a separate optimizer pass. Returns dW."""
     dW = wgrad(X, dY, dW_workspace, stream, x_scale, dy_scale)
-    optimizer_step(dW, W, m, v, opt, hyper, step, seed, m_scale, v_scale, stream)
+    optimizer_step(dW, W, m, v, opt, hyper, step, seed, m_scale, v_scale, stream, code)
     return dW
 
 
 def new_states(W: torch.Tensor, opt: str = "adamw", fmt: str = "f32"):
-    """Zero moment slots for `opt` in format f32, bf16 or q8: returns (m, v, m_scale, v_scale)."""
+    """Zero moment slots for `opt` in format f32, bf16, q8 (linear codes) or q8dyn (dynamic
+    codes; pass code="dynamic" to the step): returns (m, v, m_scale, v_scale)."""
     use_m, use_v = SLOTS[opt]
     rows, cols = W.shape
     m = v = ms = vs = None
@@ -274,7 +298,7 @@ def new_states(W: torch.Tensor, opt: str = "adamw", fmt: str = "f32"):
             m = torch.zeros((rows, cols), dtype=torch.bfloat16, device=W.device)
         if use_v:
             v = torch.zeros((rows, cols), dtype=torch.bfloat16, device=W.device)
-    elif fmt == "q8":
+    elif fmt in ("q8", "q8dyn"):
         if use_m:
             m = torch.zeros((rows, cols), dtype=torch.int8, device=W.device)
             ms = torch.zeros((rows, cols // 64), dtype=torch.float32, device=W.device)

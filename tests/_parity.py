@@ -90,6 +90,11 @@ def summation_bound_ok(gpu: np.ndarray, ref: np.ndarray, abs_sum: np.ndarray, K:
     return int(np.count_nonzero(err > bound)), float(np.max(err / np.maximum(bound, 1e-300))) if err.size else 0.0
 
 
+def state_code(state: str) -> str:
+    """The binding's code argument for a moment state format."""
+    return "dynamic" if state == "q8dyn" else "linear"
+
+
 def codes_ok(gpu: np.ndarray, ref: np.ndarray):
     d = np.abs(gpu.astype(np.int32) - ref.astype(np.int32))
     return int(np.count_nonzero(d > 1)), int(np.count_nonzero(d)), int(d.max()) if d.size else 0
@@ -280,7 +285,12 @@ def verify_step(opt, X, dY, before, after, hp, t, seed, io, state, sr, sel, g=No
             bad, worst = state_ok(got, ref[slot])
             assert bad == 0, f"step {t}: {slot}: {bad} elements out of tolerance (worst {worst:.3g}x)"
         else:
-            big, nd, mx = codes_ok(got, ref[slot])
+            if state == "q8dyn":
+                # dynamic codes: compare positions in value order (adjacent code values)
+                from oracle import q8
+                big, nd, mx = codes_ok(q8.dyn_rank(got, slot == "m"), q8.dyn_rank(ref[slot], slot == "m"))
+            else:
+                big, nd, mx = codes_ok(got, ref[slot])
             assert big == 0, f"step {t}: {slot} codes: {big} off by more than one step"
             bad, worst = state_ok(gs, ref[slot + "_scale"])
             assert bad == 0, f"step {t}: {slot} scales: {bad} out of tolerance (worst {worst:.3g}x)"

@@ -6,6 +6,8 @@ the update is element-wise and INT8 blocks never cross rows). Every checked
 step is teacher-forced from the GPU's previous state. dgrad is checked on a
 seeded sample of token rows.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -50,7 +52,8 @@ def _run_layer(f, wl, li, spec, opt, n_steps, check_steps, n_rows, check_dgrad_s
         if t == check_dgrad_step:
             _check_dgrad(f, dYd, Wd, dY, P.host(Wd), wl.config, li)
         before = P.snapshot((Wd, m, v, ms, vs), sel) if check else None
-        f.wgrad_step(Xd, dYd, Wd, m, v, opt, _gh(hp, wl.stochastic_round), t, seed, ms, vs)
+        f.wgrad_step(Xd, dYd, Wd, m, v, opt, _gh(hp, wl.stochastic_round), t, seed, ms, vs,
+                     code=P.state_code(wl.state))
         torch.cuda.synchronize()
         if check:
             after = P.snapshot((Wd, m, v, ms, vs), sel)
@@ -87,6 +90,13 @@ def test_down_proj_int8_states_twenty_steps():
     f = _forge()
     wl = WORKLOADS["down_q8_16384"]
     _run_layer(f, wl, 0, wl.layers[0], "adamw", 20, {1, 2, 3, 10, 20}, 128)
+
+
+@pytest.mark.timeout(600)
+def test_down_proj_dynamic_code_states_five_steps():
+    f = _forge()
+    wl = dataclasses.replace(WORKLOADS["down_q8_16384"], state="q8dyn")
+    _run_layer(f, wl, 1, wl.layers[0], "adamw", 5, {1, 2, 5}, 96)
 
 
 @pytest.mark.timeout(600)

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import gemm, optim, step
+from oracle import gemm, optim, q8, step
 from synth import LayerSpec, draw_layer_batch, draw_layer_init, f32_from_bf16_bits
 from tests import _parity as P
 
@@ -44,7 +44,7 @@ def run_case(spec, opt, steps, config=90, layer=0, state="f32", sr=True, rows=No
         Xd = P.dev_bf16(X) if io == "bf16" else P.dev(X)
         dYd = P.dev_bf16(dY) if io == "bf16" else P.dev(dY)
         before = P.snapshot((Wd, m, v, ms, vs), sel)
-        f.wgrad_step(Xd, dYd, Wd, m, v, opt, _gpu_hyper(hp, sr), t, seed, ms, vs)
+        f.wgrad_step(Xd, dYd, Wd, m, v, opt, _gpu_hyper(hp, sr), t, seed, ms, vs, code=P.state_code(state))
         torch.cuda.synchronize()
         after = P.snapshot((Wd, m, v, ms, vs), sel)
         P.verify_step(opt, X, dY, before, after, hp, t, seed, io, state, sr, sel)
@@ -102,6 +102,12 @@ def test_q8_states(opt):
     run_case(LayerSpec("q", 136, 320, 200, outlier_frac=0.01), opt, 3, config=98, state="q8", label="q8")
 
 
+@pytest.mark.parametrize("opt", ["adamw", "lion", "rmsprop", "sgd_momentum", "nadam", "radam", "adagrad"])
+def test_q8_dynamic_code_states(opt):
+    run_case(LayerSpec("q", 136, 320, 200, outlier_frac=0.01), opt, 3, config=98, layer=1, state="q8dyn",
+             label="q8 dynamic code")
+
+
 # ---------------------------------------------------------------- bfloat16 states
 @pytest.mark.parametrize("opt", optim.OPTIMIZERS)
 def test_bf16_states_all_optimizers_sr(opt):
@@ -152,7 +158,7 @@ CONFIGS = ["big", "small", "split", "band_n", "band_m", "band_full", "band_small
 
 
 @pytest.mark.parametrize("cfg", CONFIGS)
-@pytest.mark.parametrize("state", ["f32", "q8", "bf16"])
+@pytest.mark.parametrize("state", ["f32", "q8", "q8dyn", "bf16"])
 def test_each_tile_configuration_fused(cfg, state):
     n_in, n_out = _shape(cfg)
     rows = np.unique(np.concatenate([np.arange(0, n_out, max(1, n_out // 96)), [n_out - 1]]))
@@ -218,7 +224,8 @@ def test_dgrad_reads_old_weights_before_step():
 
 # ---------------------------------------------------------------- unfused baseline
 @pytest.mark.parametrize("opt,state", [("adamw", "f32"), ("lion", "f32"), ("radam", "f32"), ("adamw", "q8"),
-                                       ("rmsprop", "q8"), ("adamw", "bf16"), ("sgd_momentum", "bf16")])
+                                       ("rmsprop", "q8"), ("adamw", "q8dyn"), ("rmsprop", "q8dyn"),
+                                       ("adamw", "bf16"), ("sgd_momentum", "bf16")])
 def test_unfused_matches_fused(opt, state):
     f = _forge()
     spec = LayerSpec("u", 200, 320, 300)
@@ -231,15 +238,18 @@ def test_unfused_matches_fused(opt, state):
             X, dY = draw_layer_batch(101, 0, t, spec)
             args = (P.dev_bf16(X), P.dev_bf16(dY), Wd, m, v, opt, None, t, 7, ms, vs)
             if fused:
-                f.wgrad_step(*args)
+                f.wgrad_step(*args, code=P.state_code(state))
             else:
-                f.wgrad_unfused(*args)
+                f.wgrad_unfused(*args, code=P.state_code(state))
         torch.cuda.synchronize()
         outs.append([P.host(x) for x in (Wd, m, v, ms, vs) if x is not None])
     for a, b in zip(*outs):
         if a.dtype == np.uint16:
             ok, n, mx = P.bf16_sr_ok(a, b)
             assert ok, (n, mx)
+        elif a.dtype in (np.int8, np.uint8) and state == "q8dyn":
+            signed = a.dtype == np.int8
+            assert P.codes_ok(q8.dyn_rank(a, signed), q8.dyn_rank(b, signed))[0] == 0
         elif a.dtype in (np.int8, np.uint8):
             assert P.codes_ok(a, b)[0] == 0
         else:

@@ -284,3 +284,56 @@ def test_step_scalars_errors(f):
     assert lib.forge_step_scalars(0, ctypes.byref(h), 1, None) == -1
     with pytest.raises(f.ForgeError):
         f.step_scalars("adamw", {"eps": -1.0}, 1)
+
+
+# ---------------------------------------------------------------- dynamic 8-bit moment code
+def test_dyn_table_matches_oracle(f):
+    """The library's constexpr tables equal the oracle's code values bit for bit."""
+    from oracle import q8
+    for k in range(256):
+        val = np.float32(f.dyn_value(False, k))
+        assert val.view(np.uint32) == q8.DYN_UNSIGNED[k].view(np.uint32), k
+        ref = -q8.DYN_SIGNED[k & 0x7F] if k & 0x80 else q8.DYN_SIGNED[k]
+        assert np.float32(f.dyn_value(True, k)) == np.float32(ref), k
+    assert math.isnan(f.dyn_value(True, 256)) and math.isnan(f.dyn_value(False, -1))
+
+
+def test_dyn_encode_matches_oracle(f):
+    """The library's encoder (the kernels' code, host build) picks the oracle's code for
+    random normalised values, for every code value and for the float32 neighbours of
+    every midpoint between codes (the decision boundaries)."""
+    from oracle import q8
+    rng = np.random.default_rng(11)
+    for signed, table in ((True, q8.DYN_SIGNED), (False, q8.DYN_UNSIGNED)):
+        t64 = table.astype(np.float64)
+        mids = ((t64[:-1] + t64[1:]) * 0.5).astype(np.float32)
+        ys = [table, mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(2)),
+              rng.uniform(0, 1, 2000).astype(np.float32), (10.0 ** rng.uniform(-9, 0, 2000)).astype(np.float32)]
+        y = np.clip(np.concatenate(ys), 0, 1).astype(np.float32)
+        if signed:
+            y = np.concatenate([y, -y[: y.size // 2]])
+        x = np.zeros((y.size, 64))
+        x[:, 0] = 1.0
+        x[:, 1] = y
+        q, _ = (q8.quant_dyn_signed if signed else q8.quant_dyn_unsigned)(x)
+        got = np.array([f.dyn_encode(signed, float(v)) for v in y])
+        np.testing.assert_array_equal(got, q[:, 1].astype(np.int64))
+
+
+@cpu_only
+def test_dyn_state_validation(f):
+    F32, BF16, I8, U8, E4M3, I8D, U8D = 0, 1, 2, 3, 4, 6, 7
+    A, B, C, Mp, Vp, S1, S2 = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000, 0x60000000, 0x70000000
+    X, dY, W = _t(f, A, BF16, 64, 256), _t(f, B, BF16, 64, 128), _t(f, C, BF16, 128, 256)
+    dm, dv = _t(f, Mp, I8D, 128, 256, scale=S1), _t(f, Vp, U8D, 128, 256, scale=S2)
+    assert _call_step(f, X, dY, W, dm, _t(f, Vp, U8, 128, 256, scale=S2)) == -3    # linear and dynamic mixed
+    assert _call_step(f, X, dY, W, _t(f, Mp, U8D, 128, 256, scale=S1), dv) == -3    # m must be the signed code
+    assert _call_step(f, X, dY, W, _t(f, Mp, I8D, 128, 256), dv) == -1             # missing scales
+    assert _call_step(f, _t(f, A, F32, 64, 256), _t(f, B, F32, 64, 128), _t(f, C, F32, 128, 256), dm, dv) == -3
+    Xr, Wr = _t(f, A, BF16, 64, 264), _t(f, C, BF16, 128, 264)
+    assert _call_step(f, Xr, dY, Wr, _t(f, Mp, I8D, 128, 264, ld=272, scale=S1),
+                      _t(f, Vp, U8D, 128, 264, ld=272, scale=S2)) == -5             # in % 64 == 0
+    one = 0x78000000
+    X8 = _t(f, A, E4M3, 64, 256, scale=one)
+    dY8 = _t(f, B, E4M3, 64, 128, scale=one + 256)
+    assert _call_step(f, X8, dY8, W, dm, dv) == -5                                  # not with FP8 inputs
