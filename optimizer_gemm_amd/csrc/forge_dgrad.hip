@@ -165,6 +165,16 @@ __global__ __launch_bounds__(256) void optimizer_kernel(const float* __restrict_
   constexpr bool Q8D = SF == ST_Q8D, Q8 = SF == ST_Q8 || Q8D, B16S = SF == ST_BF16;
   constexpr int SL = opt_slots(OPT);
   constexpr bool HAS_M = SL & 1, HAS_V = SL & 2;
+  // dynamic-code tables staged in LDS, as in the fused epilogue
+  const DynTables* dyn = &g_dyn;
+  if constexpr (Q8D) {
+    __shared__ DynTables dyn_lds;
+    float* dst = reinterpret_cast<float*>(&dyn_lds);
+    const float* src = reinterpret_cast<const float*>(&g_dyn);
+    for (int j = threadIdx.x; j < (int)(sizeof(DynTables) / 4); j += 256) dst[j] = src[j];
+    __syncthreads();
+    dyn = &dyn_lds;
+  }
   const int64_t vec_per_row = a.in >> 2;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = (int64_t)a.out * vec_per_row;
@@ -181,13 +191,13 @@ __global__ __launch_bounds__(256) void optimizer_kernel(const float* __restrict_
         const uint32_t q = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.m) + (int64_t)o * a.ldm + i);
         const float sc = a.m_scale[si];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) m[j] = dyn_decode_s((q >> (8 * j)) & 0xFFu, g_dyn.vs) * sc;
+        for (int j = 0; j < 4; ++j) m[j] = dyn_decode_s((q >> (8 * j)) & 0xFFu, dyn->vs) * sc;
       }
       if constexpr (HAS_V) {
         const uint32_t q = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.v) + (int64_t)o * a.ldv + i);
         const float sc = a.v_scale[si];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = g_dyn.vu[(q >> (8 * j)) & 0xFFu] * sc;
+        for (int j = 0; j < 4; ++j) v[j] = dyn->vu[(q >> (8 * j)) & 0xFFu] * sc;
       }
     } else if constexpr (Q8) {
       if constexpr (HAS_M) dequant_m4(a, o, i, m);
@@ -221,10 +231,10 @@ __global__ __launch_bounds__(256) void optimizer_kernel(const float* __restrict_
     if (valid) {
       if constexpr (HAS_M)
         *reinterpret_cast<uint32_t*>(reinterpret_cast<int8_t*>(a.m) + (int64_t)o * a.ldm + i) =
-            Q8D ? quant_dyn_m4(m, sm, g_dyn.ms) : quant_m4(m, sm);
+            Q8D ? quant_dyn_m4(m, sm, dyn->ms) : quant_m4(m, sm);
       if constexpr (HAS_V)
         *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.v) + (int64_t)o * a.ldv + i) =
-            Q8D ? quant_dyn_v4(r, sv, g_dyn.mu) : quant_v4(r, sv);
+            Q8D ? quant_dyn_v4(r, sv, dyn->mu) : quant_v4(r, sv);
       if ((i & 63) == 0) {
         const int64_t si = (int64_t)o * (a.in >> 6) + (i >> 6);
         if constexpr (HAS_M) a.m_scale[si] = sm;

@@ -299,7 +299,8 @@ constexpr DynTables make_dyn_tables() {
 // Device copy (one per translation unit that uses it; read-only).
 static __constant__ DynTables g_dyn = make_dyn_tables();
 
-// Number of the N sorted midpoints mid[0..N-1] (padded with +inf) that are <= a.
+// Number of the N sorted midpoints mid[0..N-1] (padded with +inf) that are <= a:
+// plain binary search (the reference form of the encoder).
 template <int N>
 __host__ __device__ __forceinline__ uint32_t dyn_search(const float* mid, float a) {
   uint32_t k = 0;
@@ -307,11 +308,39 @@ __host__ __device__ __forceinline__ uint32_t dyn_search(const float* mid, float 
   for (int step = N / 2; step >= 1; step >>= 1) k += (mid[k + step - 1] <= a) ? (uint32_t)step : 0u;
   return k;
 }
+// The same count for a code of NB magnitude bits, from a guess and one check: the
+// decade of a is found by comparing with the float powers 10^-1 .. 10^-(NB-1), the
+// index inside it by inverting the linear fraction (k = 2^F (t + 0.8) / 0.9 - 1 for
+// t = a 10^E); the guess is within one step of the count for every float a in
+// [0, 1] (checked exhaustively on the host), so the midpoints on either side of it
+// settle the answer. All operations are IEEE float with no contraction, so the
+// guess is the same on host and device.
+// a <= 0 (and NaN) give 0.
+template <int NB>
+__host__ __device__ __forceinline__ uint32_t dyn_search_fast(const float* mid, float a) {
+#pragma clang fp contract(off)
+  if (!(a > 0.f)) return 0u;
+  constexpr float kPow10Neg[8] = {1.f, 1e-1f, 1e-2f, 1e-3f, 1e-4f, 1e-5f, 1e-6f, 1e-7f};
+  float p = 1.f;
+  int F = NB - 1;
+#pragma unroll
+  for (int j = 1; j < NB; ++j) {
+    const bool below = a <= kPow10Neg[j];
+    p = below ? p * 10.f : p;
+    F -= below ? 1 : 0;
+  }
+  const float kr = ldexpf((a * p + 0.8f) * (1.f / 0.9f), F) - 1.f;
+  int k = (int)rintf(kr);
+  k = k < 0 ? 0 : (k > (1 << NB) - 1 ? (1 << NB) - 1 : k);
+  const float hi = mid[k];
+  const float lo = k > 0 ? mid[k - 1] : -__builtin_huge_valf();
+  return (uint32_t)(k + (hi <= a ? 1 : 0) - (lo > a ? 1 : 0));
+}
 __host__ __device__ __forceinline__ uint32_t dyn_encode_s(float y, const float* mid) {
-  const uint32_t k = dyn_search<128>(mid, fabsf(y));
+  const uint32_t k = dyn_search_fast<7>(mid, fabsf(y));
   return (y < 0.f && k != 0u) ? (k | 0x80u) : k;
 }
-__host__ __device__ __forceinline__ uint32_t dyn_encode_u(float y, const float* mid) { return dyn_search<256>(mid, y); }
+__host__ __device__ __forceinline__ uint32_t dyn_encode_u(float y, const float* mid) { return dyn_search_fast<8>(mid, y); }
 __host__ __device__ __forceinline__ float dyn_decode_s(uint32_t b, const float* vs) {
   const float x = vs[b & 0x7Fu];
   return (b & 0x80u) ? -x : x;
