@@ -337,3 +337,22 @@ def test_dyn_state_validation(f):
     X8 = _t(f, A, E4M3, 64, 256, scale=one)
     dY8 = _t(f, B, E4M3, 64, 128, scale=one + 256)
     assert _call_step(f, X8, dY8, W, dm, dv) == -5                                  # not with FP8 inputs
+
+
+def test_dyn_fast_encoder_exhaustive(tmp_path):
+    """The kernels' dynamic-code encoder (guess + one-step check) equals the binary
+    search over the midpoints for every float in [0, 1] (host build of the same code;
+    the guess uses only IEEE float operations, so the device computes the same)."""
+    import shutil
+    import subprocess
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    exe = str(tmp_path / "dyn_exhaustive")
+    src = os.path.join(ROOT, "tests", "dyn_encoder_exhaustive.cpp")
+    r = subprocess.run([hipcc, "-O2", "-std=c++17", "-x", "hip", "--offload-arch=gfx950", "-pthread", src, "-o", exe],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.startswith("0 mismatches")
