@@ -47,7 +47,7 @@ class _ForgeLinearFn(torch.autograd.Function):
             dx = forge.dgrad(dy2, w.detach()).reshape(x.shape)  # old W, before the update below
         layer._step_count += 1
         forge.wgrad_step(x2, dy2, w.detach(), layer.m, layer.v, layer.opt, layer.hyper, layer._step_count,
-                         layer.seed, layer.m_scale, layer.v_scale)
+                         layer.seed, layer.m_scale, layer.v_scale, code=layer.code)
         return dx, None, None
 
 
@@ -56,7 +56,8 @@ class ForgeLinear(torch.nn.Module):
 
     weight: [out, in] bf16 or float32 parameter (bias-free, as the linear
     layers the pages evaluate). opt / hyper: the optimizer and its
-    hyper-parameters (forge_hyper fields). states: "f32" or "q8" (INT8 block-64).
+    hyper-parameters (forge_hyper fields). states: "f32", "bf16", "q8" (INT8
+    block-64, linear codes) or "q8dyn" (INT8 block-64, dynamic 8-bit code).
     """
 
     def __init__(self, in_features: int, out_features: int, opt: str = "adamw", hyper: Optional[dict] = None,
@@ -70,6 +71,7 @@ class ForgeLinear(torch.nn.Module):
         self.opt = opt
         self.hyper = forge.make_hyper(opt, **(hyper or {}))
         m, v, ms, vs = forge.new_states(self.weight.detach(), opt, states)
+        self.code = "dynamic" if states == "q8dyn" else "linear"
         for name, t in (("m", m), ("v", v), ("m_scale", ms), ("v_scale", vs)):
             if t is None:
                 setattr(self, name, None)

@@ -80,3 +80,28 @@ def test_forge_linear_no_gradient_memory():
     grown = torch.cuda.max_memory_allocated() - base
     assert layer.weight.grad is None
     assert grown < 2048 * 2048 * 2  # well below one bf16 weight gradient
+
+
+@pytest.mark.parametrize("states", ["q8", "q8dyn", "bf16"])
+def test_forge_linear_low_precision_states_match_direct_calls(states):
+    # a ForgeLinear with INT8 (linear or dynamic codes) or bf16 moments updates W and its
+    # moments exactly as the direct call with the same state format does
+    import optimizer_gemm_amd as forge
+    from optimizer_gemm_amd.nn import ForgeLinear
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(6)
+    T, d_in, d_out = 160, 256, 192
+    print(f"[case] ForgeLinear states={states}", flush=True)
+    layer = ForgeLinear(d_in, d_out, device=dev, seed=4, states=states)
+    W0 = layer.weight.detach().clone()
+    x = torch.randn(T, d_in, device=dev, generator=g).to(torch.bfloat16)
+    G = (torch.randn(T, d_out, device=dev, generator=g) * 1e-3).to(torch.bfloat16)
+    layer(x).backward(G)
+    W = W0.clone()
+    m, v, ms, vs = forge.new_states(W, "adamw", states)
+    forge.wgrad_step(x, G, W, m, v, "adamw", None, 1, layer.seed, ms, vs, code=P.state_code(states))
+    torch.cuda.synchronize()
+    assert torch.equal(layer.weight.detach().view(torch.int16), W.view(torch.int16))
+    for a, b in ((layer.m, m), (layer.v, v), (layer.m_scale, ms), (layer.v_scale, vs)):
+        assert (a is None and b is None) or torch.equal(a, b)
