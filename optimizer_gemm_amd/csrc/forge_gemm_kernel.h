@@ -53,6 +53,17 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 enum { G_EPI_STORE = 0, G_EPI_OPT = 1, G_EPI_DX = 2 };
 
+// Cache policy of the optimizer epilogue's W / m / v (and block-scale) loads and
+// stores: non-temporal (the nt bit of the buffer instructions), since each state
+// element is read once and written once per step; the X / dY operand stages keep
+// the default policy so their panels stay in L2 for the neighbouring tiles.
+#ifndef FORGE_EPI_LD_CPOL
+#define FORGE_EPI_LD_CPOL 2
+#endif
+#ifndef FORGE_EPI_ST_CPOL
+#define FORGE_EPI_ST_CPOL 2
+#endif
+
 
 // Operand formats of the GEMM core: bfloat16, or OCP FP8 (E4M3 / E5M2 per operand).
 enum { G_BF16 = 0, G_FP8 = 1 };
@@ -596,28 +607,30 @@ void gemm_kernel(GArgs g, OptArgs a) {
           const int o = nrow0 + row, i = m0 + col;
           const bool ok = o < g.N && i < g.M;
           ow[k] = ok ? (uint32_t)(o * a.ldw + i) * 2u : kOOB;
-          wb[k] = __builtin_amdgcn_raw_buffer_load_b64(R.W, ow[k], 0, 0);
+          wb[k] = __builtin_amdgcn_raw_buffer_load_b64(R.W, ow[k], 0, FORGE_EPI_LD_CPOL);
           if constexpr (B16S) {
             om[k] = ok ? (uint32_t)(o * a.ldm + i) * 2u : kOOB;
             ov_[k] = ok ? (uint32_t)(o * a.ldv + i) * 2u : kOOB;
-            if constexpr (HAS_M) mb[k] = __builtin_amdgcn_raw_buffer_load_b64(R.m, om[k], 0, 0);
-            if constexpr (HAS_V) vb[k] = __builtin_amdgcn_raw_buffer_load_b64(R.v, ov_[k], 0, 0);
+            if constexpr (HAS_M) mb[k] = __builtin_amdgcn_raw_buffer_load_b64(R.m, om[k], 0, FORGE_EPI_LD_CPOL);
+            if constexpr (HAS_V) vb[k] = __builtin_amdgcn_raw_buffer_load_b64(R.v, ov_[k], 0, FORGE_EPI_LD_CPOL);
           } else if constexpr (!Q8) {
             om[k] = ok ? (uint32_t)(o * a.ldm + i) * 4u : kOOB;
             ov_[k] = ok ? (uint32_t)(o * a.ldv + i) * 4u : kOOB;
-            if constexpr (HAS_M) mv[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(R.m, om[k], 0, 0));
-            if constexpr (HAS_V) vv[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(R.v, ov_[k], 0, 0));
+            if constexpr (HAS_M)
+              mv[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(R.m, om[k], 0, FORGE_EPI_LD_CPOL));
+            if constexpr (HAS_V)
+              vv[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(R.v, ov_[k], 0, FORGE_EPI_LD_CPOL));
           } else {
             om[k] = ok ? (uint32_t)(o * a.ldm + i) : kOOB;
             ov_[k] = ok ? (uint32_t)(o * a.ldv + i) : kOOB;
             osc[k] = ok ? (uint32_t)(o * (a.in >> 6) + (i >> 6)) * 4u : kOOB;
             if constexpr (HAS_M) {
-              qm[k] = __builtin_amdgcn_raw_buffer_load_b32(R.m, om[k], 0, 0);
-              msc[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(R.ms, osc[k], 0, 0));
+              qm[k] = __builtin_amdgcn_raw_buffer_load_b32(R.m, om[k], 0, FORGE_EPI_LD_CPOL);
+              msc[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(R.ms, osc[k], 0, FORGE_EPI_LD_CPOL));
             }
             if constexpr (HAS_V) {
-              qv[k] = __builtin_amdgcn_raw_buffer_load_b32(R.v, ov_[k], 0, 0);
-              vsc[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(R.vs, osc[k], 0, 0));
+              qv[k] = __builtin_amdgcn_raw_buffer_load_b32(R.v, ov_[k], 0, FORGE_EPI_LD_CPOL);
+              vsc[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(R.vs, osc[k], 0, FORGE_EPI_LD_CPOL));
             }
           }
         }
@@ -668,19 +681,22 @@ void gemm_kernel(GArgs g, OptArgs a) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             bb[j] = SR ? sr_bf16_bits(w[j], rand16_from_base(a.rng_base, idx0 + j)) : rne_bf16_bits(w[j]);
-          __builtin_amdgcn_raw_buffer_store_b64(u32x2{bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16)}, R.W, ow[k], 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16)}, R.W, ow[k], 0,
+                                                FORGE_EPI_ST_CPOL);
           if constexpr (B16S) {
             if constexpr (HAS_M)
               __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4<SR>(m, rng_stream_base(a.rng_base, 1), idx0), R.m, om[k],
-                                                    0, 0);
+                                                    0, FORGE_EPI_ST_CPOL);
             if constexpr (HAS_V)
               __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4<SR>(v, rng_stream_base(a.rng_base, 2), idx0), R.v,
-                                                    ov_[k], 0, 0);
+                                                    ov_[k], 0, FORGE_EPI_ST_CPOL);
           } else if constexpr (!Q8) {
             if constexpr (HAS_M)
-              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{m[0], m[1], m[2], m[3]}), R.m, om[k], 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{m[0], m[1], m[2], m[3]}), R.m, om[k], 0,
+                                                     FORGE_EPI_ST_CPOL);
             if constexpr (HAS_V)
-              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{v[0], v[1], v[2], v[3]}), R.v, ov_[k], 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{v[0], v[1], v[2], v[3]}), R.v, ov_[k], 0,
+                                                     FORGE_EPI_ST_CPOL);
           } else {
             // block-64 absmax over the 16 adjacent lanes holding this row's block
             // (linear codes: of m and sqrt(v); dynamic codes: of m and v)
@@ -698,15 +714,15 @@ void gemm_kernel(GArgs g, OptArgs a) {
             }
             const float sm = Q8D ? mmax : mmax / 127.f, sv = Q8D ? vmax : vmax / 255.f;
             if constexpr (Q8D) {
-              if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(quant_dyn_m4(m, sm, dyn->ms), R.m, om[k], 0, 0);
-              if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(quant_dyn_v4(r, sv, dyn->mu), R.v, ov_[k], 0, 0);
+              if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(quant_dyn_m4(m, sm, dyn->ms), R.m, om[k], 0, FORGE_EPI_ST_CPOL);
+              if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(quant_dyn_v4(r, sv, dyn->mu), R.v, ov_[k], 0, FORGE_EPI_ST_CPOL);
             } else {
-              if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(quant_m4(m, sm), R.m, om[k], 0, 0);
-              if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(quant_v4(r, sv), R.v, ov_[k], 0, 0);
+              if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(quant_m4(m, sm), R.m, om[k], 0, FORGE_EPI_ST_CPOL);
+              if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(quant_v4(r, sv), R.v, ov_[k], 0, FORGE_EPI_ST_CPOL);
             }
             if ((col & 63) == 0) {
-              if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sm), R.ms, osc[k], 0, 0);
-              if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sv), R.vs, osc[k], 0, 0);
+              if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sm), R.ms, osc[k], 0, FORGE_EPI_ST_CPOL);
+              if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sv), R.vs, osc[k], 0, FORGE_EPI_ST_CPOL);
             }
           }
         }
