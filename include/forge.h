@@ -85,7 +85,7 @@ typedef struct {
  *   AdamW, Lion: decoupled decay theta *= (1 - lr*weight_decay).
  *   SGD, SGD-momentum, RMSprop, AdaGrad, NAdam, RAdam: coupled L2, g += weight_decay*theta.
  *   Lion: beta1 interpolates the sign argument, beta2 tracks the state.
- *   RMSprop: alpha is the smoothing constant. AdaGrad: lr_decay. NAdam: momentum_decay.
+ *   RMSprop: alpha is the smoothing constant. AdaGrad: lr_decay. NAdam: momentum_decay (>= 0).
  *   SGD-momentum: momentum, dampening, nesterov. */
 typedef struct {
   double lr, beta1, beta2, eps, weight_decay;

@@ -82,6 +82,7 @@ int check_hyper(int opt, const forge_hyper* h, int64_t step) {
     case FORGE_RADAM:
     case FORGE_LION:
       if (h->beta1 < 0.0 || h->beta1 >= 1.0 || h->beta2 < 0.0 || h->beta2 >= 1.0) return FORGE_ERR_HYPER;
+      if (opt == FORGE_NADAM && h->momentum_decay < 0.0) return FORGE_ERR_HYPER;
       break;
     case FORGE_SGD_MOMENTUM:
       if (h->momentum < 0.0 || h->momentum >= 1.0 || h->dampening < 0.0 || h->dampening > 1.0) return FORGE_ERR_HYPER;
@@ -258,10 +259,19 @@ int forge_step_scalars(int32_t opt, const forge_hyper* h, int64_t step, forge_sc
       s.lr = (float)(lr / (1.0 + (t - 1.0) * h->lr_decay));
       break;
     case FORGE_NADAM: {
-      const double psi = h->momentum_decay;
-      auto mu = [&](double k) { return b1 * (1.0 - 0.5 * pow(0.96, k * psi)); };
-      double prod = 1.0;
-      for (int64_t k = 1; k <= step; ++k) prod *= mu((double)k);
+      // mu_k = beta1 (1 - q^k / 2) with q = 0.96^psi. The product over k <= t has an
+      // exact series of constant cost in t (psi >= 0, so q^k / 2 <= 1/2):
+      //   log prod_{k<=t} (1 - q^k / 2) = -sum_{n>=1} (2^-n / n) q^n (1 - q^(n t)) / (1 - q^n),
+      // both differences through expm1; 64 terms reach double precision (terms ~ 2^-n).
+      const double L = h->momentum_decay * log(0.96);  // log q
+      auto mu = [&](double k) { return b1 * (1.0 - 0.5 * exp(k * L)); };
+      double S = 0.0, half_n = 1.0;
+      for (int n = 1; n <= 64; ++n) {
+        half_n *= 0.5;
+        const double ratio = (L == 0.0) ? t : expm1((double)n * t * L) / expm1((double)n * L);
+        S += half_n / n * exp((double)n * L) * ratio;
+      }
+      const double prod = b1 > 0.0 ? exp(t * log(b1) - S) : 0.0;
       const double mu_t = mu(t), mu_n = mu(t + 1.0);
       s.inv_sqrt_bc2 = (float)(1.0 / sqrt(bc2));
       s.c_g = (float)(lr * (1.0 - mu_t) / (1.0 - prod));

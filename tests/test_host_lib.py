@@ -356,3 +356,32 @@ def test_dyn_fast_encoder_exhaustive(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout + r.stderr
     assert r.stdout.startswith("0 mismatches")
+
+
+@pytest.mark.parametrize("psi", [4e-3, 0.0, 0.5])
+def test_nadam_scalars_at_large_steps(f, psi):
+    """NAdam's momentum product prod_{k<=t} mu_k, computed by the library in constant
+    time, matches the plain product of the oracle's mu_k up to float rounding of the
+    kernel arguments, from step 1 to 10^5; a call at step 10^9 stays cheap."""
+    import time
+    hp = dict(optim.hyper("nadam"), momentum_decay=psi)
+    b1, lr = hp["beta1"], hp["lr"]
+    prod = 1.0
+    marks = {1, 2, 7, 100, 5000, 100000}
+    for t in range(1, 100001):
+        prod *= optim.nadam_mu(b1, psi, t)
+        if t in marks:
+            mu_t, mu_n = optim.nadam_mu(b1, psi, t), optim.nadam_mu(b1, psi, t + 1)
+            s = f.step_scalars("nadam", dict(momentum_decay=psi), t)
+            np.testing.assert_allclose(s["c_g"], lr * (1 - mu_t) / (1 - prod), rtol=2e-6)
+            np.testing.assert_allclose(s["c_m"], lr * mu_n / (1 - prod * mu_n), rtol=2e-6)
+    c0 = time.perf_counter()
+    s = f.step_scalars("nadam", dict(momentum_decay=psi), 10 ** 9)
+    assert time.perf_counter() - c0 < 0.05
+    mu_inf = b1 * (1 - 0.5 * 0.96 ** (psi * 10 ** 9))
+    np.testing.assert_allclose(s["c_m"], lr * mu_inf, rtol=2e-6)  # the product has vanished
+
+
+def test_nadam_negative_momentum_decay_rejected(f):
+    with pytest.raises(f.ForgeError):
+        f.step_scalars("nadam", dict(momentum_decay=-1e-3), 1)
