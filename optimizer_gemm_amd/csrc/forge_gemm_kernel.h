@@ -795,15 +795,15 @@ using DgradBig = GCfg<FORGE_DGRAD_BIG_CFG>;
 using DgradSmall = GCfg<FORGE_DGRAD_SMALL_CFG>;
 using DgradSplit = GCfg<FORGE_DGRAD_SPLIT_CFG>;
 
+// Compute units of the device current at the first launch (the library targets one
+// part, gfx950); the function-local static is initialised once, thread-safely.
 static int g_num_cus() {
-  static int n = 0;
-  if (n == 0) {
+  static const int n = [] {
     int dev = 0, v = 0;
     if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      n = v;
-    else
-      n = 256;
-  }
+      return v;
+    return 256;
+  }();
   return n;
 }
 
