@@ -12,10 +12,10 @@ can reproduce it bit for bit):
   `seed` (Steele, Lea & Flood, "Fast splittable pseudorandom number generators",
   OOPSLA 2014): z = seed + (c+1)*0x9E3779B97F4A7C15 (mod 2**64), then the
   SplitMix64 finaliser. r16 = z >> 48.
-* bfloat16 moment states are rounded the same way from their own streams: the
-  stream s uses the seed seed + s * 2**62 (mod 2**64), s = 0 for the weight, 1 for
-  m, 2 for v. With step < 2**30 the SplitMix64 states z of different streams never
-  coincide (they would need counters 2**62 apart).
+* bfloat16 moment states are rounded the same way with other 16-bit fields of
+  the same 64-bit word: bits 32..47 for m, bits 16..31 for v (the weight takes
+  bits 48..63), so one SplitMix64 evaluation serves all three roundings of an
+  element.
 * Stochastic rounding of a float32 x: bf16 bits = (bits(x) + r16) >> 16 on the
   unsigned 32-bit pattern, which rounds the magnitude away from zero with
   probability low16(bits(x)) / 65536. NaN becomes the quiet NaN 0x7FC0 with the
@@ -66,15 +66,13 @@ def counters(step: int, idx: np.ndarray) -> np.ndarray:
 STREAM_W, STREAM_M, STREAM_V = 0, 1, 2
 
 
-def stream_seed(seed: int, stream: int) -> int:
-    """Seed of random stream `stream` (0: weight, 1: m, 2: v)."""
-    return (seed + (stream << 62)) & _M64
-
-
 def rand16(seed: int, step: int, idx: np.ndarray, stream: int = STREAM_W) -> np.ndarray:
-    """16 random bits per element: top 16 bits of the SplitMix64 word (uint32 array)."""
-    z = splitmix64_at(stream_seed(seed, stream), counters(step, idx))
-    return (z >> np.uint64(48)).astype(np.uint32)
+    """16 random bits per element (uint32 array): bits 48..63 of the SplitMix64 word
+    for the weight (stream 0), bits 32..47 for m (1), bits 16..31 for v (2)."""
+    if stream not in (STREAM_W, STREAM_M, STREAM_V):
+        raise ValueError(stream)
+    z = splitmix64_at(seed, counters(step, idx))
+    return ((z >> np.uint64(48 - 16 * stream)) & np.uint64(0xFFFF)).astype(np.uint32)
 
 
 def element_index(rows: np.ndarray, n_in: int) -> np.ndarray:

@@ -4,11 +4,15 @@ Closed forms through the whole composition (gradient -> update -> storage), and
 the pages' exactness claim: a tile-wise schedule gives the same step as the
 full-gradient step for element-wise optimizers (§2 "Precision and fidelity").
 """
+import os
+
 import numpy as np
 import pytest
 
 from oracle import gemm, optim, q8, rounding, step
 from synth import inputs
+
+GOLDEN_SPLITMIX = os.path.join(os.path.dirname(__file__), "golden", "splitmix64_published.txt")
 
 
 def _f32_layer(seed, T=64, n_out=32, n_in=48):
@@ -121,14 +125,22 @@ def test_q8_state_step_updates_with_unquantised_moments():
 
 
 # ---------------------------------------------------------------- bfloat16 moment states
-def test_moment_streams_follow_the_sequential_generator():
-    # stream s is SplitMix64 started from seed + s * 2^62: the c-th counter draws the
-    # (c+1)-th output of the sequential generator from that state
+def test_moment_bits_are_fields_of_the_published_words():
+    # the m and v draws are bits 32..47 and 16..31 of the same SplitMix64 word as the
+    # weight's: for counter c it is output number c+1 of the generator, checked against
+    # the published outputs for seed 1234567 and the sequential generator
+    lines = [l.split() for l in open(GOLDEN_SPLITMIX) if l.strip() and not l.startswith("#")]
+    seed = int(lines[0][1])
+    words = [int(l[0]) for l in lines[1:]]
+    idx = np.arange(len(words), dtype=np.uint64)
+    for s, shift in ((0, 48), (1, 32), (2, 16)):
+        got = rounding.rand16(seed, 0, idx, stream=s)
+        np.testing.assert_array_equal(got, np.array([(z >> shift) & 0xFFFF for z in words], dtype=np.uint32))
     seed = 0x0123456789ABCDEF
-    for s in (1, 2):
-        seq = rounding.splitmix64_py((seed + (s << 62)) % (1 << 64), 40)
+    seq = rounding.splitmix64_py(seed, 40)
+    for s, shift in ((1, 32), (2, 16)):
         got = rounding.rand16(seed, 0, np.arange(40, dtype=np.uint64), stream=s)
-        np.testing.assert_array_equal(got, np.array([z >> 48 for z in seq], dtype=np.uint32))
+        np.testing.assert_array_equal(got, np.array([(z >> shift) & 0xFFFF for z in seq], dtype=np.uint32))
 
 
 def test_moment_streams_are_uncorrelated_with_the_weight_stream():
