@@ -148,7 +148,7 @@ int32_t forge_dyn_encode(int32_t is_signed, float y);
  * dtypes: X, dY, W all FORGE_F32, or all FORGE_BF16. m and v: FORGE_F32, or
  * FORGE_I8 (m) and FORGE_U8 (v) with block scales, or FORGE_I8_DYN (m) and
  * FORGE_U8_DYN (v) with block scales (both INT8 forms: bf16 W, in % 64 == 0, ld a
- * multiple of 16), or FORGE_BF16 (with bf16 W; ld a multiple of 8; step < 2^30);
+ * multiple of 16), or FORGE_BF16 (with bf16 W; ld a multiple of 8);
  * m and v must share one format.
  * Slots an optimizer does not use may be NULL and are never touched:
  *   SGD: none; SGD-momentum, Lion: m; RMSprop, AdaGrad: v; others: m and v.
@@ -156,9 +156,10 @@ int32_t forge_dyn_encode(int32_t is_signed, float y);
  * driven by a counter hash: r16 = top 16 bits of the SplitMix64 output number
  * ((step << 32) | (o*in + i)) + 1 from state `seed`; bf16 = (bits(w32) + r16) >> 16
  * (NaN -> quiet NaN). bfloat16 m and v are rounded the same way from their float32
- * update (the weight update uses the unrounded moments), with their own streams:
- * the seed is seed + 2^62 for m and seed + 2^63 for v (W: seed); with
- * stochastic_round = 0 all three round to nearest-even.
+ * update (the weight update uses the unrounded moments), with other 16-bit fields
+ * of the same SplitMix64 word: bits 32..47 for m, bits 16..31 for v (W: bits
+ * 48..63); with stochastic_round = 0 all three round to nearest-even.
+ * 1 <= step < 2^31.
  * T == 0 is allowed (zero gradient). Requires out*in < 2^32.
  * FP8 inputs (the pages' outlook, §5): X FORGE_E4M3 and dY FORGE_E4M3 or
  * FORGE_E5M2, each with its scale (see forge_tensor), with W FORGE_BF16 and

@@ -335,7 +335,6 @@ int forge_linear_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge
   if (X->rows != dY->rows || X->cols != W->cols || dY->cols != W->rows) return FORGE_ERR_SHAPE;
   const int fmt = check_states(opt, io, W, m, v);
   if (fmt < 0) return fmt;
-  if (fmt == ST_BF16 && step >= ((int64_t)1 << 30)) return FORGE_ERR_HYPER;
   if (f8 && (fmt == ST_Q8 || fmt == ST_Q8D)) return FORGE_ERR_UNSUPPORTED;
   if (W->rows * W->cols >= ((int64_t)1 << 32)) return FORGE_ERR_UNSUPPORTED;
   const int sl = opt_slots(opt);
@@ -414,7 +413,6 @@ int forge_optimizer_step(const float* dW, int64_t ld_dw, forge_tensor* W, forge_
   if (!aligned16(dW) || ld_dw % 4) return FORGE_ERR_ALIGN;
   const int fmt = check_states(opt, io, W, m, v);
   if (fmt < 0) return fmt;
-  if (fmt == ST_BF16 && step >= ((int64_t)1 << 30)) return FORGE_ERR_HYPER;
   if (W->rows * W->cols >= ((int64_t)1 << 32)) return FORGE_ERR_UNSUPPORTED;
   const int sl = opt_slots(opt);
   const forge_tensor dWt{const_cast<float*>(dW), FORGE_F32, 0, W->rows, W->cols, ld_dw, nullptr};

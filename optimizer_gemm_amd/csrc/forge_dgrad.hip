@@ -182,6 +182,7 @@ __global__ __launch_bounds__(256) void optimizer_kernel(const float* __restrict_
   const int o = valid ? (int)(gid / vec_per_row) : 0;
   const int i = valid ? (int)(gid % vec_per_row) * 4 : 0;
   float w[4] = {0.f, 0.f, 0.f, 0.f}, m[4] = {0.f, 0.f, 0.f, 0.f}, v[4] = {0.f, 0.f, 0.f, 0.f}, g[4];
+  uint64_t zz[4] = {0ull, 0ull, 0ull, 0ull};  // random words of the four elements (W, m, v fields)
   if (valid) {
     load_f4(dW, ld_dw, o, i, g);
     load_w4<W_BF16>(a, o, i, w);
@@ -211,7 +212,8 @@ __global__ __launch_bounds__(256) void optimizer_kernel(const float* __restrict_
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) opt_apply<OPT>(g[j], w[j], m[j], v[j], a.s);
-    store_w4<W_BF16, SR>(a, o, i, w);
+    rand64x4<SR>(a.rng_base, (uint32_t)o * (uint32_t)a.in + (uint32_t)i, zz);
+    store_w4<W_BF16, SR>(a, o, i, w, zz);
   }
   if constexpr (Q8) {
     // linear codes: absmax of m and sqrt(v); dynamic codes: of m and v
@@ -243,13 +245,12 @@ __global__ __launch_bounds__(256) void optimizer_kernel(const float* __restrict_
     }
   } else if constexpr (B16S) {
     if (valid) {
-      const uint32_t idx0 = (uint32_t)o * (uint32_t)a.in + (uint32_t)i;
       if constexpr (HAS_M)
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.m) + (int64_t)o * a.ldm + i) =
-            pack_bf16x4<SR>(m, rng_stream_base(a.rng_base, 1), idx0);
+            pack_bf16x4<SR>(m, zz, RF_M);
       if constexpr (HAS_V)
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.v) + (int64_t)o * a.ldv + i) =
-            pack_bf16x4<SR>(v, rng_stream_base(a.rng_base, 2), idx0);
+            pack_bf16x4<SR>(v, zz, RF_V);
     }
   } else {
     if (valid) {

@@ -677,19 +677,18 @@ void gemm_kernel(GArgs g, OptArgs a) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) opt_apply<OPT>(gg[j], w[j], m[j], v[j], a.s);
           const uint32_t idx0 = (uint32_t)o * (uint32_t)a.in + (uint32_t)i;
+          uint64_t zz[4];  // one random word per element serves W, m and v
+          rand64x4<SR>(a.rng_base, idx0, zz);
           uint32_t bb[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            bb[j] = SR ? sr_bf16_bits(w[j], rand16_from_base(a.rng_base, idx0 + j)) : rne_bf16_bits(w[j]);
+          for (int j = 0; j < 4; ++j) bb[j] = SR ? sr_bf16_bits(w[j], rand_field(zz[j], RF_W)) : rne_bf16_bits(w[j]);
           __builtin_amdgcn_raw_buffer_store_b64(u32x2{bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16)}, R.W, ow[k], 0,
                                                 FORGE_EPI_ST_CPOL);
           if constexpr (B16S) {
             if constexpr (HAS_M)
-              __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4<SR>(m, rng_stream_base(a.rng_base, 1), idx0), R.m, om[k],
-                                                    0, FORGE_EPI_ST_CPOL);
+              __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4<SR>(m, zz, RF_M), R.m, om[k], 0, FORGE_EPI_ST_CPOL);
             if constexpr (HAS_V)
-              __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4<SR>(v, rng_stream_base(a.rng_base, 2), idx0), R.v,
-                                                    ov_[k], 0, FORGE_EPI_ST_CPOL);
+              __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4<SR>(v, zz, RF_V), R.v, ov_[k], 0, FORGE_EPI_ST_CPOL);
           } else if constexpr (!Q8) {
             if constexpr (HAS_M)
               __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{m[0], m[1], m[2], m[3]}), R.m, om[k], 0,

@@ -48,15 +48,18 @@ __host__ __device__ __forceinline__ uint64_t splitmix64_mix(uint64_t z) {
 __host__ __device__ __forceinline__ uint64_t rng_base(uint64_t seed, uint64_t step) {
   return seed + 0x9E3779B97F4A7C15ull * (step << 32);
 }
-// Independent streams for the bfloat16 write-backs of one element: stream s uses
-// the seed seed + s * 2^62 (W: 0, m: 1, v: 2). For steps below 2^30 the counters of
-// different streams never reach the same SplitMix64 state.
-__host__ __device__ __forceinline__ uint64_t rng_stream_base(uint64_t base, int s) {
-  return base + ((uint64_t)s << 62);
+// The random word of element idx; its 16-bit fields round the element's bfloat16
+// write-backs: bits 48..63 the weight, bits 32..47 the first moment m, bits 16..31
+// the second moment v (one SplitMix64 evaluation serves all three).
+__host__ __device__ __forceinline__ uint64_t rand64_from_base(uint64_t base, uint32_t idx) {
+  return splitmix64_mix(base + 0x9E3779B97F4A7C15ull * ((uint64_t)idx + 1ull));
+}
+enum RandField { RF_W = 0, RF_M = 1, RF_V = 2 };
+__host__ __device__ __forceinline__ uint32_t rand_field(uint64_t z, int field) {
+  return (uint32_t)(z >> (48 - 16 * field)) & 0xFFFFu;
 }
 __host__ __device__ __forceinline__ uint32_t rand16_from_base(uint64_t base, uint32_t idx) {
-  uint64_t z = base + 0x9E3779B97F4A7C15ull * ((uint64_t)idx + 1ull);
-  return (uint32_t)(splitmix64_mix(z) >> 48);
+  return rand_field(rand64_from_base(base, idx), RF_W);
 }
 
 __host__ __device__ __forceinline__ uint32_t f32_bits(float x) {
@@ -175,25 +178,31 @@ __device__ __forceinline__ void bf16x4_to_f32(u32x2 r, float x[4]) {
   x[2] = bits_f32(r.y << 16);
   x[3] = bits_f32(r.y & 0xFFFF0000u);
 }
-// Rounds four consecutive elements (flat index idx0..idx0+3) to bfloat16:
-// stochastically with the r16 of the stream whose base is `base`, or to nearest-even.
+// Rounds four consecutive elements to bfloat16: stochastically with field `field`
+// of their random words z[0..3], or to nearest-even.
 template <bool SR>
-__device__ __forceinline__ u32x2 pack_bf16x4(const float x[4], uint64_t base, uint32_t idx0) {
+__device__ __forceinline__ u32x2 pack_bf16x4(const float x[4], const uint64_t z[4], int field) {
   uint32_t b[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) b[j] = SR ? sr_bf16_bits(x[j], rand16_from_base(base, idx0 + j)) : rne_bf16_bits(x[j]);
+  for (int j = 0; j < 4; ++j) b[j] = SR ? sr_bf16_bits(x[j], rand_field(z[j], field)) : rne_bf16_bits(x[j]);
   return u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
 }
+// The random words of four consecutive elements idx0..idx0+3 (only with stochastic rounding).
+template <bool SR>
+__device__ __forceinline__ void rand64x4(uint64_t base, uint32_t idx0, uint64_t z[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) z[j] = SR ? rand64_from_base(base, idx0 + j) : 0ull;
+}
 
+// Stores four consecutive weights; bf16 weights round with field RF_W of z[0..3].
 template <bool W_BF16, bool SR>
-__device__ __forceinline__ void store_w4(const OptArgs& a, int o, int i, const float w[4]) {
+__device__ __forceinline__ void store_w4(const OptArgs& a, int o, int i, const float w[4], const uint64_t z[4]) {
   if constexpr (W_BF16) {
     uint32_t b[4];
-    const uint32_t idx0 = (uint32_t)o * (uint32_t)a.in + (uint32_t)i;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if constexpr (SR)
-        b[j] = sr_bf16_bits(w[j], rand16_from_base(a.rng_base, idx0 + j));
+        b[j] = sr_bf16_bits(w[j], rand_field(z[j], RF_W));
       else
         b[j] = rne_bf16_bits(w[j]);
     }

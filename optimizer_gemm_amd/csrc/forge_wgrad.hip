@@ -230,7 +230,7 @@ __global__ __launch_bounds__(C::NT) void wgrad_f32_kernel(const void* __restrict
         const float g[4] = {acc[fm][fn].x, acc[fm][fn].y, acc[fm][fn].z, acc[fm][fn].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) opt_apply<OPT>(g[j], w[j], m[j], v[j], a.s);
-        store_w4<false, false>(a, o, i, w);
+        store_w4<false, false>(a, o, i, w, nullptr);
         if constexpr (HAS_M) store_f4(a.m, a.ldm, o, i, m);
         if constexpr (HAS_V) store_f4(a.v, a.ldv, o, i, v);
       }

@@ -204,7 +204,7 @@ def test_validation_errors(f):
     mb, vb = _t(f, Mp, BF16, 128, 256), _t(f, Vp, BF16, 128, 256)
     assert _call_step(f, _t(f, A, F32, 64, 256), _t(f, B, F32, 64, 128), _t(f, C, F32, 128, 256), mb, vb) == -3
     assert _call_step(f, X, dY, W, _t(f, Mp, BF16, 128, 256, ld=260), vb) == -4  # bf16 moment rows of 8
-    assert _call_step(f, X, dY, W, mb, vb, step=1 << 30) == -6                   # bf16 moment streams: step < 2^30
+    assert _call_step(f, X, dY, W, mb, vb, step=1 << 31) == -6                   # step < 2^31
     assert _call_step(f, X, dY, W, _t(f, Mp, I8, 128, 256, scale=S1), v) == -3  # mixed state formats
     assert _call_step(f, X, dY, _t(f, C, F32, 128, 256), m, v) == -3      # W dtype differs from X
     assert _call_step(f, _t(f, A + 2, BF16, 64, 256), dY, W, m, v) == -4  # misaligned pointer
