@@ -65,6 +65,8 @@ def parse():
                         "(W and dgrad stay bf16)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-unfused", action="store_true")
+    p.add_argument("--no-mfma-peak", action="store_true",
+                   help="skip the MFMA-throughput microbenchmark (achieved bf16 peak beside the data-sheet one)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain 1 GiB device copy (3 times) to calibrate HBM byte counters")
     p.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"),
@@ -398,6 +400,14 @@ def main() -> int:
                "sample": f"{spec.name} {n_rows} of {spec.out} output rows x {spec.inn}, T={spec.T}: float64 "
                          f"dgrad + fused-step oracle, median of {reps} ({tcpu:.2f} s each)"}
 
+    # achieved bf16 MFMA rate of this device under full load (outside the timed region)
+    mfma = None
+    if not args.no_mfma_peak and io == "bf16" and not fp8:
+        pk = forge.mfma_peak()
+        mfma = {"tflops": round(pk["tflops"], 1), "unit": "TFLOP/s",
+                "kernel": "back-to-back v_mfma_f32_32x32x16_bf16, register operands, all CUs",
+                "fused_frac": round(fused_tflops / pk["tflops"], 4)}
+
     rec = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -421,6 +431,7 @@ def main() -> int:
         "pct_mfma_peak": round(100.0 * fused_tflops / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(fused_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(fused_tflops / peak, 4), "traffic": traffic},
+        "mfma_peak_measured": mfma,
         "cpu_baseline": cpu,
         "unfused": unfused,
         "resident_bytes": int(resident),

@@ -219,6 +219,21 @@ const char* forge_status_str(int status);
 /* Library ABI version (major*100 + minor). */
 int forge_version(void);
 
+/*
+ * MFMA-throughput microbenchmark (no part of the method; it measures the matrix
+ * cores' achievable bf16 rate for the roofline of the kernels above). Enqueues
+ * n_workgroups workgroups of 256 threads (4 waves); every wave issues 8 * iters
+ * v_mfma_f32_32x32x16_bf16 back to back on four independent accumulator sets with
+ * all elements of A equal to a and of B equal to b (as bfloat16), then writes the
+ * sum of its thread's 64 accumulator values to out[workgroup * 256 + thread]
+ * (out: device float array of n_workgroups * 256 elements, caller-owned), which is
+ * 2048 * iters * bf16(a) * bf16(b) up to float32 summation (exact for a = 1,
+ * b = 2^-10). Requires 1 <= n_workgroups <= 2^20 and 1 <= iters <= 2^24.
+ * forge_mfma_peak_flops gives the floating-point operations of such a launch.
+ */
+int forge_mfma_peak(float* out, int32_t n_workgroups, int32_t iters, float a, float b, forge_stream_t stream);
+double forge_mfma_peak_flops(int32_t n_workgroups, int32_t iters);
+
 #ifdef __cplusplus
 }
 #endif

@@ -74,6 +74,9 @@ def _load() -> ctypes.CDLL:
         "forge_sr_bf16": ([ctypes.c_float, ctypes.c_uint32], ctypes.c_uint16),
         "forge_status_str": ([ctypes.c_int], ctypes.c_char_p),
         "forge_dyn_value": ([ctypes.c_int32, ctypes.c_int32], ctypes.c_float),
+        "forge_mfma_peak": ([ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float,
+                             ctypes.c_void_p], ctypes.c_int),
+        "forge_mfma_peak_flops": ([ctypes.c_int32, ctypes.c_int32], ctypes.c_double),
         "forge_dyn_encode": ([ctypes.c_int32, ctypes.c_float], ctypes.c_int32),
         "forge_version": ([], ctypes.c_int),
     }
@@ -190,6 +193,32 @@ def rand16(seed: int, step: int, idx: int) -> int:
 
 def sr_bf16(x: float, r16: int) -> int:
     return int(_lib.forge_sr_bf16(float(x), int(r16)))
+
+
+def mfma_peak(n_workgroups: Optional[int] = None, iters: int = 4000, reps: int = 5, stream=None) -> Dict[str, float]:
+    """Achieved bf16 MFMA rate of the device (the library's microbenchmark): median
+    TFLOP/s over `reps` timed launches on the current stream, after one warm-up. The
+    outputs are checked exactly (A = 1, B = 2^-10: every thread writes 2 * iters)."""
+    if n_workgroups is None:
+        n_workgroups = 3 * torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    out = torch.empty(n_workgroups * 256, dtype=torch.float32, device="cuda")
+    st = _stream(stream)
+    times = []
+    for r in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rc = _lib.forge_mfma_peak(out.data_ptr(), n_workgroups, iters, 1.0, 2.0 ** -10, st)
+        e1.record()
+        if rc:
+            raise ForgeError(rc, "forge_mfma_peak")
+        torch.cuda.synchronize()
+        if r:
+            times.append(e0.elapsed_time(e1))
+    if not bool(torch.all(out == 2.0 * iters)):
+        raise RuntimeError("forge_mfma_peak: accumulator check failed")
+    ms = sorted(times)[len(times) // 2]
+    flops = _lib.forge_mfma_peak_flops(n_workgroups, iters)
+    return {"tflops": flops / (ms * 1e-3) / 1e12, "ms": ms, "workgroups": n_workgroups, "iters": iters}
 
 
 def dyn_value(is_signed: bool, code: int) -> float:

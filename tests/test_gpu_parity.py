@@ -319,3 +319,13 @@ def test_tensor_parallel_shards_equal_unsharded():
     for got in ((Wr, mr, vr), (Wc, mc, vc)):
         for a, b in zip(got, (Wn, mn, vn)):
             assert np.array_equal(P.host(a), P.host(b))
+
+
+# ---------------------------------------------------------------- MFMA-peak microbenchmark
+def test_mfma_peak_probe_exact_and_plausible():
+    # every thread's accumulator sum is exactly 2 * iters (A = 1, B = 2^-10), and the
+    # measured rate lies between a floor and the data-sheet dense bf16 peak (2.5 PFLOP/s)
+    f = _forge()
+    pk = f.mfma_peak(iters=2000, reps=3)
+    print(f"[mfma peak] {pk}", flush=True)
+    assert 300.0 < pk["tflops"] < 2520.0

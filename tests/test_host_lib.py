@@ -385,3 +385,14 @@ def test_nadam_scalars_at_large_steps(f, psi):
 def test_nadam_negative_momentum_decay_rejected(f):
     with pytest.raises(f.ForgeError):
         f.step_scalars("nadam", dict(momentum_decay=-1e-3), 1)
+
+
+@cpu_only
+def test_mfma_peak_validation(f):
+    lib = f.lib()
+    assert lib.forge_mfma_peak(None, 1, 1, 1.0, 1.0, None) == -1
+    assert lib.forge_mfma_peak(ctypes.c_void_p(0x10000000), 0, 1, 1.0, 1.0, None) == -5
+    assert lib.forge_mfma_peak(ctypes.c_void_p(0x10000000), 1, 0, 1.0, 1.0, None) == -5
+    assert lib.forge_mfma_peak(ctypes.c_void_p(0x10000002), 1, 1, 1.0, 1.0, None) == -4
+    # 2 flops x 32x32x16 per MFMA, 8 MFMAs per iteration and wave, 4 waves per workgroup
+    assert lib.forge_mfma_peak_flops(3, 5) == 2 * 32 * 32 * 16 * 8 * 5 * 4 * 3
