@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from oracle import gemm, optim
-from synth import WORKLOADS, draw_layer_batch, draw_layer_init, f32_from_bf16_bits, sample_rows
+from synth import WORKLOADS, LayerSpec, draw_layer_batch, draw_layer_init, f32_from_bf16_bits, sample_rows
 from tests import _parity as P
 
 pytestmark = pytest.mark.gpu
@@ -126,3 +126,41 @@ def test_qwen14b_mlp_eight_optimizers_ten_steps():
             P.verify_step(opt, X, dY, before, after, hp, t, seed, "bf16", "f32", True, sel, g=g)
         print(f"[ok] qwen mlp step {t}: all eight optimizers", flush=True)
         del Xd, dYd
+
+
+@pytest.mark.timeout(300)
+def test_largest_weight_the_abi_accepts_int8_states_and_dgrad():
+    # W 32760 x 32768 bf16 is 2,146,959,360 bytes, just below the 2^31-byte limit of a
+    # tensor (all kernel addressing is 32-bit buffer offsets; rows stay multiples of 8
+    # elements, and 32760 leaves a ragged last tile row): the fused AdamW step with
+    # INT8 states is checked on sampled rows that include the last ones, and dgrad (which
+    # reads all of W) on sampled tokens and columns, before the step as the method requires.
+    f = _forge()
+    out, inn, T = 32760, 32768, 64
+    spec = LayerSpec("max", out, inn, T)
+    print(f"[case] largest weight {out}x{inn} bf16 ({out * inn * 2} bytes), T={T}, AdamW + INT8 states",
+          flush=True)
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    Wd = (torch.randn(out, inn, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    m, v, ms, vs = f.new_states(Wd, "adamw", "q8")
+    hp = optim.hyper("adamw")
+    seed = 0x5EED_7777
+    sel = np.unique(np.concatenate([sample_rows(77, 0, out, 24), [0, 1, out // 2, out - 2, out - 1]]))
+    cols = np.unique(np.concatenate([np.random.default_rng(3).choice(inn, 24, replace=False), [0, inn - 1]]))
+    for t in (1, 2):
+        X, dY = draw_layer_batch(77, 0, t, spec)
+        Xd, dYd = P.dev_bf16(X), P.dev_bf16(dY)
+        if t == 1:
+            dX = f.dgrad(dYd, Wd)
+            torch.cuda.synchronize()
+            Wcols = P.host(Wd.index_select(1, torch.as_tensor(cols, device="cuda")))
+            ref = f32_from_bf16_bits(dY).astype(np.float64) @ f32_from_bf16_bits(Wcols).astype(np.float64)
+            bad, worst = P.dgrad_bf16_ok(P.host_bits(dX)[:, cols], ref)
+            assert bad == 0, f"dgrad: {bad} sampled dX elements beyond one bf16 ulp (worst {worst:.3g})"
+        before = P.snapshot((Wd, m, v, ms, vs), sel)
+        f.wgrad_step(Xd, dYd, Wd, m, v, "adamw", _gh(hp), t, seed, ms, vs)
+        torch.cuda.synchronize()
+        after = P.snapshot((Wd, m, v, ms, vs), sel)
+        P.verify_step("adamw", X, dY, before, after, hp, t, seed, "bf16", "q8", True, sel)
+        print(f"[ok] largest weight, step {t}", flush=True)
+    del Wd, m, v, ms, vs
