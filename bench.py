@@ -145,7 +145,7 @@ def main() -> int:
     if args.record_traffic:
         return record_traffic(args)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(tensor-parallel shards run the same kernel on each GPU's share)", file=sys.stderr)
         return 2
     import numpy as np

@@ -396,3 +396,13 @@ def test_mfma_peak_validation(f):
     assert lib.forge_mfma_peak(ctypes.c_void_p(0x10000002), 1, 1, 1.0, 1.0, None) == -4
     # 2 flops x 32x32x16 per MFMA, 8 MFMAs per iteration and wave, 4 waves per workgroup
     assert lib.forge_mfma_peak_flops(3, 5) == 2 * 32 * 32 * 16 * 8 * 5 * 4 * 3
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the measurement covers one GPU; asking for more exits with a message before any GPU work
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
