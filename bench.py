@@ -387,7 +387,7 @@ def main() -> int:
         if fp8:
             Xs, dYs, sx, sd = draw_layer_batch_fp8(wl_config, 0, 1, spec, "e4m3", "e5m2")
             fkw = dict(x_fmt="e4m3", dy_fmt="e5m2", x_scale=sx, dy_scale=sd)
-        reps, times = 2, []
+        reps, times = 4, []  # about 10 s of host work on the q_proj layer
         for _ in range(reps):
             c0 = time.perf_counter()
             gemm.dgrad(dYw[:, rows], Ww)  # dX contribution of the sampled rows of W
