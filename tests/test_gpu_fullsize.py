@@ -70,6 +70,16 @@ def test_q_proj_8192_ten_steps():
 
 
 @pytest.mark.timeout(300)
+def test_q_proj_8192_whole_layer_first_step():
+    # every one of the 16.8 M weights and moments of the q_proj layer against the oracle
+    # (the full float64 dY^T X over 8192 tokens), not a sample of rows
+    f = _forge()
+    wl = WORKLOADS["q_proj_8192"]
+    spec = wl.layers[0]
+    _run_layer(f, wl, 1, spec, "adamw", 1, {1}, spec.out)
+
+
+@pytest.mark.timeout(300)
 def test_llama8b_decoder_layer_all_seven_linears():
     f = _forge()
     wl = WORKLOADS["llama8b_layer_8192"]
