@@ -329,3 +329,31 @@ def test_mfma_peak_probe_exact_and_plausible():
     pk = f.mfma_peak(iters=2000, reps=3)
     print(f"[mfma peak] {pk}", flush=True)
     assert 300.0 < pk["tflops"] < 2520.0
+
+
+# ---------------------------------------------------------------- late steps
+@pytest.mark.parametrize("opt,over", [("adamw", {}), ("nadam", {}), ("radam", {}), ("adagrad", {"lr_decay": 1e-3})])
+def test_step_one_hundred_thousand_from_nonzero_moments(opt, over):
+    # one fused step at t = 100000 from seeded non-zero moments: bias corrections near 1,
+    # NAdam's momentum product over 10^5 steps, RAdam in its rectified branch, AdaGrad's
+    # decayed rate — the host scalars and the kernel against the oracle's own formulas
+    f = _forge()
+    spec = LayerSpec("late", 136, 264, 96)
+    t = 100_000
+    print(f"[case] late step t={t} opt={opt}", flush=True)
+    W0 = draw_layer_init(96, 0, spec)
+    X, dY = draw_layer_batch(96, 0, 1, spec)
+    rng = np.random.default_rng(11)
+    m0 = (rng.standard_normal(W0.shape) * 1e-4).astype(np.float32)
+    v0 = (rng.standard_normal(W0.shape) ** 2 * 1e-8 + 1e-12).astype(np.float32)
+    hp = optim.hyper(opt, **over)
+    Wd = P.dev_bf16(W0)
+    slots = optim.SLOTS[opt]
+    m = P.dev(m0) if "m" in slots else None
+    v = P.dev(v0) if "v" in slots else None
+    sel = np.arange(spec.out)
+    before = P.snapshot((Wd, m, v, None, None), sel)
+    f.wgrad_step(P.dev_bf16(X), P.dev_bf16(dY), Wd, m, v, opt, _gpu_hyper(hp), t, 0x5EED_1000)
+    torch.cuda.synchronize()
+    after = P.snapshot((Wd, m, v, None, None), sel)
+    P.verify_step(opt, X, dY, before, after, hp, t, 0x5EED_1000, "bf16", "f32", True, sel)
