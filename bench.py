@@ -54,7 +54,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="q_proj_8192",
                    help="q_proj_8192 | llama8b_layer_8192 | llama8b_tp8_8192 | down_q8_16384 | qwen14b_mlp_4096 | "
-                        "fp32_256 | stack")
+                        "fp32_256 | stack | llama8b_mlp_train_8192 (training steps through autograd)")
+    p.add_argument("--blocks", type=int, default=4,
+                   help="llama8b_mlp_train_8192: number of SwiGLU MLP blocks in the model")
     p.add_argument("--cold-calls", type=int, default=10,
                    help="fused calls of the first layer timed after a 1 GiB write that evicts the memory-side cache")
     p.add_argument("--opt", default="adamw")
@@ -138,6 +140,177 @@ def calibrate_copy() -> int:
     return 0
 
 
+def cpu_baseline(spec, wl_config, opt, io, sr, fp8):
+    """The float64 oracle (dgrad + fused step) timed on the host on a bounded sample of one layer."""
+    import numpy as np
+    from oracle import gemm, optim, step as ostep
+    from synth import draw_layer_batch, draw_layer_batch_fp8, draw_layer_init, f32_from_bf16_bits
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    X, dY = draw_layer_batch(wl_config, 0, 1, spec)
+    W0 = draw_layer_init(wl_config, 0, spec)
+    n_rows = spec.out if spec.P <= 32 * 1024 * 1024 else 1024
+    rows = np.arange(n_rows)
+    hp = optim.hyper(opt)
+    slots = optim.SLOTS[opt]
+    z = np.zeros((n_rows, spec.inn), np.float32)
+    dYw = f32_from_bf16_bits(dY) if io == "bf16" else dY
+    Ww = f32_from_bf16_bits(W0[rows]) if io == "bf16" else W0[rows]
+    fkw, Xs, dYs = {}, X, dY
+    if fp8:
+        Xs, dYs, sx, sd = draw_layer_batch_fp8(wl_config, 0, 1, spec, "e4m3", "e5m2")
+        fkw = dict(x_fmt="e4m3", dy_fmt="e5m2", x_scale=sx, dy_scale=sd)
+    reps, times = 4, []  # about 10 s of host work on the q_proj layer
+    for _ in range(reps):
+        c0 = time.perf_counter()
+        gemm.dgrad(dYw[:, rows], Ww)  # dX contribution of the sampled rows of W
+        ostep.wgrad_step(opt, Xs, dYs, W0[rows], z if "m" in slots else None, z if "v" in slots else None,
+                         hp, 1, 1, io=io, sr=sr, rows=rows, **fkw)
+        times.append(time.perf_counter() - c0)
+    tcpu = float(np.median(times))
+    flops = 4.0 * spec.T * n_rows * spec.inn
+    return {"value": round(flops / tcpu / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{spec.name} {n_rows} of {spec.out} output rows x {spec.inn}, T={spec.T}: float64 "
+                      f"dgrad + fused-step oracle, median of {reps} ({tcpu:.2f} s each)"}
+
+
+TRAIN_WORKLOAD = "llama8b_mlp_train_8192"
+
+
+def train_main(args) -> int:
+    """Training steps through autograd: a model of SwiGLU MLP blocks of Llama-3.1-8B
+    shape (d 4096, hidden 14336; gate, up and down are ForgeLinear layers), 8192 tokens,
+    AdamW with stochastic rounding and float32 moments. One step = forward, backward
+    (dgrad and the fused step per layer) for the fused schedule; forward, backward with
+    the float32 dW stored per layer, then the optimizer pass over every layer for the
+    two-phase schedule. Each schedule runs with and without activation checkpointing
+    (per block); each reports its step time and its peak memory above what the model,
+    its moments and the batch hold."""
+    import numpy as np
+    import torch
+
+    from optimizer_gemm_amd.nn import ForgeLinear, SwiGLUBlock, step_all
+    from synth import LayerSpec
+
+    d, hidden, T, blocks = 4096, 14336, 8192, args.blocks
+    if blocks < 1:
+        print("--blocks must be at least 1", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    opt = args.opt
+    state = args.states or "f32"
+    P = hidden * d                          # weights per linear (all three have hidden x d)
+    n_lin = 3 * blocks
+    step_flops = n_lin * 6.0 * T * P        # forward, dgrad and wgrad GEMMs of every linear
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0x5EED_7000)
+    x = torch.randn(T, d, device=dev, generator=gen).to(torch.bfloat16)
+    G = (torch.randn(T, d, device=dev, generator=gen) * 1e-3).to(torch.bfloat16)
+
+    def run(fused: bool, ckpt: bool):
+        torch.manual_seed(0x5EED_7001)   # same initial weights in every schedule
+        model = torch.nn.Sequential(*[
+            SwiGLUBlock(d, hidden, checkpoint=ckpt, seed=b, fused=fused, device=dev, opt=opt, states=state,
+                        hyper={"stochastic_round": 1}) for b in range(blocks)])
+        xin = x.clone().requires_grad_(True)
+        lins = [m for m in model.modules() if isinstance(m, ForgeLinear)]
+
+        def step():
+            xin.grad = None
+            model(xin).backward(G)
+            if not fused:
+                step_all(model)
+
+        for _ in range(args.warmup):
+            step()
+        xin.grad = None
+        torch.cuda.synchronize()
+        resident = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        if fused:
+            for m in lins:
+                m.timing = []
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - resident
+        ms = e0.elapsed_time(e1) / args.steps
+        calls = [a.elapsed_time(b) for m in lins for (a, b) in (m.timing or [])]
+        for m in lins:
+            m.timing = None
+        # what the training state itself holds: weights, moments (and scales), batch and output gradient
+        state_bytes = sum(t.numel() * t.element_size() for t in list(model.parameters()) + list(model.buffers()))
+        state_bytes += sum(t.numel() * t.element_size() for t in (x, G))
+        out = {"ms_per_step": round(ms, 3), "tflops": round(step_flops / (ms * 1e-3) / 1e12, 2),
+               "peak_above_resident_bytes": int(peak), "model_state_bytes": int(state_bytes),
+               "process_resident_bytes": int(resident)}
+        del model, xin, lins
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        return out, calls
+
+    res = {}
+    fused_calls = []
+    for fused in (True, False):
+        for ckpt in (False, True):
+            name = ("fused" if fused else "two_phase") + ("_ckpt" if ckpt else "")
+            print(f"[bench] training schedule {name}: {blocks} block(s), T={T}", file=sys.stderr, flush=True)
+            r, calls = run(fused, ckpt)
+            res[name] = r
+            if fused and not ckpt:
+                fused_calls = calls
+            print(f"[bench]   {r}", file=sys.stderr, flush=True)
+    floor = n_lin * 4 * P
+    for sfx in ("", "_ckpt"):
+        f, t = res["fused" + sfx], res["two_phase" + sfx]
+        res["speedup" + sfx] = round(t["ms_per_step"] / f["ms_per_step"], 3)
+        # peak = model state + the step's transient peak; the state is the same in both schedules
+        res["peak_reduction" + sfx] = round(1.0 - (f["model_state_bytes"] + f["peak_above_resident_bytes"]) /
+                                            (t["model_state_bytes"] + t["peak_above_resident_bytes"]), 4)
+        res["transient_reduction" + sfx] = round(1.0 - f["peak_above_resident_bytes"] /
+                                                 t["peak_above_resident_bytes"], 4)
+    res["gradient_floor_bytes"] = int(floor)
+
+    call_ms = float(np.mean(fused_calls)) if fused_calls else float("nan")
+    fused_tflops = 2.0 * T * P / (call_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["bf16"]
+    fz = res["fused"]
+    spec = LayerSpec("gate_proj", hidden, d, T)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(spec, 2, opt, "bf16", True, False)
+    rec = {
+        "metric": METRIC,
+        "value": fz["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": fz["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian batch and output gradient; random-init weights)",
+        "config": {"workload": TRAIN_WORKLOAD, "blocks": blocks, "shapes": [f"{hidden}x{d}", f"{d}x{hidden}"],
+                   "tokens": T, "optimizer": opt, "states": state, "stochastic_round": True,
+                   "step": "forward, then backward: dgrad(old W) and the fused wgrad+optimizer per layer "
+                           "(value counts 6*T*out*in per linear: forward, dgrad, wgrad)"},
+        "fused_tflops": round(fused_tflops, 2),
+        "pct_mfma_peak": round(100.0 * fused_tflops / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(fused_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(fused_tflops / peak, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "train_step": res,
+    }
+    print(json.dumps(rec))
+    return 0
+
+
 def main() -> int:
     args = parse()
     if args.calibrate_copy:
@@ -148,6 +321,8 @@ def main() -> int:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(tensor-parallel shards run the same kernel on each GPU's share)", file=sys.stderr)
         return 2
+    if args.workload == TRAIN_WORKLOAD:
+        return train_main(args)
     import numpy as np
     import torch
 
@@ -362,43 +537,7 @@ def main() -> int:
         stack_two_phase = {"ms_per_pass": round(e0.elapsed_time(e1), 3), "peak_transient_bytes": int(floor),
                            "largest_layer_dW_bytes": int(max(4 * s.out * s.inn for s, *_ in per_layer))}
 
-    # --- CPU baseline: the float64 oracle on a bounded sample (first layer) ---
-    cpu = None
-    if not args.no_cpu_baseline:
-        from oracle import gemm, optim, step as ostep
-        from synth import f32_from_bf16_bits
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
-        except Exception:
-            cores = os.cpu_count() or 1
-        spec = layers[0]
-        X, dY = draw_layer_batch(wl_config, 0, 1, spec)
-        W0 = draw_layer_init(wl_config, 0, spec)
-        n_rows = spec.out if spec.P <= 32 * 1024 * 1024 else 1024
-        rows = np.arange(n_rows)
-        hp = optim.hyper(opt)
-        slots = optim.SLOTS[opt]
-        z = np.zeros((n_rows, spec.inn), np.float32)
-        Xw = f32_from_bf16_bits(X) if io == "bf16" else X
-        dYw = f32_from_bf16_bits(dY) if io == "bf16" else dY
-        Ww = f32_from_bf16_bits(W0[rows]) if io == "bf16" else W0[rows]
-        fkw, Xs, dYs = {}, X, dY
-        if fp8:
-            Xs, dYs, sx, sd = draw_layer_batch_fp8(wl_config, 0, 1, spec, "e4m3", "e5m2")
-            fkw = dict(x_fmt="e4m3", dy_fmt="e5m2", x_scale=sx, dy_scale=sd)
-        reps, times = 4, []  # about 10 s of host work on the q_proj layer
-        for _ in range(reps):
-            c0 = time.perf_counter()
-            gemm.dgrad(dYw[:, rows], Ww)  # dX contribution of the sampled rows of W
-            ostep.wgrad_step(opt, Xs, dYs, W0[rows], z if "m" in slots else None, z if "v" in slots else None,
-                             hp, 1, 1, io=io, sr=sr, rows=rows, **fkw)
-            times.append(time.perf_counter() - c0)
-        tcpu = float(np.median(times))
-        flops = 4.0 * spec.T * n_rows * spec.inn
-        cpu = {"value": round(flops / tcpu / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-               "sample": f"{spec.name} {n_rows} of {spec.out} output rows x {spec.inn}, T={spec.T}: float64 "
-                         f"dgrad + fused-step oracle, median of {reps} ({tcpu:.2f} s each)"}
+    cpu = None if args.no_cpu_baseline else cpu_baseline(layers[0], wl_config, opt, io, sr, fp8)
 
     # achieved bf16 MFMA rate of this device under full load (outside the timed region)
     mfma = None

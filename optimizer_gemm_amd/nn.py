@@ -11,12 +11,20 @@ so `weight.grad` stays None and no optimizer.step() follows.
 
 Each backward call is one optimizer step of that layer (a module used several
 times per step, such as a tied embedding, is outside what the method supports).
+
+For comparison the same module runs the usual two-phase schedule with
+fused=False: backward stores the float32 dW (the "gradient floor" every layer
+holds until the optimizer runs) and `step_all(model)` then applies the update
+with the library's stand-alone optimizer pass. Both schedules use the same
+kernels and the same per-element update, so they differ only in when the
+gradient exists and where it lives.
 """
 from __future__ import annotations
 
 from typing import Optional
 
 import torch
+import torch.utils.checkpoint
 
 from . import forge
 
@@ -45,9 +53,25 @@ class _ForgeLinearFn(torch.autograd.Function):
         dx = None
         if ctx.needs_input_grad[0]:
             dx = forge.dgrad(dy2, w.detach()).reshape(x.shape)  # old W, before the update below
+        if not layer.fused:
+            # two-phase schedule: the float32 gradient waits for step_all(); a second
+            # backward before it adds to it, as the usual gradient accumulation does
+            g = forge.wgrad(x2, dy2)
+            if layer.grad32 is None:
+                layer.grad32 = g
+            else:
+                layer.grad32.add_(g)
+            return dx, None, None
         layer._step_count += 1
+        ev = layer.timing
+        if ev is not None:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
         forge.wgrad_step(x2, dy2, w.detach(), layer.m, layer.v, layer.opt, layer.hyper, layer._step_count,
                          layer.seed, layer.m_scale, layer.v_scale, code=layer.code)
+        if ev is not None:
+            e1.record()
+            ev.append((e0, e1))
         return dx, None, None
 
 
@@ -58,12 +82,18 @@ class ForgeLinear(torch.nn.Module):
     layers the pages evaluate). opt / hyper: the optimizer and its
     hyper-parameters (forge_hyper fields). states: "f32", "bf16", "q8" (INT8
     block-64, linear codes) or "q8dyn" (INT8 block-64, dynamic 8-bit code).
+    fused: True for the fused step in backward; False for the two-phase schedule
+    (float32 gradient kept in `grad32`, update applied by `step()`).
+    timing: if a list, each fused call appends its (start, end) CUDA events.
     """
 
     def __init__(self, in_features: int, out_features: int, opt: str = "adamw", hyper: Optional[dict] = None,
                  states: str = "f32", dtype: torch.dtype = torch.bfloat16, device=None, seed: int = 0,
-                 weight: Optional[torch.Tensor] = None):
+                 weight: Optional[torch.Tensor] = None, fused: bool = True):
         super().__init__()
+        self.fused = bool(fused)
+        self.grad32: Optional[torch.Tensor] = None
+        self.timing: Optional[list] = None
         if weight is None:
             weight = torch.empty(out_features, in_features, dtype=dtype, device=device)
             torch.nn.init.normal_(weight, std=0.02)
@@ -86,3 +116,50 @@ class ForgeLinear(torch.nn.Module):
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         return _ForgeLinearFn.apply(x, self.weight, self)
+
+    def step(self) -> None:
+        """Two-phase schedule: apply the optimizer to the stored gradient and free it
+        (nothing to do for a fused layer, whose backward already stepped)."""
+        if self.fused or self.grad32 is None:
+            return
+        self._step_count += 1
+        forge.optimizer_step(self.grad32, self.weight.detach(), self.m, self.v, self.opt, self.hyper,
+                             self._step_count, self.seed, self.m_scale, self.v_scale, code=self.code)
+        self.grad32 = None
+
+
+def step_all(model: torch.nn.Module) -> None:
+    """The optimizer phase of the two-phase schedule for every ForgeLinear in `model`."""
+    for mod in model.modules():
+        if isinstance(mod, ForgeLinear):
+            mod.step()
+
+
+def _rms_norm(x: torch.Tensor, eps: float = 1e-5) -> torch.Tensor:
+    xf = x.float()
+    return (xf * torch.rsqrt(xf.pow(2).mean(-1, keepdim=True) + eps)).to(x.dtype)
+
+
+class SwiGLUBlock(torch.nn.Module):
+    """Residual SwiGLU MLP block of a Llama-style decoder layer built from ForgeLinear:
+    y = x + down(silu(gate(n(x))) * up(n(x))), with n a parameter-free RMS norm.
+    gate / up: [hidden, d] weights, down: [d, hidden]. With checkpoint=True the block
+    keeps only its input for backward and recomputes the rest (activation
+    checkpointing); the recomputation runs before any of the block's layers steps,
+    so it sees the same weights as the forward pass."""
+
+    def __init__(self, d: int, hidden: int, checkpoint: bool = False, seed: int = 0, **kw):
+        super().__init__()
+        self.gate = ForgeLinear(d, hidden, seed=3 * seed, **kw)
+        self.up = ForgeLinear(d, hidden, seed=3 * seed + 1, **kw)
+        self.down = ForgeLinear(hidden, d, seed=3 * seed + 2, **kw)
+        self.checkpoint = checkpoint
+
+    def _body(self, x: torch.Tensor) -> torch.Tensor:
+        h = _rms_norm(x)
+        return x + self.down(torch.nn.functional.silu(self.gate(h)) * self.up(h))
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if self.checkpoint and torch.is_grad_enabled():
+            return torch.utils.checkpoint.checkpoint(self._body, x, use_reentrant=False)
+        return self._body(x)

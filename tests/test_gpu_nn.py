@@ -105,3 +105,114 @@ def test_forge_linear_low_precision_states_match_direct_calls(states):
     assert torch.equal(layer.weight.detach().view(torch.int16), W.view(torch.int16))
     for a, b in ((layer.m, m), (layer.v, v), (layer.m_scale, ms), (layer.v_scale, vs)):
         assert (a is None and b is None) or torch.equal(a, b)
+
+
+def _mlp_model(fused, ckpt, d, hidden, blocks, dev):
+    from optimizer_gemm_amd.nn import SwiGLUBlock
+    torch.manual_seed(21)
+    return torch.nn.Sequential(*[SwiGLUBlock(d, hidden, checkpoint=ckpt, seed=b, fused=fused, device=dev)
+                                 for b in range(blocks)])
+
+
+def _train(model, x, G, steps, fused):
+    from optimizer_gemm_amd.nn import step_all
+    grads = []
+    for _ in range(steps):
+        xin = x.clone().requires_grad_(True)
+        model(xin).backward(G)
+        if not fused:
+            step_all(model)
+        grads.append(xin.grad)
+    torch.cuda.synchronize()
+    return grads
+
+
+def _lin_state(model):
+    from optimizer_gemm_amd.nn import ForgeLinear
+    return [(m.weight.detach().clone(), m.m.clone(), m.v.clone()) for m in model.modules()
+            if isinstance(m, ForgeLinear)]
+
+
+def test_checkpointed_block_equals_plain_block():
+    # activation checkpointing recomputes each block's forward before any of its layers
+    # steps, so weights, moments and the input gradient are bit-identical to the run
+    # that keeps its activations
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(8)
+    T, d, hidden = 192, 256, 640
+    print("[case] SwiGLU blocks, checkpoint on/off", flush=True)
+    x = torch.randn(T, d, device=dev, generator=g).to(torch.bfloat16)
+    G = (torch.randn(T, d, device=dev, generator=g) * 1e-3).to(torch.bfloat16)
+    runs = []
+    for ckpt in (False, True):
+        model = _mlp_model(True, ckpt, d, hidden, 2, dev)
+        grads = _train(model, x, G, 3, True)
+        runs.append((_lin_state(model), grads))
+    (s0, g0), (s1, g1) = runs
+    for (w0, m0, v0), (w1, m1, v1) in zip(s0, s1):
+        assert torch.equal(w0.view(torch.int16), w1.view(torch.int16))
+        assert torch.equal(m0, m1) and torch.equal(v0, v1)
+    for a, b in zip(g0, g1):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_two_phase_schedule_matches_fused():
+    # the two-phase schedule (float32 dW stored in backward, optimizer pass afterwards)
+    # and the fused one apply the same update: at step 1 bit for bit up to the SR flips the
+    # tolerance of the unfused comparison allows, and the step-1 input gradients are equal
+    from optimizer_gemm_amd.nn import ForgeLinear
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(9)
+    T, d, hidden = 160, 256, 512
+    print("[case] SwiGLU block, fused vs two-phase", flush=True)
+    x = torch.randn(T, d, device=dev, generator=g).to(torch.bfloat16)
+    G = (torch.randn(T, d, device=dev, generator=g) * 1e-3).to(torch.bfloat16)
+    res = []
+    for fused in (True, False):
+        model = _mlp_model(fused, False, d, hidden, 1, dev)
+        grads = _train(model, x, G, 1, fused)
+        lins = [m for m in model.modules() if isinstance(m, ForgeLinear)]
+        assert all(m.weight.grad is None and m.grad32 is None and m.step_count == 1 for m in lins)
+        res.append((_lin_state(model), grads))
+    (sf, gf), (st, gt) = res
+    assert torch.equal(gf[0].view(torch.int16), gt[0].view(torch.int16))
+    for (wf, mf, vf), (wt, mt, vt) in zip(sf, st):
+        ok, n, mx = P.bf16_sr_ok(P.host_bits(wf), P.host_bits(wt))
+        assert ok, (n, mx)
+        assert P.state_ok(P.host(mf), P.host(mt), rel=1e-6)[0] == 0
+        assert P.state_ok(P.host(vf), P.host(vt), rel=1e-6)[0] == 0
+
+
+def test_two_phase_peak_memory_holds_the_gradient_floor():
+    # the two-phase step holds the float32 gradients of every layer (4 bytes per weight) at
+    # once at the end of backward, when the activations are already freed; the fused
+    # schedule never allocates them, so its peak is the activations and input gradients
+    from optimizer_gemm_amd.nn import step_all
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(10)
+    T, d, hidden, blocks = 256, 1024, 2816, 2
+    print("[case] SwiGLU blocks, peak memory fused vs two-phase", flush=True)
+    x = torch.randn(T, d, device=dev, generator=g).to(torch.bfloat16)
+    G = (torch.randn(T, d, device=dev, generator=g) * 1e-3).to(torch.bfloat16)
+    peaks = {}
+    for fused in (True, False):
+        model = _mlp_model(fused, False, d, hidden, blocks, dev)
+        xin = x.clone().requires_grad_(True)
+        # one step first: the first GEMMs of a process allocate library workspaces
+        model(xin).backward(G)
+        if not fused:
+            step_all(model)
+        xin.grad = None
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        model(xin).backward(G)
+        if not fused:
+            step_all(model)
+        torch.cuda.synchronize()
+        peaks[fused] = torch.cuda.max_memory_allocated() - base
+        del model, xin
+        torch.cuda.empty_cache()
+    floor = blocks * 3 * 4 * d * hidden
+    assert peaks[False] >= floor, (peaks, floor)
+    assert peaks[True] < 0.35 * floor, (peaks, floor)

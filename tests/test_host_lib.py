@@ -406,3 +406,13 @@ def test_bench_refuses_more_than_one_gpu():
                        timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_bench_training_workload_rejects_empty_model():
+    # the training-step workload checks its block count before any GPU work
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "llama8b_mlp_train_8192",
+                        "--blocks", "0"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "--blocks" in r.stderr
