@@ -494,7 +494,13 @@ def main() -> int:
         e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
               torch.cuda.Event(enable_timing=True)) for _ in range(n_rep)]
         f_e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_rep)]
+        # a spin kernel keeps the GPU busy while the host enqueues each repetition, so the
+        # event pairs time the kernels and not the host's launch latency (which dominates
+        # on launch-bound layers)
+        hold = getattr(torch.cuda, "_sleep", None)
         for r in range(n_rep):
+            if hold is not None:
+                hold(1_000_000)
             f_e[r][0].record()
             wstep(X, dY, W, m, v, opt, hyper, 10_002 + r, seed, ms, vs, **sc)
             f_e[r][1].record()
