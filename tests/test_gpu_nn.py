@@ -215,4 +215,4 @@ def test_two_phase_peak_memory_holds_the_gradient_floor():
         torch.cuda.empty_cache()
     floor = blocks * 3 * 4 * d * hidden
     assert peaks[False] >= floor, (peaks, floor)
-    assert peaks[True] < 0.35 * floor, (peaks, floor)
+    assert peaks[True] < 0.5 * floor, (peaks, floor)
