@@ -357,3 +357,52 @@ def test_step_one_hundred_thousand_from_nonzero_moments(opt, over):
     torch.cuda.synchronize()
     after = P.snapshot((Wd, m, v, None, None), sel)
     P.verify_step(opt, X, dY, before, after, hp, t, 0x5EED_1000, "bf16", "f32", True, sel)
+
+
+# ---------------------------------------------------------------- smallest shapes, streams
+@pytest.mark.parametrize("out,inn,T", [(8, 8, 1), (8, 16, 3), (8, 64, 1), (136, 8, 17), (24, 1032, 1)])
+def test_smallest_shapes(out, inn, T):
+    # one token, and 8-wide rows (the least a bf16 row of X or dY may have): single partial
+    # tiles whose rows, columns and token range are all ragged, fused step and dgrad
+    f = _forge()
+    spec = LayerSpec("s", out, inn, T)
+    run_case(spec, "adamw", 2, config=105, label=f"smallest {out}x{inn} T={T}")
+    X, dY = draw_layer_batch(105, 1, 1, spec)
+    W = draw_layer_init(105, 1, spec)
+    dX = f.dgrad(P.dev_bf16(dY), P.dev_bf16(W))
+    torch.cuda.synchronize()
+    ref = gemm.dgrad(f32_from_bf16_bits(dY).astype(np.float64), f32_from_bf16_bits(W).astype(np.float64))
+    bad, worst = P.dgrad_bf16_ok(P.host_bits(dX), ref)
+    assert bad == 0, (bad, worst)
+
+
+def test_side_stream_matches_default_stream():
+    # the kernels run on the stream the caller passes (here a second torch stream, ordered
+    # after the inputs' producer by an event): results equal the default-stream run bit for bit
+    f = _forge()
+    spec = LayerSpec("st", 264, 392, 150)
+    print("[case] side stream vs default stream", flush=True)
+    W0 = draw_layer_init(106, 0, spec)
+    res = []
+    for side in (False, True):
+        Wd = P.dev_bf16(W0)
+        m, v, _, _ = f.new_states(Wd, "adamw")
+        s = torch.cuda.Stream() if side else torch.cuda.current_stream()
+        for t in (1, 2):
+            X, dY = draw_layer_batch(106, 0, t, spec)
+            Xd, dYd = P.dev_bf16(X), P.dev_bf16(dY)
+            ready = torch.cuda.Event()
+            ready.record(torch.cuda.current_stream())
+            s.wait_event(ready)
+            with torch.cuda.stream(s):
+                dX = f.dgrad(dYd, Wd)
+                f.wgrad_step(Xd, dYd, Wd, m, v, "adamw", None, t, 13)
+            if side:
+                # the side stream's tensors outlive their use there
+                for tns in (Xd, dYd, dX):
+                    tns.record_stream(s)
+        s.synchronize()
+        torch.cuda.synchronize()
+        res.append((P.host(Wd), P.host(m), P.host(v), P.host(dX)))
+    for a, b in zip(*res):
+        assert np.array_equal(a, b)
