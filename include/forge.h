@@ -162,10 +162,10 @@ int32_t forge_dyn_encode(int32_t is_signed, float y);
  * 1 <= step < 2^31.
  * T == 0 is allowed (zero gradient). Requires out*in < 2^32.
  * FP8 inputs (the pages' outlook, §5): X FORGE_E4M3 and dY FORGE_E4M3 or
- * FORGE_E5M2, each with its scale (see forge_tensor), with W FORGE_BF16 and
- * float32 or bfloat16 m, v; cols and ld of X and dY must be multiples of 16 (else
- * FORGE_ERR_ALIGN); INT8 moments with FP8 inputs return FORGE_ERR_UNSUPPORTED. The
- * gradient is (sum over tokens of the decoded code products) * scale_X * scale_dY.
+ * FORGE_E5M2, each with its scale (see forge_tensor), with W FORGE_BF16 and m, v
+ * in any of the moment formats above; cols and ld of X and dY must be multiples of
+ * 16 (else FORGE_ERR_ALIGN). The gradient is (sum over tokens of the decoded code
+ * products) * scale_X * scale_dY.
  * Must be enqueued after forge_linear_dgrad of the same layer (which reads the old W).
  */
 int forge_linear_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge_tensor* W,

@@ -335,7 +335,6 @@ int forge_linear_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge
   if (X->rows != dY->rows || X->cols != W->cols || dY->cols != W->rows) return FORGE_ERR_SHAPE;
   const int fmt = check_states(opt, io, W, m, v);
   if (fmt < 0) return fmt;
-  if (f8 && (fmt == ST_Q8 || fmt == ST_Q8D)) return FORGE_ERR_UNSUPPORTED;
   if (W->rows * W->cols >= ((int64_t)1 << 32)) return FORGE_ERR_UNSUPPORTED;
   const int sl = opt_slots(opt);
   if (!fits_31(X) || !fits_31(dY) || !fits_31(W) || ((sl & 1) && !fits_31(m)) || ((sl & 2) && !fits_31(v)))

@@ -885,12 +885,10 @@ hipError_t wgrad_fused_bf16_opt(int sf, int sr, const GArgs& g, const OptArgs& a
 // optimizer, and the float32 dW store (instantiated in forge_gemm_f8_*.hip).
 template <class C, int OPT>
 static hipError_t g_launch_opt_f8(int sf, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
-  if (sf == ST_BF16)
-    return sr ? g_launch<C, G_EPI_OPT, OPT, ST_BF16, true>(g, a, st) : g_launch<C, G_EPI_OPT, OPT, ST_BF16, false>(g, a, st);
-  return sr ? g_launch<C, G_EPI_OPT, OPT, ST_F32, true>(g, a, st) : g_launch<C, G_EPI_OPT, OPT, ST_F32, false>(g, a, st);
+  return g_launch_opt<C, OPT>(sf, sr, g, a, st);
 }
 
-// sf: ST_F32 or ST_BF16 (INT8 moments are not offered with FP8 inputs)
+// sf: any moment format (float32, bfloat16, INT8 linear or dynamic codes)
 template <int OPT, int FB>
 hipError_t wgrad_fused_f8_opt(int sf, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
   return g_pick<WgradF8Big<FB>, WgradF8Small<FB>, WgradF8Small<FB>, WgradF8Small<FB>>(

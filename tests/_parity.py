@@ -233,6 +233,53 @@ def state_envelope_ok(opt, slot, got, X, dY, W_b, m_b, v_b, hp, t, seed, sel, fp
     return int(bad.sum()), float(np.max(over / np.maximum(tol, 1e-300))) if r.size else 0.0
 
 
+def scale_envelope_ok(opt, slot, got, X, dY, W_b, m_b, v_b, ms_b, vs_b, hp, t, seed, sel, fp8, ref, delta,
+                      state, n_samples=9):
+    """(n_bad, worst): INT8 block scales of moment `slot` with FP8 inputs. A block
+    scale is a non-decreasing function of the block's largest magnitude, so it lies
+    between the scales of the elementwise smallest and largest magnitudes the
+    oracle's unquantised moment takes over gradients in [g - delta, g + delta]
+    (sampled, plus the point nearest zero); widened by the tolerance of state_ok."""
+    from oracle import step as ostep
+    g0 = ref["g"]
+    lo = hi = None
+    for s in list(np.linspace(-1.0, 1.0, n_samples)) + [None]:
+        g = g0 + s * delta if s is not None else np.sign(g0) * np.maximum(np.abs(g0) - delta, 0.0)
+        out = _oracle_rows(opt, X, dY, W_b, m_b, v_b, hp, t, seed, "bf16", state, sel, ms_b, vs_b, g, fp8)
+        a = np.abs(np.asarray(out[slot + "64"], np.float64))
+        lo = a if lo is None else np.minimum(lo, a)
+        hi = a if hi is None else np.maximum(hi, a)
+    s_lo = np.asarray(ostep.store_state(slot, lo, state)[1], np.float64)
+    s_hi = np.asarray(ostep.store_state(slot, hi, state)[1], np.float64)
+    r = np.asarray(ref[slot + "_scale"], np.float64)
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    tol = 1e-4 * np.maximum(np.abs(r), 0.1 * rms)
+    got = np.asarray(got, np.float64)
+    over = np.maximum(s_lo - tol - got, got - s_hi - tol)
+    return int((over > 0).sum()), float(np.max(over / np.maximum(tol, 1e-300))) if r.size else 0.0
+
+
+def codes_envelope_ok(opt, slot, got, X, dY, W_b, m_b, v_b, ms_b, vs_b, hp, t, seed, sel, fp8, ref, delta,
+                      state, n_samples=9):
+    """(n_bad, worst): INT8 codes of moment `slot` with FP8 inputs, each within one
+    code (in value order) of the codes the oracle stores over gradients in
+    [g - delta, g + delta] (sampled, plus the point nearest zero). The dynamic code
+    is dense near zero, so an error inside the FP8 bound can span several codes there."""
+    from oracle import q8
+    rank = (lambda c: q8.dyn_rank(c, slot == "m")) if state == "q8dyn" else (lambda c: np.asarray(c, np.int64))
+    g0 = ref["g"]
+    lo = hi = None
+    for s in list(np.linspace(-1.0, 1.0, n_samples)) + [None]:
+        g = g0 + s * delta if s is not None else np.sign(g0) * np.maximum(np.abs(g0) - delta, 0.0)
+        out = _oracle_rows(opt, X, dY, W_b, m_b, v_b, hp, t, seed, "bf16", state, sel, ms_b, vs_b, g, fp8)
+        c = rank(out[slot])
+        lo = c if lo is None else np.minimum(lo, c)
+        hi = c if hi is None else np.maximum(hi, c)
+    r = rank(got)
+    over = np.maximum(lo - 1 - r, r - hi - 1)
+    return int((over > 0).sum()), int(over.max()) if over.size else 0
+
+
 def snapshot(tensors, sel):
     """Host copies of the selected rows of (W, m, v, m_scale, v_scale) (None stays None)."""
     out, idx = [], None
@@ -277,7 +324,7 @@ def verify_step(opt, X, dY, before, after, hp, t, seed, io, state, sr, sel, g=No
             print(f"[bf16 {slot}] step {t}: {n} of {got.size} differ, {unexplained} unexplained", flush=True)
             assert ok, (f"step {t}: {n} of {got.size} bf16 {slot} values differ, {unexplained} not explained "
                         f"by a rounding boundary or the gradient error bound: {detail}")
-        elif fp8 is not None:
+        elif fp8 is not None and state == "f32":
             bad, worst = state_envelope_ok(opt, slot, got, X, dY, W_b, m_b, v_b, hp, t, seed, sel, fp8, ref, delta)
             assert bad == 0, (f"step {t}: {slot}: {bad} elements outside the FP8 gradient envelope "
                               f"(worst {worst:.3g}x the fp32 tolerance beyond it)")
@@ -285,13 +332,20 @@ def verify_step(opt, X, dY, before, after, hp, t, seed, io, state, sr, sel, g=No
             bad, worst = state_ok(got, ref[slot])
             assert bad == 0, f"step {t}: {slot}: {bad} elements out of tolerance (worst {worst:.3g}x)"
         else:
-            if state == "q8dyn":
+            if fp8 is not None:
+                big, _ = codes_envelope_ok(opt, slot, got, X, dY, W_b, m_b, v_b, ms_b, vs_b, hp, t, seed, sel,
+                                           fp8, ref, delta, state)
+            elif state == "q8dyn":
                 # dynamic codes: compare positions in value order (adjacent code values)
                 from oracle import q8
                 big, nd, mx = codes_ok(q8.dyn_rank(got, slot == "m"), q8.dyn_rank(ref[slot], slot == "m"))
             else:
                 big, nd, mx = codes_ok(got, ref[slot])
             assert big == 0, f"step {t}: {slot} codes: {big} off by more than one step"
-            bad, worst = state_ok(gs, ref[slot + "_scale"])
+            if fp8 is not None:
+                bad, worst = scale_envelope_ok(opt, slot, gs, X, dY, W_b, m_b, v_b, ms_b, vs_b, hp, t, seed, sel,
+                                               fp8, ref, delta, state)
+            else:
+                bad, worst = state_ok(gs, ref[slot + "_scale"])
             assert bad == 0, f"step {t}: {slot} scales: {bad} out of tolerance (worst {worst:.3g}x)"
     return ref

@@ -45,15 +45,16 @@ def run_fp8_case(spec, opt, steps, dy_fmt="e5m2", config=120, layer=0, sr=True, 
     hp = optim.hyper(opt, **(hp_over or {}))
     seed = (0x5EED0000 + config) ^ layer
     Wd = P.dev_bf16(draw_layer_init(config, layer, spec))
-    m, v, _, _ = f.new_states(Wd, opt, state)
+    m, v, ms, vs = f.new_states(Wd, opt, state)
     sel = np.arange(spec.out) if rows is None else np.asarray(rows)
     for t in range(1, steps + 1):
         Xq, dYq, sx, sd = draw_layer_batch_fp8(config, layer, t, spec, "e4m3", dy_fmt)
-        before = P.snapshot((Wd, m, v, None, None), sel)
+        before = P.snapshot((Wd, m, v, ms, vs), sel)
         f.wgrad_step(dev_fp8(Xq, "e4m3"), dev_fp8(dYq, dy_fmt), Wd, m, v, opt, _gpu_hyper(hp, sr), t, seed,
-                     x_scale=dev_scale(sx), dy_scale=dev_scale(sd))
+                     m_scale=ms, v_scale=vs, x_scale=dev_scale(sx), dy_scale=dev_scale(sd),
+                     code=P.state_code(state))
         torch.cuda.synchronize()
-        after = P.snapshot((Wd, m, v, None, None), sel)
+        after = P.snapshot((Wd, m, v, ms, vs), sel)
         P.verify_step(opt, Xq, dYq, before, after, hp, t, seed, "bf16", state, sr, sel,
                       fp8=("e4m3", dy_fmt, sx, sd))
     return Wd, m, v
@@ -75,6 +76,26 @@ def test_fp8_e4m3_gradients(opt):
 def test_fp8_with_bf16_states(opt):
     run_fp8_case(LayerSpec("f8", 208, 336, 130), opt, 2, "e5m2", config=129, label="fp8 + bf16 states",
                  state="bf16")
+
+
+@pytest.mark.parametrize("state", ["q8", "q8dyn"])
+@pytest.mark.parametrize("opt", ["adamw", "lion", "rmsprop", "sgd_momentum", "nadam"])
+def test_fp8_with_int8_states(opt, state):
+    # FP8 inputs with INT8 block-64 moments (linear or dynamic codes): 208 = 128 + 80 rows,
+    # 320 = 2 * 128 + 64 columns (whole 64-element blocks), 130 tokens, outlier rows
+    run_fp8_case(LayerSpec("f8", 208, 320, 130, outlier_frac=0.01), opt, 3, "e5m2", config=131,
+                 label=f"fp8 + {state} states", state=state)
+
+
+@pytest.mark.parametrize("cfg", ["big", "small"])
+def test_fp8_int8_states_each_tile_configuration(cfg):
+    # the 256x256 FP8 tiles run one wave per SIMD, so their INT8 epilogue takes the deeper
+    # load batches; both FP8 tile configurations, row-sampled at full width
+    sh = _tile_config_shapes()
+    n_in, n_out = sh[cfg]
+    rows = np.unique(np.concatenate([np.arange(0, n_out, max(1, n_out // 64)), [n_out - 1]]))
+    run_fp8_case(LayerSpec("c", n_out, n_in, 200), "adamw", 2, "e5m2", config=132, rows=rows,
+                 label=f"fp8 + q8 tile config {cfg}", state="q8")
 
 
 def test_fp8_round_to_nearest_and_outliers():

@@ -263,8 +263,8 @@ def test_fp8_validation_errors(f):
     assert _call_step(f, _t(f, A + 8, E4M3, 64, 256, scale=SX), dY, W, m, v) == -4      # 16-byte base
     assert _call_step(f, _t(f, A, E4M3, 64, 256, scale=SX + 2), dY, W, m, v) == -4      # float scale alignment
     assert _call_step(f, X, _t(f, B, E5M2, 63, 128, scale=SD), W, m, v) == -2   # T mismatch
-    assert _call_step(f, X, dY, W, _t(f, Mp, I8, 128, 256, scale=S1),
-                      _t(f, Vp, U8, 128, 256, scale=S2)) == -5                   # no INT8 states with FP8
+    assert _call_step(f, X, dY, W, _t(f, Mp, I8, 128, 256),
+                      _t(f, Vp, U8, 128, 256, scale=S2)) == -1                   # INT8 m with FP8: needs its scales
     r = lambda x: ctypes.byref(x)  # noqa: E731
     lib = f.lib()
     assert lib.forge_linear_dgrad(r(_t(f, B, E4M3, 64, 128, scale=SD)), r(W), r(_t(f, A, BF16, 64, 256)),
@@ -336,7 +336,8 @@ def test_dyn_state_validation(f):
     one = 0x78000000
     X8 = _t(f, A, E4M3, 64, 256, scale=one)
     dY8 = _t(f, B, E4M3, 64, 128, scale=one + 256)
-    assert _call_step(f, X8, dY8, W, dm, dv) == -5                                  # not with FP8 inputs
+    assert _call_step(f, X8, dY8, W, dm, _t(f, Vp, U8, 128, 256, scale=S2)) == -3   # mixed codes, FP8 inputs
+    assert _call_step(f, X8, dY8, W, _t(f, Mp, I8D, 128, 256), dv) == -1             # scales, FP8 inputs
 
 
 def test_dyn_fast_encoder_exhaustive(tmp_path):

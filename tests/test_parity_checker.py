@@ -6,6 +6,7 @@ update is ill-conditioned in the gradient (g ~ 0 under an adaptive optimizer),
 and reject the same change at an ordinary element or too many changed elements.
 """
 import numpy as np
+import pytest
 
 from oracle import optim, step
 from synth import LayerSpec, draw_layer_batch, draw_layer_init
@@ -167,3 +168,29 @@ def test_fp8_bound_holds_for_the_alignment_model_and_catches_a_dropped_token():
     ok, n, unexp, _ = P.bf16_step_explained(w_drop, ref_s, "sgd", Xq, dYq, W, None, None, hp2, 1, 77, "bf16", "f32",
                                             sel, fp8=fp8, delta=bound, frac=P.FP8_FLIP_FRAC)
     assert not ok and unexp > 0
+
+
+@pytest.mark.parametrize("state", ["q8", "q8dyn"])
+def test_fp8_int8_code_and_scale_envelopes(state):
+    # INT8 moments with FP8 inputs: codes and block scales from the alignment model's
+    # gradient pass the envelope checks; those from a gradient missing one token do not
+    spec, W, Xq, dYq, fp8, hp, z, _, kw = _fp8_case()
+    sel = np.arange(spec.out)
+    zeros = np.zeros(W.shape)
+    m0, ms0 = step.store_state("m", zeros, state)
+    v0, vs0 = step.store_state("v", zeros, state)
+    skw = dict(state=state, m_scale=ms0, v_scale=vs0, **kw)
+    ref = step.wgrad_step("adamw", Xq, dYq, W, m0, v0, hp, 1, 77, **skw)
+    bound = P.fp8_grad_bound(Xq, dYq, fp8, sel, ref["g"])
+    from oracle import fp8 as ofp8
+    Xw, dYw = ofp8.dequant(Xq, "e4m3", fp8[2]), ofp8.dequant(dYq, "e5m2", fp8[3])
+    g_hw = _truncated_block_sums(Xq, dYq, fp8)
+    g_drop = ref["g"] - np.outer(dYw[7], Xw[7])
+    args = (Xq, dYq, W, m0, v0, ms0, vs0, hp, 1, 77, sel, fp8, ref, bound, state)
+    hw = step.wgrad_step("adamw", Xq, dYq, W, m0, v0, hp, 1, 77, g=g_hw, **skw)
+    drop = step.wgrad_step("adamw", Xq, dYq, W, m0, v0, hp, 1, 77, g=g_drop, **skw)
+    for slot in ("m", "v"):
+        assert P.codes_envelope_ok("adamw", slot, hw[slot], *args)[0] == 0
+        assert P.scale_envelope_ok("adamw", slot, hw[slot + "_scale"], *args)[0] == 0
+        assert P.codes_envelope_ok("adamw", slot, drop[slot], *args)[0] > 0
+        assert P.scale_envelope_ok("adamw", slot, drop[slot + "_scale"], *args)[0] > 0
