@@ -532,8 +532,13 @@ void gemm_kernel(GArgs g, OptArgs a) {
     };
     for (int st = 0; st < nstr; st += C::NSTAGE)
       static_for<0, C::NSTAGE>([&](auto r_c) { stage(r_c, st + decltype(r_c)::value); });
-    // the loads issued past the end still write LDS: let them land before it is reused
+    // the loads issued past the end still write LDS: let them land before it is reused.
+    // The last k-step also read fragments that nothing consumes: the compiler takes
+    // their registers as free once the reads are issued, so both sets stay pinned
+    // until those reads have landed, else a later value placed there is overwritten.
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    settle(F0);
+    settle(F1);
 
     // ---- epilogue ----
     // The finished tile is handed through LDS one wave-column (TN rows of n) at a
@@ -875,8 +880,14 @@ static hipError_t g_launch_opt(int sf, int sr, const GArgs& g, const OptArgs& a,
   }
 }
 
+#ifndef FORGE_Q8_SMALL
+#define FORGE_Q8_SMALL 0
+#endif
 template <int OPT>
 hipError_t wgrad_fused_bf16_opt(int sf, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
+  if (FORGE_Q8_SMALL && (sf == ST_Q8 || sf == ST_Q8D))
+    return g_pick<WgradSmall, WgradSmall, WgradSplit, WgradSmall>(
+        g, [&](auto c, const GArgs& gc) { return g_launch_opt<decltype(c), OPT>(sf, sr, gc, a, st); });
   return g_pick<WgradBig, WgradSmall, WgradSplit, WgradBand>(
       g, [&](auto c, const GArgs& gc) { return g_launch_opt<decltype(c), OPT>(sf, sr, gc, a, st); });
 }
@@ -891,6 +902,9 @@ static hipError_t g_launch_opt_f8(int sf, int sr, const GArgs& g, const OptArgs&
 // sf: any moment format (float32, bfloat16, INT8 linear or dynamic codes)
 template <int OPT, int FB>
 hipError_t wgrad_fused_f8_opt(int sf, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
+  if (FORGE_Q8_SMALL && (sf == ST_Q8 || sf == ST_Q8D))
+    return g_pick<WgradF8Small<FB>, WgradF8Small<FB>, WgradF8Small<FB>, WgradF8Small<FB>>(
+        g, [&](auto c, const GArgs& gc) { return g_launch_opt_f8<decltype(c), OPT>(sf, sr, gc, a, st); });
   return g_pick<WgradF8Big<FB>, WgradF8Small<FB>, WgradF8Small<FB>, WgradF8Small<FB>>(
       g, [&](auto c, const GArgs& gc) { return g_launch_opt_f8<decltype(c), OPT>(sf, sr, gc, a, st); });
 }
