@@ -880,14 +880,8 @@ static hipError_t g_launch_opt(int sf, int sr, const GArgs& g, const OptArgs& a,
   }
 }
 
-#ifndef FORGE_Q8_SMALL
-#define FORGE_Q8_SMALL 0
-#endif
 template <int OPT>
 hipError_t wgrad_fused_bf16_opt(int sf, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
-  if (FORGE_Q8_SMALL && (sf == ST_Q8 || sf == ST_Q8D))
-    return g_pick<WgradSmall, WgradSmall, WgradSplit, WgradSmall>(
-        g, [&](auto c, const GArgs& gc) { return g_launch_opt<decltype(c), OPT>(sf, sr, gc, a, st); });
   return g_pick<WgradBig, WgradSmall, WgradSplit, WgradBand>(
       g, [&](auto c, const GArgs& gc) { return g_launch_opt<decltype(c), OPT>(sf, sr, gc, a, st); });
 }
@@ -902,9 +896,6 @@ static hipError_t g_launch_opt_f8(int sf, int sr, const GArgs& g, const OptArgs&
 // sf: any moment format (float32, bfloat16, INT8 linear or dynamic codes)
 template <int OPT, int FB>
 hipError_t wgrad_fused_f8_opt(int sf, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
-  if (FORGE_Q8_SMALL && (sf == ST_Q8 || sf == ST_Q8D))
-    return g_pick<WgradF8Small<FB>, WgradF8Small<FB>, WgradF8Small<FB>, WgradF8Small<FB>>(
-        g, [&](auto c, const GArgs& gc) { return g_launch_opt_f8<decltype(c), OPT>(sf, sr, gc, a, st); });
   return g_pick<WgradF8Big<FB>, WgradF8Small<FB>, WgradF8Small<FB>, WgradF8Small<FB>>(
       g, [&](auto c, const GArgs& gc) { return g_launch_opt_f8<decltype(c), OPT>(sf, sr, gc, a, st); });
 }
