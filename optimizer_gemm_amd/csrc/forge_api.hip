@@ -133,19 +133,31 @@ int check_states(int opt, int io_dtype, const forge_tensor* W, const forge_tenso
   return fmt < 0 ? ST_F32 : fmt;
 }
 
+// Byte range of a tensor's scale: the [rows, cols / 64] float32 block scales of an INT8
+// state, the one float32 dequantisation scale of an FP8 input; empty otherwise.
+Range scale_range_of(const forge_tensor* t) {
+  const uintptr_t lo = (uintptr_t)t->scale;
+  if (!t->scale) return Range{0, 0};
+  if (is_fp8(t->dtype)) return Range{lo, lo + 4};
+  if (t->dtype == FORGE_I8 || t->dtype == FORGE_U8 || t->dtype == FORGE_I8_DYN || t->dtype == FORGE_U8_DYN)
+    return Range{lo, lo + (uintptr_t)(t->rows * (t->cols / 64) * 4)};
+  return Range{0, 0};
+}
+
+// Everything an output writes (its data and block scales) must overlap nothing else the
+// call reads or writes: other outputs' data and scales, inputs' data and scales.
 int check_alias(const forge_tensor* const* outs, int n_out, const forge_tensor* const* ins, int n_in) {
   for (int a = 0; a < n_out; ++a) {
     if (!outs[a]) continue;
-    const Range ra = range_of(outs[a]);
-    for (int b = a + 1; b < n_out; ++b)
-      if (outs[b] && overlap(ra, range_of(outs[b]))) return FORGE_ERR_ALIAS;
-    for (int b = 0; b < n_in; ++b)
-      if (ins[b] && overlap(ra, range_of(ins[b]))) return FORGE_ERR_ALIAS;
-    if (outs[a]->scale) {
-      const int64_t nb = outs[a]->rows * (outs[a]->cols / 64) * 4;
-      const Range rs{(uintptr_t)outs[a]->scale, (uintptr_t)outs[a]->scale + (uintptr_t)nb};
-      for (int b = 0; b < n_out; ++b)
-        if (outs[b] && overlap(rs, range_of(outs[b]))) return FORGE_ERR_ALIAS;
+    const Range wa[2] = {range_of(outs[a]), scale_range_of(outs[a])};
+    for (const Range& ra : wa) {
+      for (int b = 0; b < n_out; ++b) {
+        if (!outs[b]) continue;
+        if (b != a && overlap(ra, range_of(outs[b]))) return FORGE_ERR_ALIAS;
+        if (overlap(ra, scale_range_of(outs[b])) && !(b == a && &ra == &wa[1])) return FORGE_ERR_ALIAS;
+      }
+      for (int b = 0; b < n_in; ++b)
+        if (ins[b] && (overlap(ra, range_of(ins[b])) || overlap(ra, scale_range_of(ins[b])))) return FORGE_ERR_ALIAS;
     }
   }
   return FORGE_OK;

@@ -29,7 +29,7 @@ FORGE_EXTERN_F8_ALL(1)
 hipError_t launch_wgrad_fused_bf16(int state_fmt, int opt, int sr, const void* X, const void* dY, const GemmDims& d,
                                    const OptArgs& a, hipStream_t st) {
   GArgs g{X, dY, d.ldx, d.lddy,
-          d.in, d.out, d.T, nullptr, 0, extent(d.T, d.ldx, 2), extent(d.T, d.lddy, 2), 0};
+          d.in, d.out, d.T, nullptr, 0, extent(d.T, d.in, d.ldx, 2), extent(d.T, d.out, d.lddy, 2), 0};
   switch (opt) {
     case FORGE_ADAMW: return wgrad_fused_bf16_opt<FORGE_ADAMW>(state_fmt, sr, g, a, st);
     case FORGE_SGD: return wgrad_fused_bf16_opt<FORGE_SGD>(state_fmt, sr, g, a, st);
@@ -46,7 +46,7 @@ hipError_t launch_wgrad_fused_bf16(int state_fmt, int opt, int sr, const void* X
 hipError_t launch_wgrad_store_bf16(const void* X, const void* dY, const GemmDims& d, float* dW, int64_t ld_dw,
                                    hipStream_t st) {
   GArgs g{X, dY, d.ldx, d.lddy,
-          d.in, d.out, d.T, dW, ld_dw, extent(d.T, d.ldx, 2), extent(d.T, d.lddy, 2), extent(d.out, ld_dw, 4)};
+          d.in, d.out, d.T, dW, ld_dw, extent(d.T, d.in, d.ldx, 2), extent(d.T, d.out, d.lddy, 2), extent(d.out, d.in, ld_dw, 4)};
   OptArgs a{};
   return g_pick<WgradBig, WgradSmall, WgradSplit, WgradBand>(
       g, [&](auto c, const GArgs& gc) { return g_launch<decltype(c), G_EPI_STORE, FORGE_SGD, ST_F32, false>(gc, a, st); });
@@ -69,22 +69,22 @@ static hipError_t wgrad_fused_f8(int sf, int opt, int sr, const GArgs& g, const 
 
 hipError_t launch_wgrad_fused_f8(int dy_e5m2, int state_fmt, int opt, int sr, const void* X, const float* x_scale, const void* dY,
                                  const float* dy_scale, const GemmDims& d, const OptArgs& a, hipStream_t st) {
-  GArgs g{X, dY, d.ldx, d.lddy, d.in, d.out, d.T, nullptr, 0, extent(d.T, d.ldx, 1), extent(d.T, d.lddy, 1), 0,
+  GArgs g{X, dY, d.ldx, d.lddy, d.in, d.out, d.T, nullptr, 0, extent(d.T, d.in, d.ldx, 1), extent(d.T, d.out, d.lddy, 1), 0,
           x_scale, dy_scale};
   return dy_e5m2 ? wgrad_fused_f8<1>(state_fmt, opt, sr, g, a, st) : wgrad_fused_f8<0>(state_fmt, opt, sr, g, a, st);
 }
 
 hipError_t launch_wgrad_store_f8(int dy_e5m2, const void* X, const float* x_scale, const void* dY,
                                  const float* dy_scale, const GemmDims& d, float* dW, int64_t ld_dw, hipStream_t st) {
-  GArgs g{X, dY, d.ldx, d.lddy, d.in, d.out, d.T, dW, ld_dw, extent(d.T, d.ldx, 1), extent(d.T, d.lddy, 1),
-          extent(d.out, ld_dw, 4), x_scale, dy_scale};
+  GArgs g{X, dY, d.ldx, d.lddy, d.in, d.out, d.T, dW, ld_dw, extent(d.T, d.in, d.ldx, 1), extent(d.T, d.out, d.lddy, 1),
+          extent(d.out, d.in, ld_dw, 4), x_scale, dy_scale};
   return dy_e5m2 ? wgrad_store_f8<1>(g, st) : wgrad_store_f8<0>(g, st);
 }
 
 hipError_t launch_dgrad_bf16(const void* dY, int64_t lddy, const void* W, int64_t ldw, void* dX, int64_t lddx,
                              int32_t T, int32_t n_out, int32_t n_in, hipStream_t st) {
   GArgs g{W, dY, ldw, lddy,
-          n_in, T, n_out, dX, lddx, extent(n_out, ldw, 2), extent(T, lddy, 2), extent(T, lddx, 2)};
+          n_in, T, n_out, dX, lddx, extent(n_out, n_in, ldw, 2), extent(T, n_out, lddy, 2), extent(T, n_in, lddx, 2)};
   OptArgs a{};
   return g_pick<DgradBig, DgradSmall, DgradSplit, DgradBand>(
       g, [&](auto c, const GArgs& gc) { return g_launch<decltype(c), G_EPI_DX, FORGE_SGD, ST_F32, false>(gc, a, st); });

@@ -65,13 +65,23 @@ enum { G_EPI_STORE = 0, G_EPI_OPT = 1, G_EPI_DX = 2 };
 #endif
 
 
+// issue priority of a ping-pong wave over its compute phase
+#ifndef FORGE_PP_PRIO
+#define FORGE_PP_PRIO 1
+#endif
+
 // Operand formats of the GEMM core: bfloat16, or OCP FP8 (E4M3 / E5M2 per operand).
 enum { G_BF16 = 0, G_FP8 = 1 };
 
 template <int BM_, int BN_, int BK_, int WM_, int WN_, bool B_TR_, int OCC_, int NSTAGE_ = 4, int KS_ = 1,
-          int IN_ = G_BF16, int FA_ = 0, int FB_ = 0>
+          int IN_ = G_BF16, int FA_ = 0, int FB_ = 0, int PP_ = 0>
 struct GCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+  // PP: ping-pong mainloop. The waves form two groups with one wave of each on every
+  // SIMD; while one group multiplies a stage held in its registers, the other reads
+  // the next stage's fragments from LDS and issues operand loads, and a workgroup
+  // barrier swaps the roles, so each SIMD's matrix pipe is fed by one group at a time.
+  static constexpr bool PP = PP_ != 0;
   static constexpr int OCC = OCC_;  // waves per SIMD
   static constexpr bool B_TR = B_TR_;
   // IN = G_FP8: both operands are OCP 8-bit codes, A in format FA and B in format FB
@@ -109,7 +119,9 @@ struct GCfg {
   static_assert((A_BYTES / 16) % NT == 0 && (B_BYTES / 16) % NT == 0, "stage must split evenly over threads");
   static_assert(NT % A_CPR == 0 && NT % B_CPR == 0, "a thread's chunks share a column");
   static_assert(TM % 32 == 0 && TN % 32 == 0 && BK % KSTEP == 0 && KSTEPS % KS == 0 && KPW >= 1, "tile shape");
-  static_assert(F8 || KPW % 2 == 0, "bf16 stages hold an even number of k-steps per wave");
+  static_assert(F8 || PP || KPW % 2 == 0, "bf16 stages hold an even number of k-steps per wave");
+  static_assert(!PP || (KS == 1 && WM * WN == 8 && OCC == 2 && !F8 && NSTAGE >= 3),
+                "ping-pong: 8 waves (two per SIMD), no k-split, bf16, a ring of three or more stages");
   // Chunk swizzles (XOR of the 16-byte chunk index of a row):
   //  * rows read with the 16-bit transpose read: 4 * (row % 4), so the four rows one read
   //    touches land in four different 64-byte bank groups (16 or more chunks per row);
@@ -230,6 +242,14 @@ __device__ __forceinline__ void vm_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(N) : "memory");
 }
 
+// Workgroup barrier alone (the waits it needs are explicit at each use).
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// Issue priority of this wave relative to the other waves of its SIMD.
+template <int P>
+__device__ __forceinline__ void issue_prio() {
+  __builtin_amdgcn_s_setprio(P);
+}
+
 // Persistent tile order: tile ids a workgroup takes are blockIdx.x + r*gridDim.x.
 // Workgroups are dealt to the 8 XCDs round-robin, so within a full round the ids of
 // one XCD are made contiguous, and contiguous ids walk GROUP tile-rows at a time.
@@ -263,11 +283,13 @@ __device__ __forceinline__ EpiRes epi_res(const OptArgs& a) {
   EpiRes r;
   constexpr bool Q8 = SF == ST_Q8 || SF == ST_Q8D;
   const uint32_t n = (uint32_t)a.out;
-  r.W = make_rsrc(a.W, n * (uint32_t)a.ldw * 2u);
+  // each resource spans its view exactly: (rows - 1) * ld + cols elements
+  const uint32_t in = (uint32_t)a.in;
+  r.W = make_rsrc(a.W, ((n - 1u) * (uint32_t)a.ldw + in) * 2u);
   constexpr int SL = opt_slots(OPT);
   const uint32_t es = Q8 ? 1u : (SF == ST_BF16 ? 2u : 4u);
-  r.m = make_rsrc((SL & 1) ? a.m : a.W, (SL & 1) ? n * (uint32_t)a.ldm * es : 0u);
-  r.v = make_rsrc((SL & 2) ? a.v : a.W, (SL & 2) ? n * (uint32_t)a.ldv * es : 0u);
+  r.m = make_rsrc((SL & 1) ? a.m : a.W, (SL & 1) ? ((n - 1u) * (uint32_t)a.ldm + in) * es : 0u);
+  r.v = make_rsrc((SL & 2) ? a.v : a.W, (SL & 2) ? ((n - 1u) * (uint32_t)a.ldv + in) * es : 0u);
   const uint32_t sb = Q8 ? n * (uint32_t)(a.in >> 6) * 4u : 0u;
   r.ms = make_rsrc(((SL & 1) && Q8) ? (const void*)a.m_scale : a.W, ((SL & 1) && Q8) ? sb : 0u);
   r.vs = make_rsrc(((SL & 2) && Q8) ? (const void*)a.v_scale : a.W, ((SL & 2) && Q8) ? sb : 0u);
@@ -496,6 +518,59 @@ void gemm_kernel(GArgs g, OptArgs a) {
       });
     };
 
+    if constexpr (C::PP) {
+    // ---- ping-pong mainloop ----
+    // Waves 0..3 (group A) and 4..7 (group B) hold one wave of each group on every
+    // SIMD. Each group alternates a memory phase M_i (issue its share of the operand
+    // loads of stage i - 1 + NSTAGE, read all fragments of stage i from LDS, wait for
+    // them and for its own loads of stage i + 1) with a compute phase C_i (the MFMAs of
+    // stage i from registers). Group B runs one phase behind group A, and every phase
+    // ends at a workgroup barrier, so while one group multiplies, the other reads:
+    //   phase 2i:   A in M_i,  B in C_{i-1}
+    //   phase 2i+1: A in C_i,  B in M_i
+    // Stage i's buffer is read in phases 2i and 2i+1 and refilled (stage i + NSTAGE)
+    // by A in phase 2i+2 and by B in phase 2i+3, each wave loading its own share as in
+    // the prologue. A wave's loads of stage s are issued in M_{s+1-NSTAGE} and waited
+    // for in M_{s-1}; the barrier that ends that phase publishes them before either
+    // group reads stage s.
+    const bool grp_b = wave_u >= C::NW / 2;
+    Frag F[C::KPW];
+    __syncthreads();  // the previous tile's epilogue is done with LDS
+    static_for<0, C::NSTAGE>([&](auto b_c) { dma(b_c, decltype(b_c)::value); });
+    vm_wait_barrier<(C::NSTAGE - 1) * LPS>();  // stage 0 published
+    if (grp_b) wg_barrier();                     // group B starts one phase later
+    auto pp_stage = [&](auto R_c, int i) {
+      constexpr int R = decltype(R_c)::value;  // i % NSTAGE
+      // memory phase M_i. Stages past the last one are issued too (their offsets are out of
+      // range and load zeros): the vmcnt waits count a fixed number of loads per phase, and a
+      // skipped load would let the wait for stage i + 1 pass before that stage has landed.
+      if (i >= 1) dma(std::integral_constant<int, (R + C::NSTAGE - 1) % C::NSTAGE>{}, i - 1 + C::NSTAGE);
+      static_for<0, C::KPW>([&](auto kk_c) {
+        static_for<0, NR>([&](auto r_c) { read_one(F[decltype(kk_c)::value], R_c, kk_c, r_c); });
+      });
+      // own loads of stage i + 1 landed (later stages may still be in flight), fragments landed
+      vm_wait_barrier<(C::NSTAGE - 2) * LPS>();
+      // compute phase C_i
+#pragma unroll
+      for (int kk = 0; kk < C::KPW; ++kk) settle(F[kk]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_prio<FORGE_PP_PRIO>();
+      static_for<0, C::KPW>([&](auto kk_c) {
+        static_for<0, C::FM * C::FN>([&](auto i_c) { mfma_one(F[decltype(kk_c)::value], i_c); });
+      });
+      issue_prio<0>();
+      __builtin_amdgcn_sched_barrier(0);
+      wg_barrier();
+    };
+    for (int i0 = 0; i0 < nst; i0 += C::NSTAGE)
+      static_for<0, C::NSTAGE>([&](auto r_c) {
+        const int i = i0 + decltype(r_c)::value;
+        if (i < nst) pp_stage(r_c, i);
+      });
+    if (!grp_b) wg_barrier();  // both groups pass the same number of barriers
+    // the loads of the stages past the last one still write LDS: let them land
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    } else {
     // ---- mainloop ----
     // Stage st sits in ring buffer st % NSTAGE. The k-steps' MFMAs run back to back,
     // each set reading the next set's fragments (two register sets alternate). Before
@@ -539,6 +614,7 @@ void gemm_kernel(GArgs g, OptArgs a) {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     settle(F0);
     settle(F1);
+    }
 
     // ---- epilogue ----
     // The finished tile is handed through LDS one wave-column (TN rows of n) at a
@@ -750,8 +826,11 @@ void gemm_kernel(GArgs g, OptArgs a) {
 // ---------------------------------------------------------------------------
 // Tile configurations (BM, BN, BK, WM, WN, B_TR, OCC[, NSTAGE, KS]); FORGE_*_CFG
 // override them at build time for tuning sweeps.
+#ifndef FORGE_BIG_PP
+#define FORGE_BIG_PP 1
+#endif
 #ifndef FORGE_WGRAD_BIG_CFG
-#define FORGE_WGRAD_BIG_CFG 256, 256, 32, 2, 4, true, 2
+#define FORGE_WGRAD_BIG_CFG 256, 256, 32, 2, 4, true, 2, 4, 1, G_BF16, 0, 0, FORGE_BIG_PP
 #endif
 #ifndef FORGE_WGRAD_SMALL_CFG
 #define FORGE_WGRAD_SMALL_CFG 128, 128, 32, 2, 2, true, 2
@@ -769,7 +848,7 @@ void gemm_kernel(GArgs g, OptArgs a) {
 #define FORGE_DGRAD_BAND_CFG 256, 128, 64, 2, 2, false, 2, 2, 2
 #endif
 #ifndef FORGE_DGRAD_BIG_CFG
-#define FORGE_DGRAD_BIG_CFG 256, 256, 32, 2, 4, false, 2
+#define FORGE_DGRAD_BIG_CFG 256, 256, 32, 2, 4, false, 2, 4, 1, G_BF16, 0, 0, FORGE_BIG_PP
 #endif
 #ifndef FORGE_DGRAD_SMALL_CFG
 #define FORGE_DGRAD_SMALL_CFG 128, 128, 32, 2, 2, false, 2
@@ -861,7 +940,11 @@ static hipError_t g_pick(const GArgs& g, F&& f) {
   return f(Split{}, g);
 }
 
-static uint32_t extent(int64_t rows, int64_t ld, int64_t es) { return (uint32_t)(rows * ld * es); }
+// Bytes a row-major view of rows x cols with row pitch ld spans: the last row ends at its
+// last column, so a view that ends at the end of its allocation is never read past.
+static uint32_t extent(int64_t rows, int64_t cols, int64_t ld, int64_t es) {
+  return rows <= 0 ? 0u : (uint32_t)(((rows - 1) * ld + cols) * es);
+}
 
 // Fused step for one optimizer on bf16 / fp32 operands (instantiated per optimizer
 // in the forge_gemm_bf16_*.hip sources).

@@ -243,6 +243,34 @@ def test_validation_errors(f):
 
 
 @cpu_only
+def test_alias_checks_cover_scales(f):
+    """Block scales of INT8 states and the one-float scales of FP8 inputs take part in the
+    overlap check: against each other, against every tensor's data, and their own data."""
+    BF16, I8, U8, E4M3, E5M2, F32 = 1, 2, 3, 4, 5, 0
+    A, B, C, Mp, Vp = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+    S1, S2 = 0x60000000, 0x70000000          # scales: 128 rows x 4 blocks x 4 bytes = 2 KiB each
+    X = _t(f, A, BF16, 64, 256)
+    dY = _t(f, B, BF16, 64, 128)
+    W = _t(f, C, BF16, 128, 256)
+    ok_m, ok_v = _t(f, Mp, I8, 128, 256, scale=S1), _t(f, Vp, U8, 128, 256, scale=S2)
+    # m's scales overlap v's scales
+    assert _call_step(f, X, dY, W, ok_m, _t(f, Vp, U8, 128, 256, scale=S1 + 1024)) == -8
+    # a scale array overlaps an input (X), W, or the other moment's codes
+    assert _call_step(f, X, dY, W, _t(f, Mp, I8, 128, 256, scale=A + 64), ok_v) == -8
+    assert _call_step(f, X, dY, W, ok_m, _t(f, Vp, U8, 128, 256, scale=C + 4096)) == -8
+    assert _call_step(f, X, dY, W, ok_m, _t(f, Vp, U8, 128, 256, scale=Mp + 128)) == -8
+    # a moment's own codes overlap its own scales
+    assert _call_step(f, X, dY, W, _t(f, Mp, I8, 128, 256, scale=Mp + 256), ok_v) == -8
+    # an FP8 input's scale lies inside W, or inside a state's block scales
+    m32, v32 = _t(f, Mp, F32, 128, 256), _t(f, Vp, F32, 128, 256)
+    Xq = _t(f, A, E4M3, 64, 256, scale=C + 16)
+    dYq = _t(f, B, E5M2, 64, 128, scale=S2)
+    assert _call_step(f, Xq, dYq, W, m32, v32) == -8
+    Xq = _t(f, A, E4M3, 64, 256, scale=S1 + 8)
+    assert _call_step(f, Xq, _t(f, B, E5M2, 64, 128, scale=0x7F000000), W, ok_m, ok_v) == -8
+
+
+@cpu_only
 def test_fp8_validation_errors(f):
     """FP8 inputs: X E4M3, dY E4M3 or E5M2, each with a one-float device scale, bf16 W, fp32 moments."""
     F32, BF16, I8, U8, E4M3, E5M2 = 0, 1, 2, 3, 4, 5
