@@ -336,59 +336,65 @@ void gemm_kernel(GArgs g, OptArgs a) {
   constexpr int NR = NRA + NRB;                                           // LDS reads per k-step and wave
   static_assert((C::NSTAGE - 1) * LPS <= 63, "vmcnt range");
 
-  // Staging: the LDS slot of this thread's chunk j in a stage is tid + j*NT (a wave's
-  // load fills 64 consecutive 16-byte slots); the swizzle picks the global chunk that
-  // lands there. Chunk j is A_RSTEP (B_RSTEP) rows below chunk 0.
-  const int a_row0 = tid / C::A_CPR, b_row0 = tid / C::B_CPR;
-  const int a_colb = ((tid % C::A_CPR) ^ C::swz_tr(a_row0, C::A_CPR)) * 16;  // byte column in the row
-  const int b_colb = ((tid % C::B_CPR) ^ C::swz_b(b_row0)) * 16;
   constexpr int A_RSTEP = C::NT / C::A_CPR, B_RSTEP = C::NT / C::B_CPR;
   const uint32_t a_rowb = (uint32_t)(A_RSTEP * g.lda * C::EB), a_stageb = (uint32_t)(C::BK * g.lda * C::EB);
   const uint32_t b_rowb = (uint32_t)(B_RSTEP * g.ldb * C::EB);
   const uint32_t b_stageb = C::B_TR ? (uint32_t)(C::BK * g.ldb * C::EB) : (uint32_t)(C::BK * C::EB);
-
-  // Byte addresses of this lane's fragment reads in stage buffer 0, k-step 0, with the
-  // chunk index swizzled as the loads placed it; buffers, k-steps and the reads of one
-  // fragment are immediates.
-  //  * 16-bit transpose read: lane (r4, c4, half, hi) reads row 8 hi + r4, elements
-  //    16 half + 4 c4 .. +3 of the 32-wide fragment; the lane receives 4 k of column l32.
-  //  * 8-bit transpose read: lane pair p = (lane % 16) / 2 reads row 32 hi + p, bytes
-  //    16 mh + 8 (lane % 2) .. +7 (mh = (lane / 16) % 2); the lane receives 8 k of
-  //    column l32. Operand byte b of lane l then holds k = 32 (l / 32) + b in both A and B.
   const uint32_t lds0 = lds_addr(smem);
   // A wave of k-split group ks reads k-steps ks*KPW .. ks*KPW + KPW-1 of each stage.
   const int kr0 = ks * C::KPW * C::KSTEP;  // first k row of this wave in a stage
-  auto tr_addr = [&](int base, int rowbytes, int cpr, int col0) -> uint32_t {
-    int row, chunk, byte;
-    if constexpr (C::F8) {
-      row = kr0 + 32 * hi + ((lane & 15) >> 1);
-      chunk = col0 / 16 + ((lane >> 4) & 1);
-      byte = 8 * (lane & 1);
-    } else {
-      const int r4 = (lane & 15) >> 2, c4 = lane & 3;
-      row = kr0 + 8 * hi + r4;
-      chunk = col0 * 2 / 16 + 2 * ((lane >> 4) & 1) + (c4 >> 1);
-      byte = 8 * (c4 & 1);
-    }
-    return lds0 + (uint32_t)(base + row * rowbytes + 16 * (chunk ^ C::swz_tr(row, cpr)) + byte);
-  };
-  uint32_t a_ad[C::FM], b_ad[C::B_TR ? C::FN : C::KPW];
-#pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) a_ad[fm] = tr_addr(C::a_base(0), C::ROWA, C::A_CPR, wave_m0 + 32 * fm);
-  if constexpr (C::B_TR) {
-#pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn) b_ad[fn] = tr_addr(C::b_base(0), C::ROWB, C::B_CPR, wave_n0 + 32 * fn);
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < C::KPW; ++kk)
-      b_ad[kk] = lds0 + (uint32_t)(C::b_base(0) + (wave_n0 + l32) * C::ROWB +
-                                   16 * ((2 * (ks * C::KPW + kk) + hi) ^ C::swz_b(l32)));
-  }
 
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     int tm, tn;
     g_tile(tile, ntm, ntn, tm, tn);
     const int m0 = g.m_off + tm * C::BM, n0 = g.n_off + tn * C::BN;
+    // Per-thread staging offsets and fragment addresses, from an opaque copy of the thread
+    // index: recomputed at every tile, so none of them is held (or spilled) through the
+    // epilogue, where the registers are full.
+    int ttid = tid;
+    asm volatile("" : "+v"(ttid));
+    const int t_lane = ttid & 63, t_hi = t_lane >> 5, t_l32 = t_lane & 31;
+    // Staging: the LDS slot of this thread's chunk j in a stage is tid + j*NT (a wave's
+    // load fills 64 consecutive 16-byte slots); the swizzle picks the global chunk that
+    // lands there. Chunk j is A_RSTEP (B_RSTEP) rows below chunk 0.
+    const int a_row0 = ttid / C::A_CPR, b_row0 = ttid / C::B_CPR;
+    const int a_colb = ((ttid % C::A_CPR) ^ C::swz_tr(a_row0, C::A_CPR)) * 16;  // byte column in the row
+    const int b_colb = ((ttid % C::B_CPR) ^ C::swz_b(b_row0)) * 16;
+
+    // Byte addresses of this lane's fragment reads in stage buffer 0, k-step 0, with the
+    // chunk index swizzled as the loads placed it; buffers, k-steps and the reads of one
+    // fragment are immediates.
+    //  * 16-bit transpose read: lane (r4, c4, half, hi) reads row 8 hi + r4, elements
+    //    16 half + 4 c4 .. +3 of the 32-wide fragment; the lane receives 4 k of column l32.
+    //  * 8-bit transpose read: lane pair p = (lane % 16) / 2 reads row 32 hi + p, bytes
+    //    16 mh + 8 (lane % 2) .. +7 (mh = (lane / 16) % 2); the lane receives 8 k of
+    //    column l32. Operand byte b of lane l then holds k = 32 (l / 32) + b in both A and B.
+    auto tr_addr = [&](int base, int rowbytes, int cpr, int col0) -> uint32_t {
+      int row, chunk, byte;
+      if constexpr (C::F8) {
+        row = kr0 + 32 * t_hi + ((t_lane & 15) >> 1);
+        chunk = col0 / 16 + ((t_lane >> 4) & 1);
+        byte = 8 * (t_lane & 1);
+      } else {
+        const int r4 = (t_lane & 15) >> 2, c4 = t_lane & 3;
+        row = kr0 + 8 * t_hi + r4;
+        chunk = col0 * 2 / 16 + 2 * ((t_lane >> 4) & 1) + (c4 >> 1);
+        byte = 8 * (c4 & 1);
+      }
+      return lds0 + (uint32_t)(base + row * rowbytes + 16 * (chunk ^ C::swz_tr(row, cpr)) + byte);
+    };
+    uint32_t a_ad[C::FM], b_ad[C::B_TR ? C::FN : C::KPW];
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) a_ad[fm] = tr_addr(C::a_base(0), C::ROWA, C::A_CPR, wave_m0 + 32 * fm);
+    if constexpr (C::B_TR) {
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) b_ad[fn] = tr_addr(C::b_base(0), C::ROWB, C::B_CPR, wave_n0 + 32 * fn);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < C::KPW; ++kk)
+        b_ad[kk] = lds0 + (uint32_t)(C::b_base(0) + (wave_n0 + t_l32) * C::ROWB +
+                                     16 * ((2 * (ks * C::KPW + kk) + t_hi) ^ C::swz_b(t_l32)));
+    }
 
     f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -617,11 +623,125 @@ void gemm_kernel(GArgs g, OptArgs a) {
     }
 
     // ---- epilogue ----
+    {
+    // Thread coordinates again, from an opaque copy of the thread index: nothing the epilogue
+    // derives from them stays live through the mainloop, where the registers are full.
+    int etid = static_cast<int>(threadIdx.x);
+    asm volatile("" : "+v"(etid));
+    const int tid = etid, lane = tid & 63, wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int ks = wave / (C::WM * C::WN), wsp = wave % (C::WM * C::WN);
+    const int wm = wsp % C::WM, wn = wsp / C::WM;
+    const int wave_m0 = wm * C::TM;
+    const int l32 = lane & 31, hi = lane >> 5;
     // The finished tile is handed through LDS one wave-column (TN rows of n) at a
     // time: the waves that own those rows write their accumulators (lane holds
     // C[m = 8q + 4*hi + j][n = l32] of each 32x32 block) as float rows, then every
     // thread takes 4 consecutive m of a row, so each wave reads and writes whole
     // contiguous row segments of W / m / v / dW / dX.
+    // One 4-element vector of a weight row (elements i .. i+3 of row o): the stored moments
+    // are decoded, the optimizer updates W and the moments from the FP32 gradient gx, and W and
+    // the moments are rounded and stored. Raw values as stored: wb = 4 bfloat16 weights; mr / vr
+    // the moments (float32: 4 words; bfloat16: .xy; INT8 codes: .x) with block scales msc / vsc.
+    constexpr int ST_CPOL = FORGE_EPI_ST_CPOL;
+    auto apply_vec = [&](const EpiRes& R, f32x4 gx, u32x2 wb, u32x4 mr, u32x4 vr, float msc, float vsc, int o,
+                         int i, bool ok) {
+      constexpr int SL = opt_slots(OPT);
+      constexpr bool HAS_M = SL & 1, HAS_V = SL & 2;
+      constexpr uint32_t es = Q8 ? 1u : (B16S ? 2u : 4u);
+      const uint32_t ow = ok ? (uint32_t)(o * a.ldw + i) * 2u : kOOB;
+      const uint32_t om = ok ? (uint32_t)(o * a.ldm + i) * es : kOOB;
+      const uint32_t ov = ok ? (uint32_t)(o * a.ldv + i) * es : kOOB;
+      const uint32_t osc = ok ? (uint32_t)(o * (a.in >> 6) + (i >> 6)) * 4u : kOOB;
+      if constexpr (C::F8) gx = gx * gscale;
+      const u32x2 mb{mr.x, mr.y}, vb{vr.x, vr.y};
+      const f32x4 mv = __builtin_bit_cast(f32x4, mr), vv = __builtin_bit_cast(f32x4, vr);
+      const uint32_t qm = mr.x, qv = vr.x;
+      const float gg[4] = {gx.x, gx.y, gx.z, gx.w};
+      float w[4] = {bits_f32(wb.x << 16), bits_f32(wb.x & 0xFFFF0000u), bits_f32(wb.y << 16),
+                    bits_f32(wb.y & 0xFFFF0000u)};
+      float m[4] = {0.f, 0.f, 0.f, 0.f}, v[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (B16S) {
+        if constexpr (HAS_M) bf16x4_to_f32(mb, m);
+        if constexpr (HAS_V) bf16x4_to_f32(vb, v);
+      } else if constexpr (!Q8) {
+        if constexpr (HAS_M) { m[0] = mv.x; m[1] = mv.y; m[2] = mv.z; m[3] = mv.w; }
+        if constexpr (HAS_V) { v[0] = vv.x; v[1] = vv.y; v[2] = vv.z; v[3] = vv.w; }
+      } else {
+        if constexpr (Q8D) {
+          if constexpr (HAS_M) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) m[j] = dyn_decode_s((qm >> (8 * j)) & 0xFFu, dyn->vs) * msc;
+          }
+          if constexpr (HAS_V) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = dyn->vu[(qv >> (8 * j)) & 0xFFu] * vsc;
+          }
+        } else {
+          if constexpr (HAS_M) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) m[j] = (float)(int8_t)((qm >> (8 * j)) & 0xFF) * msc;
+          }
+          if constexpr (HAS_V) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float r = (float)((qv >> (8 * j)) & 0xFF) * vsc;
+              v[j] = r * r;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) opt_apply<OPT>(gg[j], w[j], m[j], v[j], a.s);
+      const uint32_t idx0 = (uint32_t)o * (uint32_t)a.in + (uint32_t)i;
+      uint64_t zz[4];  // one random word per element serves W, m and v
+      rand64x4<SR>(a.rng_base, idx0, zz);
+      uint32_t bb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bb[j] = SR ? sr_bf16_bits(w[j], rand_field(zz[j], RF_W)) : rne_bf16_bits(w[j]);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16)}, R.W, ow, 0,
+                                            ST_CPOL);
+      if constexpr (B16S) {
+        if constexpr (HAS_M)
+          __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4<SR>(m, zz, RF_M), R.m, om, 0, ST_CPOL);
+        if constexpr (HAS_V)
+          __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4<SR>(v, zz, RF_V), R.v, ov, 0, ST_CPOL);
+      } else if constexpr (!Q8) {
+        if constexpr (HAS_M)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{m[0], m[1], m[2], m[3]}), R.m, om, 0,
+                                                 ST_CPOL);
+        if constexpr (HAS_V)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{v[0], v[1], v[2], v[3]}), R.v, ov, 0,
+                                                 ST_CPOL);
+      } else {
+        // block-64 absmax over the 16 adjacent lanes holding this row's block
+        // (linear codes: of m and sqrt(v); dynamic codes: of m and v)
+        float r[4], mmax = 0.f, vmax = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          r[j] = Q8D ? v[j] : sqrtf(v[j]);
+          mmax = fmaxf(mmax, fabsf(m[j]));
+          vmax = fmaxf(vmax, r[j]);
+        }
+#pragma unroll
+        for (int sh = 1; sh < 16; sh <<= 1) {
+          mmax = fmaxf(mmax, __shfl_xor(mmax, sh));
+          vmax = fmaxf(vmax, __shfl_xor(vmax, sh));
+        }
+        const float sm = Q8D ? mmax : mmax / 127.f, sv = Q8D ? vmax : vmax / 255.f;
+        if constexpr (Q8D) {
+          if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(quant_dyn_m4(m, sm, dyn->ms), R.m, om, 0, ST_CPOL);
+          if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(quant_dyn_v4(r, sv, dyn->mu), R.v, ov, 0, ST_CPOL);
+        } else {
+          if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(quant_m4(m, sm), R.m, om, 0, ST_CPOL);
+          if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(quant_v4(r, sv), R.v, ov, 0, ST_CPOL);
+        }
+        if ((i & 63) == 0) {
+          if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sm), R.ms, osc, 0, ST_CPOL);
+          if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sv), R.vs, osc, 0, ST_CPOL);
+        }
+      }
+    };
     float* E = reinterpret_cast<float*>(smem);
     constexpr int LDE = C::BM + 4;
     constexpr int VPR = C::BM / 4;                   // 4-element vectors per row
@@ -673,9 +793,11 @@ void gemm_kernel(GArgs g, OptArgs a) {
         const EpiRes R = epi_res<OPT, SF>(a);
         // loads of KB vectors are issued before any of them is consumed; KB bounds the
         // registers a batch holds next to the accumulators still to be written out
-        constexpr int KB_MAX = C::OCC >= 2 ? 2 : (Q8 ? 4 : 8);
+        constexpr int KB_MAX = Q8 && C::OCC >= 2 ? 1 : 2;
         constexpr int KB = NV > KB_MAX ? KB_MAX : NV;
-#pragma unroll
+        // at most 8 batches unrolled (the one-wave FP8 tiles have 32 vectors per thread and
+        // chunk: unrolling all of them exhausts the scalar registers)
+#pragma unroll 8
         for (int kb = 0; kb < NV; kb += KB) {
         uint32_t ow[KB], om[KB], ov_[KB], osc[KB];
         u32x2 wb[KB], mb[KB], vb[KB];
@@ -719,97 +841,26 @@ void gemm_kernel(GArgs g, OptArgs a) {
         for (int k = 0; k < KB; ++k) {
           const int vi = tid + (kb + k) * C::NT, row = vi / VPR, col = (vi % VPR) * 4;
           const int o = nrow0 + row, i = m0 + col;
-          f32x4 gx = *reinterpret_cast<const f32x4*>(E + row * LDE + col);
-          if constexpr (C::F8) gx = gx * gscale;
-          const float gg[4] = {gx.x, gx.y, gx.z, gx.w};
-          float w[4] = {bits_f32(wb[k].x << 16), bits_f32(wb[k].x & 0xFFFF0000u), bits_f32(wb[k].y << 16),
-                        bits_f32(wb[k].y & 0xFFFF0000u)};
-          float m[4] = {0.f, 0.f, 0.f, 0.f}, v[4] = {0.f, 0.f, 0.f, 0.f};
+          const f32x4 gx = *reinterpret_cast<const f32x4*>(E + row * LDE + col);
+          u32x4 mr{0u, 0u, 0u, 0u}, vr{0u, 0u, 0u, 0u};
+          float ms_k = 0.f, vs_k = 0.f;
           if constexpr (B16S) {
-            if constexpr (HAS_M) bf16x4_to_f32(mb[k], m);
-            if constexpr (HAS_V) bf16x4_to_f32(vb[k], v);
+            if constexpr (HAS_M) mr = u32x4{mb[k].x, mb[k].y, 0u, 0u};
+            if constexpr (HAS_V) vr = u32x4{vb[k].x, vb[k].y, 0u, 0u};
           } else if constexpr (!Q8) {
-            if constexpr (HAS_M) { m[0] = mv[k].x; m[1] = mv[k].y; m[2] = mv[k].z; m[3] = mv[k].w; }
-            if constexpr (HAS_V) { v[0] = vv[k].x; v[1] = vv[k].y; v[2] = vv[k].z; v[3] = vv[k].w; }
+            if constexpr (HAS_M) mr = __builtin_bit_cast(u32x4, mv[k]);
+            if constexpr (HAS_V) vr = __builtin_bit_cast(u32x4, vv[k]);
           } else {
-            if constexpr (Q8D) {
-              if constexpr (HAS_M) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) m[j] = dyn_decode_s((qm[k] >> (8 * j)) & 0xFFu, dyn->vs) * msc[k];
-              }
-              if constexpr (HAS_V) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) v[j] = dyn->vu[(qv[k] >> (8 * j)) & 0xFFu] * vsc[k];
-              }
-            } else {
-              if constexpr (HAS_M) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) m[j] = (float)(int8_t)((qm[k] >> (8 * j)) & 0xFF) * msc[k];
-              }
-              if constexpr (HAS_V) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                  const float r = (float)((qv[k] >> (8 * j)) & 0xFF) * vsc[k];
-                  v[j] = r * r;
-                }
-              }
-            }
+            if constexpr (HAS_M) { mr = u32x4{qm[k], 0u, 0u, 0u}; ms_k = msc[k]; }
+            if constexpr (HAS_V) { vr = u32x4{qv[k], 0u, 0u, 0u}; vs_k = vsc[k]; }
           }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) opt_apply<OPT>(gg[j], w[j], m[j], v[j], a.s);
-          const uint32_t idx0 = (uint32_t)o * (uint32_t)a.in + (uint32_t)i;
-          uint64_t zz[4];  // one random word per element serves W, m and v
-          rand64x4<SR>(a.rng_base, idx0, zz);
-          uint32_t bb[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) bb[j] = SR ? sr_bf16_bits(w[j], rand_field(zz[j], RF_W)) : rne_bf16_bits(w[j]);
-          __builtin_amdgcn_raw_buffer_store_b64(u32x2{bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16)}, R.W, ow[k], 0,
-                                                FORGE_EPI_ST_CPOL);
-          if constexpr (B16S) {
-            if constexpr (HAS_M)
-              __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4<SR>(m, zz, RF_M), R.m, om[k], 0, FORGE_EPI_ST_CPOL);
-            if constexpr (HAS_V)
-              __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4<SR>(v, zz, RF_V), R.v, ov_[k], 0, FORGE_EPI_ST_CPOL);
-          } else if constexpr (!Q8) {
-            if constexpr (HAS_M)
-              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{m[0], m[1], m[2], m[3]}), R.m, om[k], 0,
-                                                     FORGE_EPI_ST_CPOL);
-            if constexpr (HAS_V)
-              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{v[0], v[1], v[2], v[3]}), R.v, ov_[k], 0,
-                                                     FORGE_EPI_ST_CPOL);
-          } else {
-            // block-64 absmax over the 16 adjacent lanes holding this row's block
-            // (linear codes: of m and sqrt(v); dynamic codes: of m and v)
-            float r[4], mmax = 0.f, vmax = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              r[j] = Q8D ? v[j] : sqrtf(v[j]);
-              mmax = fmaxf(mmax, fabsf(m[j]));
-              vmax = fmaxf(vmax, r[j]);
-            }
-#pragma unroll
-            for (int sh = 1; sh < 16; sh <<= 1) {
-              mmax = fmaxf(mmax, __shfl_xor(mmax, sh));
-              vmax = fmaxf(vmax, __shfl_xor(vmax, sh));
-            }
-            const float sm = Q8D ? mmax : mmax / 127.f, sv = Q8D ? vmax : vmax / 255.f;
-            if constexpr (Q8D) {
-              if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(quant_dyn_m4(m, sm, dyn->ms), R.m, om[k], 0, FORGE_EPI_ST_CPOL);
-              if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(quant_dyn_v4(r, sv, dyn->mu), R.v, ov_[k], 0, FORGE_EPI_ST_CPOL);
-            } else {
-              if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(quant_m4(m, sm), R.m, om[k], 0, FORGE_EPI_ST_CPOL);
-              if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(quant_v4(r, sv), R.v, ov_[k], 0, FORGE_EPI_ST_CPOL);
-            }
-            if ((col & 63) == 0) {
-              if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sm), R.ms, osc[k], 0, FORGE_EPI_ST_CPOL);
-              if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sv), R.vs, osc[k], 0, FORGE_EPI_ST_CPOL);
-            }
-          }
+          apply_vec(R, gx, wb[k], mr, vr, ms_k, vs_k, o, i, o < g.N && i < g.M);
         }
         __builtin_amdgcn_sched_barrier(0);
         }
       }
       __syncthreads();  // the chunk's LDS rows are consumed before the next chunk overwrites them
+    }
     }
   }
 }
