@@ -344,13 +344,19 @@ def bf16_step_explained(W_gpu_bits, ref, opt, X, dY, W_b, m_b, v_b, hp, t, seed,
         dl = np.asarray(delta)[r_b, i_b]
     lo = np.full(n, np.iinfo(np.int64).max)
     hi = np.full(n, np.iinfo(np.int64).min)
+    # the update is element-wise and INT8 blocks stay inside a row: the oracle is re-run on
+    # the rows that hold differences only (r_loc: row of each difference among them)
+    ur, r_loc = np.unique(r_b, return_inverse=True)
+    sub = lambda a: None if a is None else np.asarray(a)[ur]  # noqa: E731
+    sel_s, g_s = np.asarray(sel)[ur], ref["g"][ur]
+    Wb_s, mb_s, vb_s, msb_s, vsb_s = sub(W_b), sub(m_b), sub(v_b), sub(ms_b), sub(vs_b)
     # samples across the interval, plus its point nearest zero (where g^2 is smallest)
     for s in list(np.linspace(-1.0, 1.0, n_samples)) + [None]:
-        g = ref["g"].copy()
-        g0 = g[r_b, i_b]
-        g[r_b, i_b] = g0 + s * dl if s is not None else np.sign(g0) * np.maximum(np.abs(g0) - dl, 0.0)
-        out = _oracle_rows(opt, X, dY, W_b, m_b, v_b, hp, t, seed, io, state, sel, ms_b, vs_b, g, fp8, sr)
-        c_lo, c_hi = _stored_range(out, slot, r_b, i_b, W_b, m_b, v_b, state, seed, t, n_in, sel, sr)
+        g = g_s.copy()
+        g0 = g[r_loc, i_b]
+        g[r_loc, i_b] = g0 + s * dl if s is not None else np.sign(g0) * np.maximum(np.abs(g0) - dl, 0.0)
+        out = _oracle_rows(opt, X, dY, Wb_s, mb_s, vb_s, hp, t, seed, io, state, sel_s, msb_s, vsb_s, g, fp8, sr)
+        c_lo, c_hi = _stored_range(out, slot, r_loc, i_b, Wb_s, mb_s, vb_s, state, seed, t, n_in, sel_s, sr)
         lo = np.minimum(lo, c_lo)
         hi = np.maximum(hi, c_hi)
     got = _ordered(W_gpu_bits[r_b, i_b])
@@ -360,8 +366,8 @@ def bf16_step_explained(W_gpu_bits, ref, opt, X, dY, W_b, m_b, v_b, hp, t, seed,
         far = np.abs(got - ref_o) > 1
         if far.any():
             fi_k = np.flatnonzero(far)
-            ok_el[fi_k] &= _far_explained(got[far], r_b[far], i_b[far], ref, opt, X, dY, W_b, m_b, v_b, hp, t,
-                                          seed, io, state, sel, ms_b, vs_b, sr, slot)
+            ok_el[fi_k] &= _far_explained(got[far], r_loc[far], i_b[far], {"g": g_s}, opt, X, dY, Wb_s, mb_s, vb_s,
+                                          hp, t, seed, io, state, sel_s, msb_s, vsb_s, sr, slot)
     unexplained = int(np.count_nonzero(~ok_el))
     ref_o = _ordered(ref[slot][r_b, i_b])
     idx = np.argsort(ok_el, kind="stable")[:5]
