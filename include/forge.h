@@ -199,6 +199,20 @@ int forge_optimizer_step(const float* dW, int64_t ld_dw, forge_tensor* W, forge_
                          forge_tensor* v, int32_t opt, const forge_hyper* hyper, int64_t step,
                          uint64_t seed, forge_stream_t stream);
 
+/*
+ * The whole unfused baseline in one call (the two-phase schedule of §1: the gradient
+ * is materialised in device memory, then a separate optimizer pass reads it back):
+ * enqueues forge_linear_wgrad into the caller's float32 workspace dW_workspace [out,
+ * ld_ws] (ld_ws >= in, a multiple of 4, 16-byte aligned), then forge_optimizer_step
+ * from it. Arguments as for forge_linear_wgrad_step; every one of them, the workspace
+ * included, is validated before anything is enqueued. The workspace may overlap no
+ * other tensor (FORGE_ERR_ALIAS) and holds dW when the work completes.
+ */
+int forge_linear_wgrad_unfused(const forge_tensor* X, const forge_tensor* dY, forge_tensor* W,
+                               forge_tensor* m, forge_tensor* v, int32_t opt, const forge_hyper* hyper,
+                               int64_t step, uint64_t seed, float* dW_workspace, int64_t ld_ws,
+                               forge_stream_t stream);
+
 /* Host-only helpers (no GPU work). */
 
 /* Fills *out with the per-step scalars of (opt, hyper, step). Returns a status. */

@@ -186,6 +186,75 @@ OptArgs make_args(forge_tensor* W, forge_tensor* m, forge_tensor* v, int opt, co
   return a;
 }
 
+// A validated step: what the launches need.
+struct StepPlan {
+  int io, fmt, sr;
+  bool f8, empty;
+  OptArgs a;
+  GemmDims d;
+};
+
+// Validates the arguments of a weight-gradient step (fused, or unfused through the float32
+// workspace ws [out, ld_ws] when ws is not NULL) and fills *p. Nothing is enqueued.
+int plan_step(const forge_tensor* X, const forge_tensor* dY, forge_tensor* W, forge_tensor* m, forge_tensor* v,
+              int32_t opt, const forge_hyper* hyper, int64_t step, uint64_t seed, float* ws, int64_t ld_ws,
+              StepPlan* p) {
+  if (!X || !dY || !W) return FORGE_ERR_NULL;
+  int r = check_hyper(opt, hyper, step);
+  if (r) return r;
+  const int io = W->dtype;
+  if (io != FORGE_F32 && io != FORGE_BF16) return FORGE_ERR_DTYPE;
+  const bool f8 = is_fp8(X->dtype) || is_fp8(dY->dtype);
+  if (f8) {
+    if (io != FORGE_BF16) return FORGE_ERR_DTYPE;
+    if ((r = check_fp8(X, false)) || (r = check_fp8(dY, true)) || (r = check_io(W, io))) return r;
+  } else if ((r = check_io(X, io)) || (r = check_io(dY, io)) || (r = check_io(W, io))) {
+    return r;
+  }
+  if (X->rows != dY->rows || X->cols != W->cols || dY->cols != W->rows) return FORGE_ERR_SHAPE;
+  const int fmt = check_states(opt, io, W, m, v);
+  if (fmt < 0) return fmt;
+  if (W->rows * W->cols >= ((int64_t)1 << 32)) return FORGE_ERR_UNSUPPORTED;
+  const int sl = opt_slots(opt);
+  if (!fits_31(X) || !fits_31(dY) || !fits_31(W) || ((sl & 1) && !fits_31(m)) || ((sl & 2) && !fits_31(v)))
+    return FORGE_ERR_UNSUPPORTED;
+  const forge_tensor* ins[2] = {X, dY};
+  if (ws) {
+    // the workspace is written by the GEMM and read by the optimizer pass: it may overlap
+    // nothing else
+    if (ld_ws < W->cols) return FORGE_ERR_SHAPE;
+    if (((uintptr_t)ws & 15u) || ld_ws % 4) return FORGE_ERR_ALIGN;
+    const forge_tensor wst{ws, FORGE_F32, 0, W->rows, W->cols, ld_ws, nullptr};
+    if (!fits_31(&wst)) return FORGE_ERR_UNSUPPORTED;
+    const forge_tensor* outs4[4] = {W, (sl & 1) ? m : nullptr, (sl & 2) ? v : nullptr, &wst};
+    if ((r = check_alias(outs4, 4, ins, 2))) return r;
+  } else {
+    const forge_tensor* outs[3] = {W, (sl & 1) ? m : nullptr, (sl & 2) ? v : nullptr};
+    if ((r = check_alias(outs, 3, ins, 2))) return r;
+  }
+  forge_scalars sc;
+  if ((r = forge_step_scalars(opt, hyper, step, &sc))) return r;
+  p->io = io;
+  p->fmt = fmt;
+  p->f8 = f8;
+  p->sr = (io == FORGE_BF16 && hyper->stochastic_round) ? 1 : 0;
+  p->empty = W->rows == 0 || W->cols == 0;
+  p->a = make_args(W, m, v, opt, sc, seed, step);
+  p->d = GemmDims{(int32_t)X->rows, (int32_t)W->rows, (int32_t)W->cols, X->ld, dY->ld};
+  return FORGE_OK;
+}
+
+// The two-phase baseline on a validated plan: float32 dW into ws, then the optimizer pass.
+int enqueue_unfused(const forge_tensor* X, const forge_tensor* dY, const StepPlan& p, int32_t opt, float* ws,
+                    int64_t ld_ws, hipStream_t st) {
+  hipError_t e = p.f8 ? launch_wgrad_store_f8(dY->dtype == FORGE_E5M2, X->data, X->scale, dY->data, dY->scale, p.d,
+                                              ws, ld_ws, st)
+                      : launch_wgrad_store(p.io == FORGE_BF16, X->data, dY->data, p.d, ws, ld_ws, st);
+  if (e != hipSuccess) return FORGE_ERR_HIP;
+  e = launch_optimizer(p.io == FORGE_BF16, p.fmt, opt, p.sr, ws, ld_ws, p.a, st);
+  return e == hipSuccess ? FORGE_OK : FORGE_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -332,38 +401,25 @@ int32_t forge_dyn_encode(int32_t is_signed, float y) {
 int forge_linear_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge_tensor* W, forge_tensor* m,
                             forge_tensor* v, int32_t opt, const forge_hyper* hyper, int64_t step, uint64_t seed,
                             forge_stream_t stream) {
-  if (!X || !dY || !W) return FORGE_ERR_NULL;
-  int r = check_hyper(opt, hyper, step);
-  if (r) return r;
-  const int io = W->dtype;
-  if (io != FORGE_F32 && io != FORGE_BF16) return FORGE_ERR_DTYPE;
-  const bool f8 = is_fp8(X->dtype) || is_fp8(dY->dtype);
-  if (f8) {
-    if (io != FORGE_BF16) return FORGE_ERR_DTYPE;
-    if ((r = check_fp8(X, false)) || (r = check_fp8(dY, true)) || (r = check_io(W, io))) return r;
-  } else if ((r = check_io(X, io)) || (r = check_io(dY, io)) || (r = check_io(W, io))) {
-    return r;
-  }
-  if (X->rows != dY->rows || X->cols != W->cols || dY->cols != W->rows) return FORGE_ERR_SHAPE;
-  const int fmt = check_states(opt, io, W, m, v);
-  if (fmt < 0) return fmt;
-  if (W->rows * W->cols >= ((int64_t)1 << 32)) return FORGE_ERR_UNSUPPORTED;
-  const int sl = opt_slots(opt);
-  if (!fits_31(X) || !fits_31(dY) || !fits_31(W) || ((sl & 1) && !fits_31(m)) || ((sl & 2) && !fits_31(v)))
-    return FORGE_ERR_UNSUPPORTED;
-  const forge_tensor* outs[3] = {W, (sl & 1) ? m : nullptr, (sl & 2) ? v : nullptr};
-  const forge_tensor* ins[2] = {X, dY};
-  if ((r = check_alias(outs, 3, ins, 2))) return r;
-  forge_scalars s;
-  if ((r = forge_step_scalars(opt, hyper, step, &s))) return r;
-  if (W->rows == 0 || W->cols == 0) return FORGE_OK;
-  const OptArgs a = make_args(W, m, v, opt, s, seed, step);
-  const GemmDims d{(int32_t)X->rows, (int32_t)W->rows, (int32_t)W->cols, X->ld, dY->ld};
-  const int sr = (io == FORGE_BF16 && hyper->stochastic_round) ? 1 : 0;
-  hipError_t e = f8 ? launch_wgrad_fused_f8(dY->dtype == FORGE_E5M2, fmt, opt, sr, X->data, X->scale, dY->data,
-                                            dY->scale, d, a, (hipStream_t)stream)
-                    : launch_wgrad_fused(io == FORGE_BF16, fmt, opt, sr, X->data, dY->data, d, a, (hipStream_t)stream);
+  StepPlan p;
+  int r = plan_step(X, dY, W, m, v, opt, hyper, step, seed, nullptr, 0, &p);
+  if (r || p.empty) return r;
+  hipError_t e = p.f8 ? launch_wgrad_fused_f8(dY->dtype == FORGE_E5M2, p.fmt, opt, p.sr, X->data, X->scale, dY->data,
+                                              dY->scale, p.d, p.a, (hipStream_t)stream)
+                      : launch_wgrad_fused(p.io == FORGE_BF16, p.fmt, opt, p.sr, X->data, dY->data, p.d, p.a,
+                                           (hipStream_t)stream);
   return e == hipSuccess ? FORGE_OK : FORGE_ERR_HIP;
+}
+
+int forge_linear_wgrad_unfused(const forge_tensor* X, const forge_tensor* dY, forge_tensor* W, forge_tensor* m,
+                               forge_tensor* v, int32_t opt, const forge_hyper* hyper, int64_t step, uint64_t seed,
+                               float* dW_workspace, int64_t ld_ws, forge_stream_t stream) {
+  // a layer with no elements needs no workspace
+  if (!dW_workspace && !(W && (W->rows == 0 || W->cols == 0))) return FORGE_ERR_NULL;
+  StepPlan p;
+  int r = plan_step(X, dY, W, m, v, opt, hyper, step, seed, dW_workspace, ld_ws, &p);
+  if (r || p.empty) return r;
+  return enqueue_unfused(X, dY, p, opt, dW_workspace, ld_ws, (hipStream_t)stream);
 }
 
 int forge_linear_dgrad(const forge_tensor* dY, const forge_tensor* W, forge_tensor* dX, forge_stream_t stream) {

@@ -68,6 +68,9 @@ def _load() -> ctypes.CDLL:
         "forge_optimizer_step": ([ctypes.c_void_p, ctypes.c_int64] + [P(ForgeTensor)] * 3 +
                                  [ctypes.c_int32, P(ForgeHyper), ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p],
                                  ctypes.c_int),
+        "forge_linear_wgrad_unfused": ([P(ForgeTensor)] * 5 + [ctypes.c_int32, P(ForgeHyper), ctypes.c_int64,
+                                                                ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int64,
+                                                                ctypes.c_void_p], ctypes.c_int),
         "forge_step_scalars": ([ctypes.c_int32, P(ForgeHyper), ctypes.c_int64, P(ForgeScalars)], ctypes.c_int),
         "forge_default_hyper": ([ctypes.c_int32, P(ForgeHyper)], ctypes.c_int),
         "forge_rand16": ([ctypes.c_uint64, ctypes.c_int64, ctypes.c_uint32], ctypes.c_uint32),
@@ -302,13 +305,28 @@ def optimizer_step(dW: torch.Tensor, W: torch.Tensor, m: Optional[torch.Tensor],
         raise ForgeError(st, "forge_optimizer_step")
 
 
+def _workspace(ws: Optional[torch.Tensor], W: torch.Tensor) -> torch.Tensor:
+    if ws is None:
+        ws = torch.empty(tuple(W.shape), dtype=torch.float32, device=W.device)
+    if ws.dtype != torch.float32 or ws.dim() != 2 or (ws.shape[1] > 1 and ws.stride(1) != 1) or not ws.is_cuda:
+        raise ValueError("dW_workspace must be a row-major float32 device tensor")
+    return ws
+
+
 def wgrad_unfused(X, dY, W, m, v, opt="adamw", hyper=None, step=1, seed=0, m_scale=None, v_scale=None,
                   dW_workspace: Optional[torch.Tensor] = None, stream=None, x_scale=None,
                   dy_scale=None, code: str = "linear") -> torch.Tensor:
-    """The two-phase baseline: store dW (float32), then a separate optimizer pass. Returns dW."""
-    dW = wgrad(X, dY, dW_workspace, stream, x_scale, dy_scale)
-    optimizer_step(dW, W, m, v, opt, hyper, step, seed, m_scale, v_scale, stream, code)
-    return dW
+    """The two-phase baseline in one call (forge_linear_wgrad_unfused): float32 dW into the
+    workspace (allocated here if not given), then a separate optimizer pass. Returns dW."""
+    ws = _workspace(dW_workspace, W)
+    h = _hyper(opt, hyper)
+    st = _lib.forge_linear_wgrad_unfused(_ref(describe(X, x_scale)), _ref(describe(dY, dy_scale)), _ref(describe(W)),
+                                         _ref(describe(m, m_scale, code=code)), _ref(describe(v, v_scale, code=code)),
+                                         OPT_ID[opt], ctypes.byref(h), int(step), seed & (2 ** 64 - 1),
+                                         ws.data_ptr() if ws.numel() else None, ws.stride(0), _stream(stream))
+    if st:
+        raise ForgeError(st, "forge_linear_wgrad_unfused")
+    return ws
 
 
 def new_states(W: torch.Tensor, opt: str = "adamw", fmt: str = "f32"):

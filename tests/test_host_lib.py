@@ -240,6 +240,20 @@ def test_validation_errors(f):
                                     None) == -6
     assert lib.forge_optimizer_step(None, 256, r(W), r(m), r(v), 0, ctypes.byref(h), 1, 0, None) == -1
     assert E.STATUS[-7] == "FORGE_ERR_HIP"
+    # the single-call unfused baseline validates its workspace like the other arguments
+    WS = 0x7A000000
+
+    def unfused(ws, ld, W_=W, m_=m, v_=v):
+        return lib.forge_linear_wgrad_unfused(r(X), r(dY), r(W_), r(m_), r(v_), 0, ctypes.byref(h), 1, 0,
+                                              ctypes.c_void_p(ws) if ws else None, ld, None)
+    assert unfused(0, 256) == -1                      # no workspace
+    assert unfused(WS + 4, 256) == -4                 # misaligned
+    assert unfused(WS, 252) == -2                     # ld_ws < in
+    assert unfused(WS, 258) == -4                     # ld_ws not a multiple of 4
+    assert unfused(C + 64, 256) == -8                 # workspace overlaps W
+    assert unfused(Mp, 256) == -8                     # workspace overlaps m
+    assert unfused(A, 256) == -8                      # workspace overlaps X
+    assert unfused(WS, 256, m_=_t(f, C, F32, 128, 256)) == -8   # m overlaps W (checked as in the fused step)
 
 
 @cpu_only
