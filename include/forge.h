@@ -14,6 +14,7 @@
  * Conventions for every entry point
  *   - All tensors are row-major and live in device memory owned by the caller;
  *     the library never allocates, frees or keeps a pointer after returning.
+ *     (forge_linear_wgrad_unfused_noalloc uses static device memory of its own.)
  *   - W and the moments are [out, in]; X is [T, in]; dY is [T, out]; dX is [T, in].
  *   - `ld` is the row pitch in elements (ld >= cols). Data pointers must be
  *     16-byte aligned; cols and ld must be multiples of 8 (bf16) or 4 (fp32).
@@ -24,7 +25,8 @@
  *     null stream). No entry point synchronises the host.
  *   - Arguments are validated on the host before anything is enqueued; on an
  *     error nothing is launched and a negative status is returned. No entry
- *     point keeps global mutable state; calls are thread-safe.
+ *     point keeps global mutable state and calls are thread-safe, except for
+ *     forge_linear_wgrad_unfused_noalloc (its per-GPU scratch; see there).
  *   - Results are deterministic: fixed reduction order, no atomics.
  */
 #ifndef FORGE_H
@@ -121,6 +123,7 @@ typedef struct {
 #define FORGE_ERR_HYPER (-6)       /* step < 1, unknown optimizer, non-finite or out-of-range hyper-parameter */
 #define FORGE_ERR_HIP (-7)         /* kernel launch failed (HIP error) */
 #define FORGE_ERR_ALIAS (-8)       /* output tensors overlap each other or an input */
+#define FORGE_ERR_SCRATCH (-9)     /* forge_linear_wgrad_unfused_noalloc: out*in > 2^24 (its scratch) */
 
 /*
  * Dynamic 8-bit moment code (FORGE_I8_DYN / FORGE_U8_DYN; §2 "Precision and
@@ -212,6 +215,23 @@ int forge_linear_wgrad_unfused(const forge_tensor* X, const forge_tensor* dY, fo
                                forge_tensor* m, forge_tensor* v, int32_t opt, const forge_hyper* hyper,
                                int64_t step, uint64_t seed, float* dW_workspace, int64_t ld_ws,
                                forge_stream_t stream);
+
+/*
+ * forge_linear_wgrad_unfused without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). The float32 dW lives in a scratch array the library holds in
+ * static device memory: 2^24 elements (64 MiB) on each GPU it runs on, for the life of
+ * the process. Layers with out*in > 2^24 return FORGE_ERR_SCRATCH (nothing enqueued).
+ * No hipMalloc / hipFree or allocating library routine is called; the first call on a
+ * device looks up that device's scratch address (hipGetSymbolAddress) and keeps it.
+ * Arguments and errors as for forge_linear_wgrad_unfused; the current device must be
+ * the one `stream` belongs to. Every call on a GPU shares that GPU's scratch, which keeps
+ * the last call's dW: calls that overlap in time on one GPU (other streams, other host
+ * threads) race on it and must be ordered by the caller.
+ */
+int forge_linear_wgrad_unfused_noalloc(const forge_tensor* X, const forge_tensor* dY, forge_tensor* W,
+                                       forge_tensor* m, forge_tensor* v, int32_t opt, const forge_hyper* hyper,
+                                       int64_t step, uint64_t seed, forge_stream_t stream);
 
 /* Host-only helpers (no GPU work). */
 

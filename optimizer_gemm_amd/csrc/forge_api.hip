@@ -4,6 +4,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "forge_internal.h"
 
 using namespace forge;
@@ -186,6 +189,35 @@ OptArgs make_args(forge_tensor* W, forge_tensor* m, forge_tensor* v, int opt, co
   return a;
 }
 
+// Scratch of the no-allocation unfused baseline: the float32 dW of a layer of at most
+// kScratchElems weights (64 MiB) in a file-scope device array. Every GPU the library runs
+// on holds its own copy until the process ends; host code addresses it only through the
+// device pointer hipGetSymbolAddress returns for the current device (the array's name is a
+// host-side stand-in, not a device address), fetched once per device and kept.
+constexpr int64_t kScratchElems = (int64_t)1 << 24;
+static __device__ __align__(256) float scratch[kScratchElems];
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_of_current_device(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FORGE_ERR_HIP;
+  float* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+      void* q = nullptr;
+      if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return FORGE_ERR_HIP;
+      p = static_cast<float*>(q);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return FORGE_OK;
+}
+
 // A validated step: what the launches need.
 struct StepPlan {
   int io, fmt, sr;
@@ -272,6 +304,7 @@ const char* forge_status_str(int status) {
     case FORGE_ERR_HYPER: return "invalid optimizer, step or hyper-parameter";
     case FORGE_ERR_HIP: return "HIP kernel launch failed";
     case FORGE_ERR_ALIAS: return "output tensors overlap each other or an input";
+    case FORGE_ERR_SCRATCH: return "the layer's float32 dW exceeds the no-allocation scratch (2^24 elements)";
     default: return "unknown status";
   }
 }
@@ -420,6 +453,18 @@ int forge_linear_wgrad_unfused(const forge_tensor* X, const forge_tensor* dY, fo
   int r = plan_step(X, dY, W, m, v, opt, hyper, step, seed, dW_workspace, ld_ws, &p);
   if (r || p.empty) return r;
   return enqueue_unfused(X, dY, p, opt, dW_workspace, ld_ws, (hipStream_t)stream);
+}
+
+int forge_linear_wgrad_unfused_noalloc(const forge_tensor* X, const forge_tensor* dY, forge_tensor* W,
+                                       forge_tensor* m, forge_tensor* v, int32_t opt, const forge_hyper* hyper,
+                                       int64_t step, uint64_t seed, forge_stream_t stream) {
+  StepPlan p;
+  int r = plan_step(X, dY, W, m, v, opt, hyper, step, seed, nullptr, 0, &p);
+  if (r || p.empty) return r;
+  if (W->rows * W->cols > kScratchElems) return FORGE_ERR_SCRATCH;
+  float* ws = nullptr;
+  if ((r = scratch_of_current_device(&ws))) return r;
+  return enqueue_unfused(X, dY, p, opt, ws, W->cols, (hipStream_t)stream);
 }
 
 int forge_linear_dgrad(const forge_tensor* dY, const forge_tensor* W, forge_tensor* dX, forge_stream_t stream) {

@@ -25,7 +25,7 @@ SLOTS = {"adamw": (1, 1), "sgd": (0, 0), "sgd_momentum": (1, 0), "lion": (1, 0),
 
 STATUS = {0: "FORGE_OK", -1: "FORGE_ERR_NULL", -2: "FORGE_ERR_SHAPE", -3: "FORGE_ERR_DTYPE",
           -4: "FORGE_ERR_ALIGN", -5: "FORGE_ERR_UNSUPPORTED", -6: "FORGE_ERR_HYPER", -7: "FORGE_ERR_HIP",
-          -8: "FORGE_ERR_ALIAS"}
+          -8: "FORGE_ERR_ALIAS", -9: "FORGE_ERR_SCRATCH"}
 
 
 class ForgeTensor(ctypes.Structure):
@@ -71,6 +71,8 @@ def _load() -> ctypes.CDLL:
         "forge_linear_wgrad_unfused": ([P(ForgeTensor)] * 5 + [ctypes.c_int32, P(ForgeHyper), ctypes.c_int64,
                                                                 ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int64,
                                                                 ctypes.c_void_p], ctypes.c_int),
+        "forge_linear_wgrad_unfused_noalloc": ([P(ForgeTensor)] * 5 + [ctypes.c_int32, P(ForgeHyper), ctypes.c_int64,
+                                                                        ctypes.c_uint64, ctypes.c_void_p], ctypes.c_int),
         "forge_step_scalars": ([ctypes.c_int32, P(ForgeHyper), ctypes.c_int64, P(ForgeScalars)], ctypes.c_int),
         "forge_default_hyper": ([ctypes.c_int32, P(ForgeHyper)], ctypes.c_int),
         "forge_rand16": ([ctypes.c_uint64, ctypes.c_int64, ctypes.c_uint32], ctypes.c_uint32),
@@ -327,6 +329,19 @@ def wgrad_unfused(X, dY, W, m, v, opt="adamw", hyper=None, step=1, seed=0, m_sca
     if st:
         raise ForgeError(st, "forge_linear_wgrad_unfused")
     return ws
+
+
+def wgrad_unfused_noalloc(X, dY, W, m, v, opt="adamw", hyper=None, step=1, seed=0, m_scale=None, v_scale=None,
+                          stream=None, x_scale=None, dy_scale=None, code: str = "linear") -> None:
+    """The two-phase baseline with dW in the library's static per-GPU scratch
+    (forge_linear_wgrad_unfused_noalloc): allocates nothing; out*in <= 2^24."""
+    h = _hyper(opt, hyper)
+    st = _lib.forge_linear_wgrad_unfused_noalloc(_ref(describe(X, x_scale)), _ref(describe(dY, dy_scale)),
+                                                 _ref(describe(W)), _ref(describe(m, m_scale, code=code)),
+                                                 _ref(describe(v, v_scale, code=code)), OPT_ID[opt], ctypes.byref(h),
+                                                 int(step), seed & (2 ** 64 - 1), _stream(stream))
+    if st:
+        raise ForgeError(st, "forge_linear_wgrad_unfused_noalloc")
 
 
 def new_states(W: torch.Tensor, opt: str = "adamw", fmt: str = "f32"):

@@ -44,7 +44,7 @@ def test_exports_every_declared_symbol(f):
 
 
 def test_status_strings(f):
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         assert f.status_str(code) not in ("", "unknown status")
     assert f.status_str(42) == "unknown status"
     assert f.version() >= 100
