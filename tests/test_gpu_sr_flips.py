@@ -6,8 +6,10 @@ element flips its stochastic rounding with probability |dx32| / 2^16 (dx32 in fl
 ulps). RMSprop's second step on the Qwen3-14B MLP weight (17408 x 5120, 4096 tokens) is
 the most sensitive case of the sweep (its early updates are about ten learning rates,
 half the weights' size). Per seed the test checks every flip (one step, explained), and
-holds the count to what a model of the matrix instruction's FP32 summation in the
-kernel's order predicts for the same inputs, and reports it against the 0.01% budget.
+holds the count to the budget of what a model of the matrix instruction's FP32 summation
+in the kernel's order predicts for the same inputs (flip_budget). The rate it reports,
+about 0.011% over the eight seeds, is above the 0.01% that the bf16 weight path is
+otherwise held to: at this step the flips the FP32 sum itself causes exceed that budget.
 """
 import numpy as np
 import pytest
@@ -55,10 +57,12 @@ def test_rmsprop_step_two_flip_rate_over_eight_seeds():
         ref = ostep.wgrad_step(opt, X, dY, W_b, m_b, v_b, hp, 2, seed, rows=sel)
         ok, n, unexp, detail = P.bf16_step_explained(after[0], ref, opt, X, dY, W_b, m_b, v_b, hp, 2, seed, "bf16",
                                                      "f32", sel, frac=1.0)
-        pred = P.predicted_flips(X, dY, "bf16", sel, opt, W_b, m_b, v_b, hp, 2, seed, "f32", order_of, ref)
+        pred = P.predicted_flips(opt, X, dY, W_b, m_b, v_b, hp, 2, seed, "bf16", "f32", sel, None, None, None, ref,
+                                 "W", True, order_of)
         print(f"[flips] seed {s}: {n} of {after[0].size} ({100 * n / after[0].size:.4f}%), predicted "
-              f"{pred:.1f}, unexplained {unexp}", flush=True)
+              f"{pred:.1f} (budget {P.flip_budget(pred)}), unexplained {unexp}", flush=True)
         assert unexp == 0, f"seed {s}: {unexp} differing weights not explained: {detail}"
+        assert n <= P.flip_budget(pred), f"seed {s}: {n} flips, above the model's budget {P.flip_budget(pred)}"
         flips.append(n)
         preds.append(pred)
         rows_total += after[0].size
