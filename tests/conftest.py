@@ -1,4 +1,6 @@
+import importlib.util
 import os
+import shutil
 import sys
 
 import pytest
@@ -25,3 +27,24 @@ def gpu():
     if not torch.cuda.is_available():
         pytest.fail("GPU test run without a visible GPU")
     return torch.device("cuda:0")
+
+
+def forge_build_module():
+    """optimizer_gemm_amd/build.py, loaded by path (importing the package would load the
+    library)."""
+    spec = importlib.util.spec_from_file_location("forge_build", os.path.join(ROOT, "optimizer_gemm_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+@pytest.fixture(scope="session")
+def host_checked_build():
+    """The library's host-checking variant (sanitizers on the host code, release device
+    code), compiled once per session with the compiler's per-kernel resource report:
+    (build module, library path, {source: compiler stderr})."""
+    if not (shutil.which("hipcc") or os.path.exists("/opt/rocm/bin/hipcc")):
+        pytest.skip("hipcc not available")
+    b = forge_build_module()
+    lib, stderr = b.build_sanitized(remarks=True)
+    return b, lib, stderr
