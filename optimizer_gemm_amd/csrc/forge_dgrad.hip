@@ -229,14 +229,15 @@ __global__ __launch_bounds__(256) void optimizer_kernel(const float* __restrict_
       mmax = fmaxf(mmax, __shfl_xor(mmax, sh));
       vmax = fmaxf(vmax, __shfl_xor(vmax, sh));
     }
-    const float sm = Q8D ? mmax : mmax / 127.f, sv = Q8D ? vmax : vmax / 255.f;
+    const float sm = Q8D ? mmax : mmax * (1.f / 127.f), sv = Q8D ? vmax : vmax * (1.f / 255.f);
+    const float im = block_inv(mmax, Q8D ? 1.f : 127.f), iv = block_inv(vmax, Q8D ? 1.f : 255.f);
     if (valid) {
       if constexpr (HAS_M)
         *reinterpret_cast<uint32_t*>(reinterpret_cast<int8_t*>(a.m) + (int64_t)o * a.ldm + i) =
-            Q8D ? quant_dyn_m4(m, sm, dyn->ms) : quant_m4(m, sm);
+            Q8D ? quant_dyn_m4(m, im, dyn->ms) : quant_m4(m, im);
       if constexpr (HAS_V)
         *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.v) + (int64_t)o * a.ldv + i) =
-            Q8D ? quant_dyn_v4(r, sv, dyn->mu) : quant_v4(r, sv);
+            Q8D ? quant_dyn_v4(r, iv, dyn->mu) : quant_v4(r, iv);
       if ((i & 63) == 0) {
         const int64_t si = (int64_t)o * (a.in >> 6) + (i >> 6);
         if constexpr (HAS_M) a.m_scale[si] = sm;

@@ -65,6 +65,15 @@ enum { G_EPI_STORE = 0, G_EPI_OPT = 1, G_EPI_DX = 2 };
 #endif
 
 
+// 4-element vectors whose W / m / v loads the optimizer epilogue issues before consuming
+// any of them, and whether the compiler may move work across those batches
+#ifndef FORGE_EPI_KB
+#define FORGE_EPI_KB 2
+#endif
+#ifndef FORGE_EPI_SCHED_BARRIER
+#define FORGE_EPI_SCHED_BARRIER 1
+#endif
+
 // issue priority of a ping-pong wave over its compute phase
 #ifndef FORGE_PP_PRIO
 #define FORGE_PP_PRIO 1
@@ -728,13 +737,14 @@ void gemm_kernel(GArgs g, OptArgs a) {
           mmax = fmaxf(mmax, __shfl_xor(mmax, sh));
           vmax = fmaxf(vmax, __shfl_xor(vmax, sh));
         }
-        const float sm = Q8D ? mmax : mmax / 127.f, sv = Q8D ? vmax : vmax / 255.f;
+        const float sm = Q8D ? mmax : mmax * (1.f / 127.f), sv = Q8D ? vmax : vmax * (1.f / 255.f);
+        const float im = block_inv(mmax, Q8D ? 1.f : 127.f), iv = block_inv(vmax, Q8D ? 1.f : 255.f);
         if constexpr (Q8D) {
-          if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(quant_dyn_m4(m, sm, dyn->ms), R.m, om, 0, ST_CPOL);
-          if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(quant_dyn_v4(r, sv, dyn->mu), R.v, ov, 0, ST_CPOL);
+          if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(quant_dyn_m4(m, im, dyn->ms), R.m, om, 0, ST_CPOL);
+          if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(quant_dyn_v4(r, iv, dyn->mu), R.v, ov, 0, ST_CPOL);
         } else {
-          if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(quant_m4(m, sm), R.m, om, 0, ST_CPOL);
-          if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(quant_v4(r, sv), R.v, ov, 0, ST_CPOL);
+          if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(quant_m4(m, im), R.m, om, 0, ST_CPOL);
+          if constexpr (HAS_V) __builtin_amdgcn_raw_buffer_store_b32(quant_v4(r, iv), R.v, ov, 0, ST_CPOL);
         }
         if ((i & 63) == 0) {
           if constexpr (HAS_M) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sm), R.ms, osc, 0, ST_CPOL);
@@ -793,7 +803,7 @@ void gemm_kernel(GArgs g, OptArgs a) {
         const EpiRes R = epi_res<OPT, SF>(a);
         // loads of KB vectors are issued before any of them is consumed; KB bounds the
         // registers a batch holds next to the accumulators still to be written out
-        constexpr int KB_MAX = Q8 && C::OCC >= 2 ? 1 : 2;
+        constexpr int KB_MAX = Q8 && C::OCC >= 2 ? 1 : FORGE_EPI_KB;
         constexpr int KB = NV > KB_MAX ? KB_MAX : NV;
         // at most 8 batches unrolled (the one-wave FP8 tiles have 32 vectors per thread and
         // chunk: unrolling all of them exhausts the scalar registers)
@@ -856,7 +866,9 @@ void gemm_kernel(GArgs g, OptArgs a) {
           }
           apply_vec(R, gx, wb[k], mr, vr, ms_k, vs_k, o, i, o < g.N && i < g.M);
         }
+#if FORGE_EPI_SCHED_BARRIER
         __builtin_amdgcn_sched_barrier(0);
+#endif
         }
       }
       __syncthreads();  // the chunk's LDS rows are consumed before the next chunk overwrites them

@@ -188,10 +188,21 @@ __device__ __forceinline__ u32x2 pack_bf16x4(const float x[4], const uint64_t z[
   return u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
 }
 // The random words of four consecutive elements idx0..idx0+3 (only with stochastic rounding).
+// Consecutive counters differ by one, so their SplitMix64 states differ by the golden gamma:
+// one 64-bit product for the first, additions for the rest (element indices stay below 2^32).
 template <bool SR>
 __device__ __forceinline__ void rand64x4(uint64_t base, uint32_t idx0, uint64_t z[4]) {
+  if constexpr (SR) {
+    uint64_t c = base + 0x9E3779B97F4A7C15ull * ((uint64_t)idx0 + 1ull);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) z[j] = SR ? rand64_from_base(base, idx0 + j) : 0ull;
+    for (int j = 0; j < 4; ++j) {
+      z[j] = splitmix64_mix(c);
+      c += 0x9E3779B97F4A7C15ull;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) z[j] = 0ull;
+  }
 }
 
 // Stores four consecutive weights; bf16 weights round with field RF_W of z[0..3].
@@ -245,26 +256,33 @@ __device__ __forceinline__ void dequant_v4(const OptArgs& a, int o, int i, float
     x[j] = r * r;
   }
 }
-// Quantises 4 values with the block scale s (already reduced over the block).
-__device__ __forceinline__ uint32_t quant_m4(const float x[4], float s) {
+// Quantises 4 values with the reciprocal of the block scale, inv = 127 / absmax (m) or
+// 255 / absmax (sqrt v), 0 for an all-zero block (already reduced over the block): the
+// code is RNE(x * inv), clamped. Multiplying by the reciprocal instead of dividing by the
+// stored scale moves x * inv by at most about one float32 ulp, which changes a code only
+// where the quotient lies that close to a rounding midpoint, and then by one step.
+__device__ __forceinline__ uint32_t quant_m4(const float x[4], float inv) {
   uint32_t q = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    float c = s > 0.f ? rintf(x[j] / s) : 0.f;
-    c = fminf(fmaxf(c, -127.f), 127.f);
+    const float c = fminf(fmaxf(rintf(x[j] * inv), -127.f), 127.f);
     q |= ((uint32_t)(int32_t)c & 0xFFu) << (8 * j);
   }
   return q;
 }
-__device__ __forceinline__ uint32_t quant_v4(const float r[4], float s) {  // r = sqrt(v)
+__device__ __forceinline__ uint32_t quant_v4(const float r[4], float inv) {  // r = sqrt(v)
   uint32_t q = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    float c = s > 0.f ? rintf(r[j] / s) : 0.f;
-    c = fminf(fmaxf(c, 0.f), 255.f);
+    const float c = fminf(fmaxf(rintf(r[j] * inv), 0.f), 255.f);
     q |= ((uint32_t)c & 0xFFu) << (8 * j);
   }
   return q;
+}
+// inv of a block from its absmax: levels / absmax through the hardware reciprocal (within
+// one ulp; it only feeds the code decision above), or 0 for an all-zero block
+__device__ __forceinline__ float block_inv(float absmax, float levels) {
+  return absmax > 0.f ? levels * __builtin_amdgcn_rcpf(absmax) : 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -354,17 +372,19 @@ __host__ __device__ __forceinline__ float dyn_decode_s(uint32_t b, const float* 
   const float x = vs[b & 0x7Fu];
   return (b & 0x80u) ? -x : x;
 }
-// 4 values with block absmax s (already reduced over the block) -> 4 codes.
-__host__ __device__ __forceinline__ uint32_t quant_dyn_m4(const float x[4], float s, const float* mid) {
+// 4 values with the reciprocal inv = 1 / absmax of their block (0 for an all-zero block,
+// already reduced over the block) -> 4 codes; as for the linear codes, the product stands
+// in for the quotient.
+__host__ __device__ __forceinline__ uint32_t quant_dyn_m4(const float x[4], float inv, const float* mid) {
   uint32_t q = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) q |= dyn_encode_s(s > 0.f ? x[j] / s : 0.f, mid) << (8 * j);
+  for (int j = 0; j < 4; ++j) q |= dyn_encode_s(x[j] * inv, mid) << (8 * j);
   return q;
 }
-__host__ __device__ __forceinline__ uint32_t quant_dyn_v4(const float x[4], float s, const float* mid) {
+__host__ __device__ __forceinline__ uint32_t quant_dyn_v4(const float x[4], float inv, const float* mid) {
   uint32_t q = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) q |= dyn_encode_u(s > 0.f ? x[j] / s : 0.f, mid) << (8 * j);
+  for (int j = 0; j < 4; ++j) q |= dyn_encode_u(x[j] * inv, mid) << (8 * j);
   return q;
 }
 
