@@ -879,11 +879,11 @@ void gemm_kernel(GArgs g, OptArgs a) {
 
 // ---------------------------------------------------------------------------
 // Launchers. Large problems use 256x256 workgroup tiles (8 waves of 128x64, two
-// per SIMD); problems with fewer such tiles than compute units use 128x128 tiles
-// (4 waves of 64x64, two workgroups per compute unit), and when even those are
-// scarce (fewer than two per compute unit) 128x128 tiles with a 2-way in-workgroup
-// split-K (8 waves of 64x64, one workgroup per compute unit), so a compute unit
-// that holds a single tile still runs two waves per SIMD. A last round of 256x256
+// per SIMD), also when they fill only part of one round (more than half of the
+// compute units); smaller problems use 128x128 tiles (4 waves of 64x64, two
+// workgroups per compute unit) when those fill a round, else 128x128 tiles with a
+// 2-way in-workgroup split-K (8 waves of 64x64, one workgroup per compute unit), so
+// a compute unit that holds a single tile still runs two waves per SIMD. A last round of 256x256
 // tiles that would be at most half full is replaced by a second launch of 256x128
 // tiles (8 waves of 128x64, 2-way in-workgroup split-K) over the rest of C.
 // ---------------------------------------------------------------------------
@@ -969,7 +969,8 @@ static int g_tiles(const GArgs& g) {
 }
 
 // Calls f(C{}, g') for each launch of the tile configuration C over the part g' of
-// the problem. Large tiles are used when there are at least as many as compute units.
+// the problem. Large tiles are used when there are more than half as many as compute
+// units.
 // When their last round would leave more than half of the compute units idle, the
 // whole rounds run as large tiles over a band of tile columns (or rows, whichever
 // band holds more of them), and the rest of C runs as a second launch on the same
@@ -999,6 +1000,9 @@ static hipError_t g_pick(const GArgs& g, F&& f) {
     }
     return f(Big{}, g);
   }
+  // more than half a round of large tiles: one partial round of them beats the 128x128
+  // tiles' two rounds (their per-CU rate is lower: twice the operand bytes per flop)
+  if (2 * tiles > cus) return f(Big{}, g);
   if (g_tiles<Small>(g) >= 2 * cus) return f(Small{}, g);
   return f(Split{}, g);
 }

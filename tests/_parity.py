@@ -195,8 +195,9 @@ def wgrad_tile_order(out, inn, cus):
     """Summation order ("seq" or "split2") of each output row of a weight-gradient launch on
     a device with `cus` compute units, following the library's choice of tiles: 256x256 tiles
     (one chain) when there are at least `cus` of them, with a last round that would be at most
-    half full moved to 256x128 tiles with a 2-way k-split over a band of rows or columns;
-    128x128 tiles (one chain) when at least 2 * cus of those; else 128x128 tiles with a k-split.
+    half full moved to 256x128 tiles with a 2-way k-split over a band of rows or columns, or
+    when there are more than cus / 2 of them (one partial round); 128x128 tiles (one chain)
+    when at least 2 * cus of those; else 128x128 tiles with a k-split.
     Returns a function row -> order, or None when the order depends on the column."""
     ntm, ntn = -(-inn // 256), -(-out // 256)
     tiles = ntm * ntn
@@ -208,6 +209,8 @@ def wgrad_tile_order(out, inn, cus):
             if nb * ntm >= mb * ntn:
                 return lambda o: "seq" if o < nb * 256 else "split2"
             return None
+        return lambda o: "seq"
+    if 2 * tiles > cus:
         return lambda o: "seq"
     if (-(-inn // 128)) * (-(-out // 128)) >= 2 * cus:
         return lambda o: "seq"

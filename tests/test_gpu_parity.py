@@ -359,18 +359,17 @@ def test_step_one_hundred_thousand_from_nonzero_moments(opt, over):
     P.verify_step(opt, X, dY, before, after, hp, t, 0x5EED_1000, "bf16", "f32", True, sel)
 
 
-# ---------------------------------------------------------------- small tiles over two rounds
+# ---------------------------------------------------------------- a partial round of large tiles
 @pytest.mark.parametrize("state", ["f32", "q8", "q8dyn", "bf16"])
-def test_small_tiles_over_two_rounds(state):
-    # 3584 x 4096: 224 tiles of 256x256 (fewer than the 256 compute units), so 896 tiles of
-    # 128x128 on 512 resident workgroups: most workgroups take a second tile while their
-    # neighbour on the compute unit is still in its first one
+def test_partial_round_of_large_tiles(state):
+    # 3584 x 4096: 224 tiles of 256x256, more than half of the 256 compute units, so one
+    # partial round of large tiles (and not 896 tiles of 128x128 over two rounds)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     if cus != 256:
         pytest.skip("shape laid out for 256 compute units")
     rows = np.unique(np.concatenate([np.arange(0, 3584, 37), [3583]]))
     run_case(LayerSpec("mr", 3584, 4096, 200), "adamw", 2, config=140, rows=rows, state=state,
-             label=f"128x128 tiles over two rounds, {state} moments")
+             label=f"a partial round of 256x256 tiles, {state} moments")
 
 
 # ---------------------------------------------------------------- smallest shapes, streams
