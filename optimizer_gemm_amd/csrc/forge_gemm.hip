@@ -48,7 +48,7 @@ hipError_t launch_wgrad_store_bf16(const void* X, const void* dY, const GemmDims
   GArgs g{X, dY, d.ldx, d.lddy,
           d.in, d.out, d.T, dW, ld_dw, extent(d.T, d.in, d.ldx, 2), extent(d.T, d.out, d.lddy, 2), extent(d.out, d.in, ld_dw, 4)};
   OptArgs a{};
-  return g_pick<WgradBig, WgradSmall, WgradSplit, WgradBand>(
+  return g_pick<WgradBig, WgradSmall, WgradSplit, WgradBand, WgradTiny>(
       g, [&](auto c, const GArgs& gc) { return g_launch<decltype(c), G_EPI_STORE, FORGE_SGD, ST_F32, false>(gc, a, st); });
 }
 
@@ -86,7 +86,7 @@ hipError_t launch_dgrad_bf16(const void* dY, int64_t lddy, const void* W, int64_
   GArgs g{W, dY, ldw, lddy,
           n_in, T, n_out, dX, lddx, extent(n_out, n_in, ldw, 2), extent(T, n_out, lddy, 2), extent(T, n_in, lddx, 2)};
   OptArgs a{};
-  return g_pick<DgradBig, DgradSmall, DgradSplit, DgradBand>(
+  return g_pick<DgradBig, DgradSmall, DgradSplit, DgradBand, DgradTiny>(
       g, [&](auto c, const GArgs& gc) { return g_launch<decltype(c), G_EPI_DX, FORGE_SGD, ST_F32, false>(gc, a, st); });
 }
 

@@ -134,6 +134,8 @@ struct GCfg {
   // Chunk swizzles (XOR of the 16-byte chunk index of a row):
   //  * rows read with the 16-bit transpose read: 4 * (row % 4), so the four rows one read
   //    touches land in four different 64-byte bank groups (16 or more chunks per row);
+  //    rows of 8 chunks (128 bytes, two rows per 256-byte bank period): 4 * ((row / 2) % 2),
+  //    so rows r and r + 2 of those four take the other 64-byte half of their row;
   //  * rows read with the 8-bit transpose read (8 rows x 32 bytes per half-wave): with
   //    16 or more chunks per row 2 * (row % 8), with 8 chunks 2 * ((row / 2) % 4), so the
   //    eight 32-byte pieces fall in eight different 32-byte bank groups;
@@ -144,11 +146,11 @@ struct GCfg {
   static constexpr int KW = B_TR ? 1 : 16 / B_CPR;
   static constexpr int TR_PERIOD = F8 ? 8 : 4;
   __host__ __device__ static constexpr int swz_tr(int row, int cpr) {
-    return F8 ? (cpr >= 16 ? 2 * (row & 7) : 2 * ((row >> 1) & 3)) : 4 * (row & 3);
+    return F8 ? (cpr >= 16 ? 2 * (row & 7) : 2 * ((row >> 1) & 3)) : (cpr >= 16 ? 4 * (row & 3) : 4 * ((row >> 1) & 1));
   }
   __host__ __device__ static constexpr int swz_b(int row) { return B_TR ? swz_tr(row, B_CPR) : (row / KW) % B_CPR; }
-  static_assert((F8 ? A_CPR >= 8 : A_CPR >= 16) && (NT / A_CPR) % TR_PERIOD == 0, "A swizzle");
-  static_assert(B_TR ? ((F8 ? B_CPR >= 8 : B_CPR >= 16) && (NT / B_CPR) % TR_PERIOD == 0)
+  static_assert(A_CPR >= 8 && (NT / A_CPR) % TR_PERIOD == 0, "A swizzle");
+  static_assert(B_TR ? (B_CPR >= 8 && (NT / B_CPR) % TR_PERIOD == 0)
                      : ((B_CPR == 4 || B_CPR == 8) && (NT / B_CPR) % 16 == 0), "B swizzle");
   // transpose reads per operand fragment and the k rows one read covers
   static constexpr int RA = F8 ? 4 : 2, RSTEP = F8 ? 8 : 4;
@@ -885,7 +887,8 @@ void gemm_kernel(GArgs g, OptArgs a) {
 // 2-way in-workgroup split-K (8 waves of 64x64, one workgroup per compute unit), so
 // a compute unit that holds a single tile still runs two waves per SIMD. A last round of 256x256
 // tiles that would be at most half full is replaced by a second launch of 256x128
-// tiles (8 waves of 128x64, 2-way in-workgroup split-K) over the rest of C.
+// tiles (8 waves of 128x64, 2-way in-workgroup split-K) over the rest of C. Split-K
+// tiles that would fill at most half of the compute units become 64x128 tiles.
 // ---------------------------------------------------------------------------
 // Tile configurations (BM, BN, BK, WM, WN, B_TR, OCC[, NSTAGE, KS]); FORGE_*_CFG
 // override them at build time for tuning sweeps.
@@ -909,6 +912,15 @@ void gemm_kernel(GArgs g, OptArgs a) {
 #endif
 #ifndef FORGE_DGRAD_BAND_CFG
 #define FORGE_DGRAD_BAND_CFG 256, 128, 64, 2, 2, false, 2, 2, 2
+#endif
+// scarce 128x128 tiles (fewer than half the compute units): 64x128 tiles, 64 columns of the
+// A side (in) by 128 of the B side, 8 waves of 32x64 in two k-split groups, so a problem
+// with 128 or 512 output rows covers twice as many compute units
+#ifndef FORGE_WGRAD_TINY_CFG
+#define FORGE_WGRAD_TINY_CFG 64, 128, 64, 2, 2, true, 2, 4, 2
+#endif
+#ifndef FORGE_DGRAD_TINY_CFG
+#define FORGE_DGRAD_TINY_CFG 64, 128, 64, 2, 2, false, 2, 4, 2
 #endif
 #ifndef FORGE_DGRAD_BIG_CFG
 #define FORGE_DGRAD_BIG_CFG 256, 256, 32, 2, 4, false, 2, 4, 1, G_BF16, 0, 0, FORGE_BIG_PP
@@ -936,6 +948,8 @@ using WgradBig = GCfg<FORGE_WGRAD_BIG_CFG>;
 using WgradSmall = GCfg<FORGE_WGRAD_SMALL_CFG>;
 using WgradSplit = GCfg<FORGE_WGRAD_SPLIT_CFG>;
 using WgradBand = GCfg<FORGE_WGRAD_BAND_CFG>;
+using WgradTiny = GCfg<FORGE_WGRAD_TINY_CFG>;
+using DgradTiny = GCfg<FORGE_DGRAD_TINY_CFG>;
 using DgradBand = GCfg<FORGE_DGRAD_BAND_CFG>;
 using DgradBig = GCfg<FORGE_DGRAD_BIG_CFG>;
 using DgradSmall = GCfg<FORGE_DGRAD_SMALL_CFG>;
@@ -976,7 +990,7 @@ static int g_tiles(const GArgs& g) {
 // band holds more of them), and the rest of C runs as a second launch on the same
 // stream: Band tiles (half a large tile) when they fit in one round, else 128x128
 // tiles. Each tile still owns its output elements outright.
-template <class Big, class Small, class Split, class Band, class F>
+template <class Big, class Small, class Split, class Band, class Tiny = Split, class F>
 static hipError_t g_pick(const GArgs& g, F&& f) {
   const int cus = g_num_cus();
   const int tiles = g_tiles<Big>(g);
@@ -1004,6 +1018,9 @@ static hipError_t g_pick(const GArgs& g, F&& f) {
   // tiles' two rounds (their per-CU rate is lower: twice the operand bytes per flop)
   if (2 * tiles > cus) return f(Big{}, g);
   if (g_tiles<Small>(g) >= 2 * cus) return f(Small{}, g);
+  // split-K tiles that would leave compute units idle: the narrower tiles when they still
+  // fit in one round
+  if (g_tiles<Tiny>(g) > g_tiles<Split>(g) && g_tiles<Tiny>(g) <= cus) return f(Tiny{}, g);
   return f(Split{}, g);
 }
 
@@ -1032,7 +1049,7 @@ static hipError_t g_launch_opt(int sf, int sr, const GArgs& g, const OptArgs& a,
 
 template <int OPT>
 hipError_t wgrad_fused_bf16_opt(int sf, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
-  return g_pick<WgradBig, WgradSmall, WgradSplit, WgradBand>(
+  return g_pick<WgradBig, WgradSmall, WgradSplit, WgradBand, WgradTiny>(
       g, [&](auto c, const GArgs& gc) { return g_launch_opt<decltype(c), OPT>(sf, sr, gc, a, st); });
 }
 

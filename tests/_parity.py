@@ -197,7 +197,8 @@ def wgrad_tile_order(out, inn, cus):
     (one chain) when there are at least `cus` of them, with a last round that would be at most
     half full moved to 256x128 tiles with a 2-way k-split over a band of rows or columns, or
     when there are more than cus / 2 of them (one partial round); 128x128 tiles (one chain)
-    when at least 2 * cus of those; else 128x128 tiles with a k-split.
+    when at least 2 * cus of those; else 128x128 or 64x128 tiles with a k-split (the same
+    alternate 32-token halves of each 64-token stage, so the same order).
     Returns a function row -> order, or None when the order depends on the column."""
     ntm, ntn = -(-inn // 256), -(-out // 256)
     tiles = ntm * ntn

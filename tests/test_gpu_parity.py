@@ -124,7 +124,9 @@ def _tile_config_shapes():
     """(rows, cols) of C = (in, out) for wgrad or (in, T) for dgrad that select each
     tile configuration of the launcher on this device: 256x256 tiles when there are
     at least as many as compute units, else 128x128 tiles when there are at least two
-    per compute unit, else 128x128 tiles with the in-workgroup split-K.
+    per compute unit, else 128x128 tiles with the in-workgroup split-K, or 64x128 split-K
+    tiles (tiny) when those fit in one round and the 128x128 ones would leave compute
+    units idle.
     The band_* shapes (256 compute units) leave a last round of 256x256 tiles at most
     half full, so the launcher runs the whole rounds over a band of tile columns or rows
     and the rest as a second launch: band_n (column band, ragged 256x128 rest), band_m
@@ -133,13 +135,15 @@ def _tile_config_shapes():
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     big = (4096, 256 * -(-cus // 16))
     small = (4096, 128 * -(-cus // 16))
-    split = (1024, 520)
+    split = (2560, 1280)
+    tiny = (4096, 128)
     cdiv = lambda a, b: -(-a // b)
-    tiles = lambda mn, t: cdiv(mn[0], t) * cdiv(mn[1], t)
+    tiles = lambda mn, t, tn=None: cdiv(mn[0], t) * cdiv(mn[1], tn or t)
     assert tiles(big, 256) >= cus
-    assert tiles(small, 256) < cus and tiles(small, 128) >= 2 * cus
-    assert tiles(split, 256) < cus and tiles(split, 128) < 2 * cus
-    shapes = {"big": big, "small": small, "split": split}
+    assert 2 * tiles(small, 256) <= cus and tiles(small, 128) >= 2 * cus
+    assert 2 * tiles(split, 256) <= cus and tiles(split, 128) < 2 * cus and tiles(split, 64, 128) > cus
+    assert 2 * tiles(tiny, 256) <= cus and tiles(tiny, 128) < tiles(tiny, 64, 128) <= cus
+    shapes = {"big": big, "small": small, "split": split, "tiny": tiny}
     if cus == 256:
         shapes.update(band_n=(4096, 4416), band_m=(4416, 4096), band_full=(4096, 6144), band_small=(5120, 4864))
         for k in ("band_n", "band_m", "band_full", "band_small"):
@@ -154,7 +158,7 @@ def _shape(cfg):
     return sh[cfg]
 
 
-CONFIGS = ["big", "small", "split", "band_n", "band_m", "band_full", "band_small"]
+CONFIGS = ["big", "small", "split", "tiny", "band_n", "band_m", "band_full", "band_small"]
 
 
 @pytest.mark.parametrize("cfg", CONFIGS)
