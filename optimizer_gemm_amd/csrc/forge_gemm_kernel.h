@@ -73,6 +73,11 @@ enum { G_EPI_STORE = 0, G_EPI_OPT = 1, G_EPI_DX = 2 };
 #ifndef FORGE_EPI_SCHED_BARRIER
 #define FORGE_EPI_SCHED_BARRIER 1
 #endif
+// tiles without a k-split: each wave writes out its own accumulators (no workgroup
+// barriers in the epilogue)
+#ifndef FORGE_EPI_WAVE
+#define FORGE_EPI_WAVE 1
+#endif
 
 // issue priority of a ping-pong wave over its compute phase
 #ifndef FORGE_PP_PRIO
@@ -120,7 +125,8 @@ struct GCfg {
   static_assert(NSTAGE >= 2, "ring");
   static constexpr int a_base(int buf) { return buf * A_BYTES; }
   static constexpr int b_base(int buf) { return NSTAGE * A_BYTES + buf * B_BYTES; }
-  static constexpr int EPI_BYTES = TN * (BM + 4) * 4;
+  // (KS = 1: each wave stages 32 rows of its TM columns at a time; else one TN-row chunk)
+  static constexpr int EPI_BYTES = KS == 1 ? NW * 32 * (TM + 4) * 4 : TN * (BM + 4) * 4;
   static constexpr int RING_BYTES = NSTAGE * (A_BYTES + B_BYTES);
   static constexpr int SMEM_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
   static constexpr int A_CPR = ROWA / 16, B_CPR = ROWB / 16;  // 16-byte chunks per row
@@ -754,41 +760,20 @@ void gemm_kernel(GArgs g, OptArgs a) {
         }
       }
     };
-    float* E = reinterpret_cast<float*>(smem);
-    constexpr int LDE = C::BM + 4;
-    constexpr int VPR = C::BM / 4;                   // 4-element vectors per row
-    constexpr int NV = C::TN * VPR / C::NT;          // vectors per thread per chunk
-    static_assert((C::TN * VPR) % C::NT == 0, "chunk must split evenly over threads");
-    static_assert(VPR % 16 == 0, "an INT8 block of 64 must be 16 adjacent lanes");
-    __syncthreads();  // every wave is done reading the operand stages
-#pragma unroll 1
-    for (int c = 0; c < C::WN; ++c) {
-      // k-split group 0 writes its partial tile, groups 1.. add theirs in order
-#pragma unroll 1
-      for (int kg = 0; kg < C::KS; ++kg) {
-        if (wn == c && ks == kg) {
-#pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-            for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                f32x4* e = reinterpret_cast<f32x4*>(E + (32 * fn + l32) * LDE + wave_m0 + 32 * fm + 8 * q + 4 * hi);
-                f32x4 x{acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3]};
-                if (kg > 0) x = *e + x;
-                *e = x;
-              }
-        }
-        __syncthreads();
-      }
-      const int nrow0 = n0 + c * C::TN;
+    // One staged block of the finished tile, as float rows of pitch LD holding VPRc 4-element
+    // vectors each: NTHR threads (this one is t) take NVc vectors each; row r, column c of the
+    // block is output row obase + r, column ibase + c.
+    auto proc = [&](const float* Es, auto ld_c, auto vpr_c, auto nv_c, auto nthr_c, int t, int obase, int ibase) {
+      constexpr int LD = decltype(ld_c)::value, VPRc = decltype(vpr_c)::value, NVc = decltype(nv_c)::value;
+      constexpr int NTHR = decltype(nthr_c)::value;
+      static_assert(VPRc % 16 == 0, "an INT8 block of 64 must be 16 adjacent lanes");
       if constexpr (EPI == G_EPI_STORE || EPI == G_EPI_DX) {
         const __amdgpu_buffer_rsrc_t rO = make_rsrc(g.out, g.out_bytes);
 #pragma unroll
-        for (int k = 0; k < NV; ++k) {
-          const int vi = tid + k * C::NT, row = vi / VPR, col = (vi % VPR) * 4;
-          const int n = nrow0 + row, m = m0 + col;
-          f32x4 x = *reinterpret_cast<const f32x4*>(E + row * LDE + col);
+        for (int k = 0; k < NVc; ++k) {
+          const int vi = t + k * NTHR, row = vi / VPRc, col = (vi % VPRc) * 4;
+          const int n = obase + row, m = ibase + col;
+          f32x4 x = *reinterpret_cast<const f32x4*>(Es + row * LD + col);
           if constexpr (C::F8) x = x * gscale;
           const bool ok = n < g.N && m < g.M;
           if constexpr (EPI == G_EPI_STORE) {
@@ -806,11 +791,11 @@ void gemm_kernel(GArgs g, OptArgs a) {
         // loads of KB vectors are issued before any of them is consumed; KB bounds the
         // registers a batch holds next to the accumulators still to be written out
         constexpr int KB_MAX = Q8 && C::OCC >= 2 ? 1 : FORGE_EPI_KB;
-        constexpr int KB = NV > KB_MAX ? KB_MAX : NV;
+        constexpr int KB = NVc > KB_MAX ? KB_MAX : NVc;
         // at most 8 batches unrolled (the one-wave FP8 tiles have 32 vectors per thread and
         // chunk: unrolling all of them exhausts the scalar registers)
 #pragma unroll 8
-        for (int kb = 0; kb < NV; kb += KB) {
+        for (int kb = 0; kb < NVc; kb += KB) {
         uint32_t ow[KB], om[KB], ov_[KB], osc[KB];
         u32x2 wb[KB], mb[KB], vb[KB];
         f32x4 mv[KB], vv[KB];
@@ -818,8 +803,8 @@ void gemm_kernel(GArgs g, OptArgs a) {
         float msc[KB], vsc[KB];
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
-          const int vi = tid + (kb + k) * C::NT, row = vi / VPR, col = (vi % VPR) * 4;
-          const int o = nrow0 + row, i = m0 + col;
+          const int vi = t + (kb + k) * NTHR, row = vi / VPRc, col = (vi % VPRc) * 4;
+          const int o = obase + row, i = ibase + col;
           const bool ok = o < g.N && i < g.M;
           ow[k] = ok ? (uint32_t)(o * a.ldw + i) * 2u : kOOB;
           wb[k] = __builtin_amdgcn_raw_buffer_load_b64(R.W, ow[k], 0, FORGE_EPI_LD_CPOL);
@@ -851,9 +836,9 @@ void gemm_kernel(GArgs g, OptArgs a) {
         }
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
-          const int vi = tid + (kb + k) * C::NT, row = vi / VPR, col = (vi % VPR) * 4;
-          const int o = nrow0 + row, i = m0 + col;
-          const f32x4 gx = *reinterpret_cast<const f32x4*>(E + row * LDE + col);
+          const int vi = t + (kb + k) * NTHR, row = vi / VPRc, col = (vi % VPRc) * 4;
+          const int o = obase + row, i = ibase + col;
+          const f32x4 gx = *reinterpret_cast<const f32x4*>(Es + row * LD + col);
           u32x4 mr{0u, 0u, 0u, 0u}, vr{0u, 0u, 0u, 0u};
           float ms_k = 0.f, vs_k = 0.f;
           if constexpr (B16S) {
@@ -873,7 +858,67 @@ void gemm_kernel(GArgs g, OptArgs a) {
 #endif
         }
       }
+    };
+    __syncthreads();  // every wave is done reading the operand stages
+    if constexpr (C::KS == 1 && FORGE_EPI_WAVE) {
+      // Each wave stages its own accumulators, one 32-row block (fn) at a time, in a private
+      // LDS region and writes them out itself: no workgroup barrier between blocks, so the
+      // waves' load, arithmetic and store phases drift apart instead of running in step.
+      constexpr int LDW = C::TM + 4;
+      static_assert(C::NW * 32 * LDW * 4 <= C::SMEM_BYTES, "wave staging fits the workgroup's LDS");
+      float* Ew = reinterpret_cast<float*>(smem) + wave_u * (32 * LDW);
+      // fn is a run-time loop (one copy of the block's processing); the accumulators are
+      // selected with compile-time indices under a uniform branch, so they stay in registers
+#pragma unroll 1
+      for (int fn = 0; fn < C::FN; ++fn) {
+#pragma unroll
+        for (int f = 0; f < C::FN; ++f) {
+          if (f == fn) {
+#pragma unroll
+            for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<f32x4*>(Ew + l32 * LDW + 32 * fm + 8 * q + 4 * hi) =
+                    f32x4{acc[fm][f][4 * q], acc[fm][f][4 * q + 1], acc[fm][f][4 * q + 2], acc[fm][f][4 * q + 3]};
+          }
+        }
+        // the other lanes' rows are written (and, after the block, read) before going on
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        proc(Ew, std::integral_constant<int, LDW>{}, std::integral_constant<int, C::TM / 4>{},
+             std::integral_constant<int, C::TM / 8>{}, std::integral_constant<int, 64>{}, lane,
+             n0 + wave_n0 + 32 * fn, m0 + wave_m0);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
+    } else {
+    float* E = reinterpret_cast<float*>(smem);
+    constexpr int LDE = C::BM + 4;
+    constexpr int VPR = C::BM / 4;                   // 4-element vectors per row
+    constexpr int NV = C::TN * VPR / C::NT;          // vectors per thread per chunk
+    static_assert((C::TN * VPR) % C::NT == 0, "chunk must split evenly over threads");
+#pragma unroll 1
+    for (int c = 0; c < C::WN; ++c) {
+      // k-split group 0 writes its partial tile, groups 1.. add theirs in order
+#pragma unroll 1
+      for (int kg = 0; kg < C::KS; ++kg) {
+        if (wn == c && ks == kg) {
+#pragma unroll
+          for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+            for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                f32x4* e = reinterpret_cast<f32x4*>(E + (32 * fn + l32) * LDE + wave_m0 + 32 * fm + 8 * q + 4 * hi);
+                f32x4 x{acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3]};
+                if (kg > 0) x = *e + x;
+                *e = x;
+              }
+        }
+        __syncthreads();
+      }
+      proc(E, std::integral_constant<int, LDE>{}, std::integral_constant<int, VPR>{}, std::integral_constant<int, NV>{},
+           std::integral_constant<int, C::NT>{}, tid, n0 + c * C::TN, m0);
       __syncthreads();  // the chunk's LDS rows are consumed before the next chunk overwrites them
+    }
     }
     }
   }
