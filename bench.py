@@ -59,6 +59,10 @@ def parse():
                    help="llama8b_mlp_train_8192: number of SwiGLU MLP blocks in the model")
     p.add_argument("--cold-calls", type=int, default=10,
                    help="fused calls of the first layer timed after a 1 GiB write that evicts the memory-side cache")
+    p.add_argument("--group", action="store_true",
+                   help="decoder-layer workloads (llama8b_layer_8192, llama8b_tp8_8192, stack): the layers that share "
+                        "an input (q, k, v; gate, up) take one grouped fused step (forge_linear_wgrad_step_group) "
+                        "on one X")
     p.add_argument("--opt", default="adamw")
     p.add_argument("--states", default=None, choices=("f32", "bf16", "q8", "q8dyn"),
                    help="moment storage format (default: the workload's)")
@@ -395,17 +399,43 @@ def main() -> int:
 
     step_counter = [0]
 
+    # units of the step: one layer each, or (--group) the layers of a decoder layer that share an
+    # input (q, k, v and gate, up, in the order q, k, v, o, gate, up, down) as one grouped step
+    units = [[k] for k in range(len(per_layer))]
+    if args.group:
+        if args.workload not in ("llama8b_layer_8192", "llama8b_tp8_8192", "stack") or fp8:
+            print("--group needs a decoder-layer workload with bf16 inputs", file=sys.stderr)
+            return 2
+        units = []
+        for b in range(0, len(per_layer), 7):
+            units += [[b, b + 1, b + 2], [b + 3], [b + 4, b + 5], [b + 6]]
+
     def one_step(fused_events=None):
         step_counter[0] += 1
         t = step_counter[0]
-        for k, (spec, W, m, v, ms, vs, seed) in enumerate(per_layer):
-            X, dY, dX, xs, ds, dYf = shape_bufs[(spec.out, spec.inn, spec.T)]
-            forge.dgrad(dY, W, dX)
+        for unit in units:
+            for k in unit:
+                spec, W = per_layer[k][0], per_layer[k][1]
+                X, dY, dX, xs, ds, dYf = shape_bufs[(spec.out, spec.inn, spec.T)]
+                forge.dgrad(dY, W, dX)
+            k0 = unit[0]
             if fused_events is not None:
-                fused_events[k][0].record()
-            wstep(X, dYf, W, m, v, opt, hyper, t, seed, ms, vs, x_scale=xs, dy_scale=ds)
+                fused_events[k0][0].record()
+            if len(unit) == 1:
+                spec, W, m, v, ms, vs, seed = per_layer[k0]
+                X, dY, dX, xs, ds, dYf = shape_bufs[(spec.out, spec.inn, spec.T)]
+                wstep(X, dYf, W, m, v, opt, hyper, t, seed, ms, vs, x_scale=xs, dy_scale=ds)
+            else:
+                mem = [per_layer[k] for k in unit]
+                bufs = [shape_bufs[(L[0].out, L[0].inn, L[0].T)] for L in mem]
+                forge.wgrad_step_group(bufs[0][0], [b[5] for b in bufs], [L[1] for L in mem], [L[2] for L in mem],
+                                       [L[3] for L in mem], opt, hyper, t, [L[6] for L in mem],
+                                       [L[4] for L in mem], [L[5] for L in mem], code=code)
             if fused_events is not None:
-                fused_events[k][1].record()
+                fused_events[k0][1].record()
+                for k in unit[1:]:  # the group's time is the first member's
+                    fused_events[k][0].record()
+                    fused_events[k][1].record()
 
     for _ in range(args.warmup):
         one_step()
@@ -569,7 +599,9 @@ def main() -> int:
         "config": {"workload": args.workload, "layers": len(layers),
                    "shapes": sorted({f"{s.out}x{s.inn}" for s in layers}), "tokens": layers[0].T,
                    "optimizer": opt, "states": state, "stochastic_round": bool(sr), "inputs": args.inputs,
-                   "step": "dgrad(old W) then fused wgrad+optimizer, per layer"},
+                   "step": ("dgrad(old W) of each layer, then its fused wgrad+optimizer step; q,k,v and gate,up "
+                            "each take one grouped fused step after their dgrads" if args.group else
+                            "dgrad(old W) then fused wgrad+optimizer, per layer")},
         "fused_ms_per_layer": [round(float(x), 4) for x in fused_ms_layer][:8],
         "fused_tflops": round(fused_tflops, 2),
         "fused_call_us": call_stats,

@@ -176,6 +176,29 @@ int forge_linear_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge
                             int64_t step, uint64_t seed, forge_stream_t stream);
 
 /*
+ * The fused step of several layers that read the same input X (the q, k, v projections
+ * of an attention block, or gate and up of an MLP), in one launch whose grid holds all
+ * their tiles; for a small layer (a few hundred output rows) that is the difference
+ * between a few and all of the compute units being busy. Layer l has its own gradient
+ * dY[l] [T, out_l], weights W[l] [out_l, in] and moments m[l], v[l] (arrays of
+ * n_layers descriptors; m or v may be NULL when the optimizer keeps no such slot), and
+ * its own seed seeds[l]; opt, hyper and step are common. Each layer is updated exactly
+ * as forge_linear_wgrad_step would update it (same element indices and random streams),
+ * except that the tile shape, and so the order of the FP32 summation over tokens, is
+ * chosen for the group as a whole. bfloat16 X, dY and W only (FP8 inputs and fp32 layers:
+ * FORGE_ERR_UNSUPPORTED); every layer's moments in the same format.
+ * 1 <= n_layers <= FORGE_MAX_GROUP, else FORGE_ERR_SHAPE. Every argument check of
+ * forge_linear_wgrad_step applies to each layer; in addition no layer's W, m, v or block
+ * scales may overlap any other layer's tensors (FORGE_ERR_ALIAS). Nothing is enqueued
+ * on an error. Must be enqueued after each layer's forge_linear_dgrad.
+ */
+#define FORGE_MAX_GROUP 4
+int forge_linear_wgrad_step_group(const forge_tensor* X, int32_t n_layers, const forge_tensor* dY,
+                                  forge_tensor* W, forge_tensor* m, forge_tensor* v, int32_t opt,
+                                  const forge_hyper* hyper, int64_t step, const uint64_t* seeds,
+                                  forge_stream_t stream);
+
+/*
  * Input gradient dX = dY W (§5, limitations: read before the weight update).
  * dY [T, out], W [out, in], dX [T, in]; all FORGE_F32, or all FORGE_BF16
  * (bf16 output rounded to nearest-even from the FP32 accumulator). FP8 dY returns

@@ -108,7 +108,7 @@ int check_states(int opt, int io_dtype, const forge_tensor* W, const forge_tenso
   for (int k = 0; k < 2; ++k) {
     if (!(sl & (1 << k))) continue;
     const forge_tensor* t = slot[k];
-    if (!t || !t->data) return FORGE_ERR_NULL;
+    if (!t || (!t->data && t->rows != 0 && t->cols != 0)) return FORGE_ERR_NULL;  // empty states may be NULL
     int r = check_shape(t);
     if (r) return r;
     if (t->rows != W->rows || t->cols != W->cols) return FORGE_ERR_SHAPE;
@@ -441,6 +441,45 @@ int forge_linear_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge
                                               dY->scale, p.d, p.a, (hipStream_t)stream)
                       : launch_wgrad_fused(p.io == FORGE_BF16, p.fmt, opt, p.sr, X->data, dY->data, p.d, p.a,
                                            (hipStream_t)stream);
+  return e == hipSuccess ? FORGE_OK : FORGE_ERR_HIP;
+}
+
+int forge_linear_wgrad_step_group(const forge_tensor* X, int32_t n_layers, const forge_tensor* dY, forge_tensor* W,
+                                  forge_tensor* m, forge_tensor* v, int32_t opt, const forge_hyper* hyper,
+                                  int64_t step, const uint64_t* seeds, forge_stream_t stream) {
+  if (!X || !dY || !W || !seeds) return FORGE_ERR_NULL;
+  if (n_layers < 1 || n_layers > FORGE_MAX_GROUP) return FORGE_ERR_SHAPE;
+  StepPlan p[FORGE_MAX_GROUP];
+  for (int l = 0; l < n_layers; ++l) {
+    int r = plan_step(X, &dY[l], &W[l], m ? &m[l] : nullptr, v ? &v[l] : nullptr, opt, hyper, step, seeds[l],
+                      nullptr, 0, &p[l]);
+    if (r) return r;
+    if (p[l].f8 || p[l].io != FORGE_BF16) return FORGE_ERR_UNSUPPORTED;
+    if (p[l].fmt != p[0].fmt) return FORGE_ERR_DTYPE;
+  }
+  // a layer's outputs overlap no other layer's tensors (each plan checked its own)
+  const int sl = opt_slots(opt);
+  const forge_tensor* outs[3 * FORGE_MAX_GROUP];
+  const forge_tensor* ins[FORGE_MAX_GROUP + 1];
+  int n_out = 0;
+  ins[0] = X;
+  for (int l = 0; l < n_layers; ++l) {
+    outs[n_out++] = &W[l];
+    outs[n_out++] = (sl & 1) ? &m[l] : nullptr;
+    outs[n_out++] = (sl & 2) ? &v[l] : nullptr;
+    ins[l + 1] = &dY[l];
+  }
+  int r = check_alias(outs, n_out, ins, n_layers + 1);
+  if (r) return r;
+  GroupLayer layers[FORGE_MAX_GROUP];
+  int n = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    if (p[l].empty) continue;  // no weights: nothing to update
+    layers[n++] = GroupLayer{dY[l].data, dY[l].ld, p[l].a};
+  }
+  if (n == 0) return FORGE_OK;
+  const StepPlan& p0 = p[0];
+  hipError_t e = launch_wgrad_fused_bf16_group(p0.fmt, opt, p0.sr, X->data, p0.d, layers, n, (hipStream_t)stream);
   return e == hipSuccess ? FORGE_OK : FORGE_ERR_HIP;
 }
 

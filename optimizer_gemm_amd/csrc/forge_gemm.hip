@@ -43,6 +43,45 @@ hipError_t launch_wgrad_fused_bf16(int state_fmt, int opt, int sr, const void* X
   }
 }
 
+hipError_t launch_wgrad_fused_bf16_group(int state_fmt, int opt, int sr, const void* X, const GemmDims& d,
+                                         const GroupLayer* layers, int n, hipStream_t st) {
+  if (n < 1 || n > kMaxGroup) return hipErrorInvalidValue;
+  GroupArgs gr{};
+  gr.count = n;
+  for (int j = 0; j < n; ++j) {
+    const OptArgs& a = layers[j].a;
+    GroupMember& M = gr.mb[j];
+    M.B = layers[j].dY;
+    M.ldb = layers[j].lddy;
+    M.b_bytes = extent(d.T, a.out, layers[j].lddy, 2);
+    M.N = a.out;
+    M.W = a.W;
+    M.m = a.m;
+    M.v = a.v;
+    M.m_scale = a.m_scale;
+    M.v_scale = a.v_scale;
+    M.ldw = a.ldw;
+    M.ldm = a.ldm;
+    M.ldv = a.ldv;
+    M.rng_base = a.rng_base;
+  }
+  // the A operand and the sizes common to the members; B and N come from each member
+  GArgs g{X, layers[0].dY, d.ldx, layers[0].lddy, d.in, layers[0].a.out, d.T, nullptr, 0,
+          extent(d.T, d.in, d.ldx, 2), gr.mb[0].b_bytes, 0};
+  const OptArgs& a = layers[0].a;
+  switch (opt) {
+    case FORGE_ADAMW: return wgrad_fused_bf16_group_opt<FORGE_ADAMW>(state_fmt, sr, g, a, gr, st);
+    case FORGE_SGD: return wgrad_fused_bf16_group_opt<FORGE_SGD>(state_fmt, sr, g, a, gr, st);
+    case FORGE_SGD_MOMENTUM: return wgrad_fused_bf16_group_opt<FORGE_SGD_MOMENTUM>(state_fmt, sr, g, a, gr, st);
+    case FORGE_LION: return wgrad_fused_bf16_group_opt<FORGE_LION>(state_fmt, sr, g, a, gr, st);
+    case FORGE_RMSPROP: return wgrad_fused_bf16_group_opt<FORGE_RMSPROP>(state_fmt, sr, g, a, gr, st);
+    case FORGE_ADAGRAD: return wgrad_fused_bf16_group_opt<FORGE_ADAGRAD>(state_fmt, sr, g, a, gr, st);
+    case FORGE_NADAM: return wgrad_fused_bf16_group_opt<FORGE_NADAM>(state_fmt, sr, g, a, gr, st);
+    case FORGE_RADAM: return wgrad_fused_bf16_group_opt<FORGE_RADAM>(state_fmt, sr, g, a, gr, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_wgrad_store_bf16(const void* X, const void* dY, const GemmDims& d, float* dW, int64_t ld_dw,
                                    hipStream_t st) {
   GArgs g{X, dY, d.ldx, d.lddy,

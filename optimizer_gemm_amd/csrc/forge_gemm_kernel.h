@@ -182,6 +182,30 @@ struct GArgs {
   int32_t m_off, n_off;
 };
 
+// A grouped fused step: up to kMaxGroup layers that share the A operand (X) and the
+// optimizer, each with its own dY, W, moments and seed, in one launch. Member j owns the
+// tile columns [tn1 of member j-1, tn1 of member j) of the launch; inside them everything
+// (rows, element indices, random streams) is the member's own, as in a launch of its own.
+constexpr int kMaxGroup = FORGE_MAX_GROUP;
+struct GroupMember {
+  const void* B;
+  int64_t ldb;
+  uint32_t b_bytes;
+  int32_t N;    // the member's rows of C (its out)
+  int32_t tn1;  // one past its last tile column in the launch
+  void* W;
+  void* m;
+  void* v;
+  float* m_scale;
+  float* v_scale;
+  int64_t ldw, ldm, ldv;
+  uint64_t rng_base;
+};
+struct GroupArgs {
+  int32_t count;  // 0: not a grouped launch
+  GroupMember mb[kMaxGroup];
+};
+
 template <class C>
 __host__ __device__ inline int g_ntm(const GArgs& g) { return (g.M - g.m_off + C::BM - 1) / C::BM; }
 template <class C>
@@ -316,7 +340,7 @@ __device__ __forceinline__ EpiRes epi_res(const OptArgs& a) {
 // SF: moment storage format (StateFmt: float32, INT8 block-64, or bfloat16).
 template <class C, int EPI, int OPT, int SF, bool SR>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
-void gemm_kernel(GArgs g, OptArgs a) {
+void gemm_kernel(GArgs g, OptArgs a, GroupArgs gr) {
   // Q8: INT8 codes with block scales, linear (ST_Q8) or the dynamic code (ST_Q8D)
   constexpr bool Q8D = SF == ST_Q8D, Q8 = SF == ST_Q8 || Q8D, B16S = SF == ST_BF16;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::SMEM_BYTES];
@@ -337,7 +361,6 @@ void gemm_kernel(GArgs g, OptArgs a) {
   const int l32 = lane & 31, hi = lane >> 5;
 
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A, g.a_bytes);
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.B, g.b_bytes);
   // FP8 operands: the gradient is the product of the two dequantisation scales times
   // the sum of code products
   const float gscale = C::F8 ? g.a_scale[0] * g.b_scale[0] : 1.f;
@@ -355,8 +378,6 @@ void gemm_kernel(GArgs g, OptArgs a) {
 
   constexpr int A_RSTEP = C::NT / C::A_CPR, B_RSTEP = C::NT / C::B_CPR;
   const uint32_t a_rowb = (uint32_t)(A_RSTEP * g.lda * C::EB), a_stageb = (uint32_t)(C::BK * g.lda * C::EB);
-  const uint32_t b_rowb = (uint32_t)(B_RSTEP * g.ldb * C::EB);
-  const uint32_t b_stageb = C::B_TR ? (uint32_t)(C::BK * g.ldb * C::EB) : (uint32_t)(C::BK * C::EB);
   const uint32_t lds0 = lds_addr(smem);
   // A wave of k-split group ks reads k-steps ks*KPW .. ks*KPW + KPW-1 of each stage.
   const int kr0 = ks * C::KPW * C::KSTEP;  // first k row of this wave in a stage
@@ -364,6 +385,42 @@ void gemm_kernel(GArgs g, OptArgs a) {
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     int tm, tn;
     g_tile(tile, ntm, ntn, tm, tn);
+    // the tile's layer (a grouped launch): its B operand, rows and pitch, and the
+    // epilogue's tensors and random stream; chosen with uniform selects
+    const void* t_B = g.B;
+    uint32_t t_b_bytes = g.b_bytes;
+    int64_t gt_ldb = g.ldb;
+    int gt_N = g.N;
+    OptArgs at = a;
+    if (gr.count > 0) {
+      int tn0 = 0;
+#pragma unroll
+      for (int j = 0; j < kMaxGroup; ++j) {
+        const int start = j == 0 ? 0 : gr.mb[j - 1].tn1;
+        if (j < gr.count && tn >= start && tn < gr.mb[j].tn1) {
+          const GroupMember& M = gr.mb[j];
+          tn0 = start;
+          t_B = M.B;
+          t_b_bytes = M.b_bytes;
+          gt_ldb = M.ldb;
+          gt_N = M.N;
+          at.W = M.W;
+          at.m = M.m;
+          at.v = M.v;
+          at.m_scale = M.m_scale;
+          at.v_scale = M.v_scale;
+          at.ldw = M.ldw;
+          at.ldm = M.ldm;
+          at.ldv = M.ldv;
+          at.out = M.N;
+          at.rng_base = M.rng_base;
+        }
+      }
+      tn -= tn0;
+    }
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(t_B, t_b_bytes);
+    const uint32_t b_rowb = (uint32_t)(B_RSTEP * gt_ldb * C::EB);
+    const uint32_t b_stageb = C::B_TR ? (uint32_t)(C::BK * gt_ldb * C::EB) : (uint32_t)(C::BK * C::EB);
     const int m0 = g.m_off + tm * C::BM, n0 = g.n_off + tn * C::BN;
     // Per-thread staging offsets and fragment addresses, from an opaque copy of the thread
     // index: recomputed at every tile, so none of them is held (or spilled) through the
@@ -427,9 +484,9 @@ void gemm_kernel(GArgs g, OptArgs a) {
     const uint32_t a_base0 = (uint32_t)((a_row0 * g.lda + m0) * C::EB + a_colb);
     uint32_t b_base0;
     if constexpr (C::B_TR)
-      b_base0 = (uint32_t)((b_row0 * g.ldb + n0) * C::EB + b_colb);
+      b_base0 = (uint32_t)((b_row0 * gt_ldb + n0) * C::EB + b_colb);
     else
-      b_base0 = (uint32_t)((int64_t)(n0 + b_row0) * g.ldb * C::EB + b_colb);
+      b_base0 = (uint32_t)((int64_t)(n0 + b_row0) * gt_ldb * C::EB + b_colb);
     auto dma = [&](auto buf_c, int s) {
       constexpr int buf = decltype(buf_c)::value;
       const int k0 = s * C::BK;
@@ -666,10 +723,10 @@ void gemm_kernel(GArgs g, OptArgs a) {
       constexpr int SL = opt_slots(OPT);
       constexpr bool HAS_M = SL & 1, HAS_V = SL & 2;
       constexpr uint32_t es = Q8 ? 1u : (B16S ? 2u : 4u);
-      const uint32_t ow = ok ? (uint32_t)(o * a.ldw + i) * 2u : kOOB;
-      const uint32_t om = ok ? (uint32_t)(o * a.ldm + i) * es : kOOB;
-      const uint32_t ov = ok ? (uint32_t)(o * a.ldv + i) * es : kOOB;
-      const uint32_t osc = ok ? (uint32_t)(o * (a.in >> 6) + (i >> 6)) * 4u : kOOB;
+      const uint32_t ow = ok ? (uint32_t)(o * at.ldw + i) * 2u : kOOB;
+      const uint32_t om = ok ? (uint32_t)(o * at.ldm + i) * es : kOOB;
+      const uint32_t ov = ok ? (uint32_t)(o * at.ldv + i) * es : kOOB;
+      const uint32_t osc = ok ? (uint32_t)(o * (at.in >> 6) + (i >> 6)) * 4u : kOOB;
       if constexpr (C::F8) gx = gx * gscale;
       const u32x2 mb{mr.x, mr.y}, vb{vr.x, vr.y};
       const f32x4 mv = __builtin_bit_cast(f32x4, mr), vv = __builtin_bit_cast(f32x4, vr);
@@ -709,10 +766,10 @@ void gemm_kernel(GArgs g, OptArgs a) {
         }
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) opt_apply<OPT>(gg[j], w[j], m[j], v[j], a.s);
-      const uint32_t idx0 = (uint32_t)o * (uint32_t)a.in + (uint32_t)i;
+      for (int j = 0; j < 4; ++j) opt_apply<OPT>(gg[j], w[j], m[j], v[j], at.s);
+      const uint32_t idx0 = (uint32_t)o * (uint32_t)at.in + (uint32_t)i;
       uint64_t zz[4];  // one random word per element serves W, m and v
-      rand64x4<SR>(a.rng_base, idx0, zz);
+      rand64x4<SR>(at.rng_base, idx0, zz);
       uint32_t bb[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) bb[j] = SR ? sr_bf16_bits(w[j], rand_field(zz[j], RF_W)) : rne_bf16_bits(w[j]);
@@ -775,7 +832,7 @@ void gemm_kernel(GArgs g, OptArgs a) {
           const int n = obase + row, m = ibase + col;
           f32x4 x = *reinterpret_cast<const f32x4*>(Es + row * LD + col);
           if constexpr (C::F8) x = x * gscale;
-          const bool ok = n < g.N && m < g.M;
+          const bool ok = n < gt_N && m < g.M;
           if constexpr (EPI == G_EPI_STORE) {
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rO,
                                                    ok ? (uint32_t)((n * g.ldo + m) * 4) : kOOB, 0, 0);
@@ -787,7 +844,7 @@ void gemm_kernel(GArgs g, OptArgs a) {
       } else {
         constexpr int SL = opt_slots(OPT);
         constexpr bool HAS_M = SL & 1, HAS_V = SL & 2;
-        const EpiRes R = epi_res<OPT, SF>(a);
+        const EpiRes R = epi_res<OPT, SF>(at);
         // loads of KB vectors are issued before any of them is consumed; KB bounds the
         // registers a batch holds next to the accumulators still to be written out
         constexpr int KB_MAX = Q8 && C::OCC >= 2 ? 1 : FORGE_EPI_KB;
@@ -805,25 +862,25 @@ void gemm_kernel(GArgs g, OptArgs a) {
         for (int k = 0; k < KB; ++k) {
           const int vi = t + (kb + k) * NTHR, row = vi / VPRc, col = (vi % VPRc) * 4;
           const int o = obase + row, i = ibase + col;
-          const bool ok = o < g.N && i < g.M;
-          ow[k] = ok ? (uint32_t)(o * a.ldw + i) * 2u : kOOB;
+          const bool ok = o < gt_N && i < g.M;
+          ow[k] = ok ? (uint32_t)(o * at.ldw + i) * 2u : kOOB;
           wb[k] = __builtin_amdgcn_raw_buffer_load_b64(R.W, ow[k], 0, FORGE_EPI_LD_CPOL);
           if constexpr (B16S) {
-            om[k] = ok ? (uint32_t)(o * a.ldm + i) * 2u : kOOB;
-            ov_[k] = ok ? (uint32_t)(o * a.ldv + i) * 2u : kOOB;
+            om[k] = ok ? (uint32_t)(o * at.ldm + i) * 2u : kOOB;
+            ov_[k] = ok ? (uint32_t)(o * at.ldv + i) * 2u : kOOB;
             if constexpr (HAS_M) mb[k] = __builtin_amdgcn_raw_buffer_load_b64(R.m, om[k], 0, FORGE_EPI_LD_CPOL);
             if constexpr (HAS_V) vb[k] = __builtin_amdgcn_raw_buffer_load_b64(R.v, ov_[k], 0, FORGE_EPI_LD_CPOL);
           } else if constexpr (!Q8) {
-            om[k] = ok ? (uint32_t)(o * a.ldm + i) * 4u : kOOB;
-            ov_[k] = ok ? (uint32_t)(o * a.ldv + i) * 4u : kOOB;
+            om[k] = ok ? (uint32_t)(o * at.ldm + i) * 4u : kOOB;
+            ov_[k] = ok ? (uint32_t)(o * at.ldv + i) * 4u : kOOB;
             if constexpr (HAS_M)
               mv[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(R.m, om[k], 0, FORGE_EPI_LD_CPOL));
             if constexpr (HAS_V)
               vv[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(R.v, ov_[k], 0, FORGE_EPI_LD_CPOL));
           } else {
-            om[k] = ok ? (uint32_t)(o * a.ldm + i) : kOOB;
-            ov_[k] = ok ? (uint32_t)(o * a.ldv + i) : kOOB;
-            osc[k] = ok ? (uint32_t)(o * (a.in >> 6) + (i >> 6)) * 4u : kOOB;
+            om[k] = ok ? (uint32_t)(o * at.ldm + i) : kOOB;
+            ov_[k] = ok ? (uint32_t)(o * at.ldv + i) : kOOB;
+            osc[k] = ok ? (uint32_t)(o * (at.in >> 6) + (i >> 6)) * 4u : kOOB;
             if constexpr (HAS_M) {
               qm[k] = __builtin_amdgcn_raw_buffer_load_b32(R.m, om[k], 0, FORGE_EPI_LD_CPOL);
               msc[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(R.ms, osc[k], 0, FORGE_EPI_LD_CPOL));
@@ -851,7 +908,7 @@ void gemm_kernel(GArgs g, OptArgs a) {
             if constexpr (HAS_M) { mr = u32x4{qm[k], 0u, 0u, 0u}; ms_k = msc[k]; }
             if constexpr (HAS_V) { vr = u32x4{qv[k], 0u, 0u, 0u}; vs_k = vsc[k]; }
           }
-          apply_vec(R, gx, wb[k], mr, vr, ms_k, vs_k, o, i, o < g.N && i < g.M);
+          apply_vec(R, gx, wb[k], mr, vr, ms_k, vs_k, o, i, o < gt_N && i < g.M);
         }
 #if FORGE_EPI_SCHED_BARRIER
         __builtin_amdgcn_sched_barrier(0);
@@ -1013,12 +1070,25 @@ static int g_num_cus() {
 }
 
 template <class C, int EPI, int OPT, int SF, bool SR>
-static hipError_t g_launch(const GArgs& g, const OptArgs& a, hipStream_t st) {
+static hipError_t g_launch(const GArgs& g0, const OptArgs& a, hipStream_t st, const GroupArgs* grp = nullptr) {
+  GArgs g = g0;
+  GroupArgs gr{};
+  if (grp != nullptr) {
+    // the members' tile columns one after another (C::BN rows each, a member's last one partial)
+    gr = *grp;
+    int tn = 0;
+    for (int j = 0; j < gr.count; ++j) {
+      tn += (gr.mb[j].N + C::BN - 1) / C::BN;
+      gr.mb[j].tn1 = tn;
+    }
+    g.n_off = 0;
+    g.N = tn * C::BN;
+  }
   const int ntiles = g_ntm<C>(g) * g_ntn<C>(g);
   if (ntiles == 0) return hipSuccess;
   const int resident = C::OCC * 4 / C::NW * g_num_cus();  // OCC waves on each of 4 SIMDs
   const int grid = ntiles < resident ? ntiles : resident;
-  hipLaunchKernelGGL((gemm_kernel<C, EPI, OPT, SF, SR>), dim3(grid), dim3(C::NT), 0, st, g, a);
+  hipLaunchKernelGGL((gemm_kernel<C, EPI, OPT, SF, SR>), dim3(grid), dim3(C::NT), 0, st, g, a, gr);
   return hipGetLastError();
 }
 
@@ -1078,24 +1148,55 @@ static uint32_t extent(int64_t rows, int64_t cols, int64_t ld, int64_t es) {
 // Fused step for one optimizer on bf16 / fp32 operands (instantiated per optimizer
 // in the forge_gemm_bf16_*.hip sources).
 template <class C, int OPT>
-static hipError_t g_launch_opt(int sf, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
+static hipError_t g_launch_opt(int sf, int sr, const GArgs& g, const OptArgs& a, hipStream_t st,
+                               const GroupArgs* gr = nullptr) {
   switch (sf) {
     case ST_Q8:
-      return sr ? g_launch<C, G_EPI_OPT, OPT, ST_Q8, true>(g, a, st) : g_launch<C, G_EPI_OPT, OPT, ST_Q8, false>(g, a, st);
+      return sr ? g_launch<C, G_EPI_OPT, OPT, ST_Q8, true>(g, a, st, gr)
+                : g_launch<C, G_EPI_OPT, OPT, ST_Q8, false>(g, a, st, gr);
     case ST_Q8D:
-      return sr ? g_launch<C, G_EPI_OPT, OPT, ST_Q8D, true>(g, a, st) : g_launch<C, G_EPI_OPT, OPT, ST_Q8D, false>(g, a, st);
+      return sr ? g_launch<C, G_EPI_OPT, OPT, ST_Q8D, true>(g, a, st, gr)
+                : g_launch<C, G_EPI_OPT, OPT, ST_Q8D, false>(g, a, st, gr);
     case ST_BF16:
-      return sr ? g_launch<C, G_EPI_OPT, OPT, ST_BF16, true>(g, a, st)
-                : g_launch<C, G_EPI_OPT, OPT, ST_BF16, false>(g, a, st);
+      return sr ? g_launch<C, G_EPI_OPT, OPT, ST_BF16, true>(g, a, st, gr)
+                : g_launch<C, G_EPI_OPT, OPT, ST_BF16, false>(g, a, st, gr);
     default:
-      return sr ? g_launch<C, G_EPI_OPT, OPT, ST_F32, true>(g, a, st) : g_launch<C, G_EPI_OPT, OPT, ST_F32, false>(g, a, st);
+      return sr ? g_launch<C, G_EPI_OPT, OPT, ST_F32, true>(g, a, st, gr)
+                : g_launch<C, G_EPI_OPT, OPT, ST_F32, false>(g, a, st, gr);
   }
+}
+
+// Tile configuration of a grouped launch (the members' tiles counted together), by the same
+// rules as g_pick without the band of a last round: large tiles for more than half a round,
+// 128x128 tiles for at least two per compute unit, else the split-K tiles that fill more of
+// the compute units in one round.
+template <class Big, class Small, class Split, class Tiny, class F>
+static hipError_t g_pick_group(const GArgs& g, const GroupArgs& gr, F&& f) {
+  const int cus = g_num_cus();
+  auto tiles = [&](auto c) {
+    using C = decltype(c);
+    int tn = 0;
+    for (int j = 0; j < gr.count; ++j) tn += (gr.mb[j].N + C::BN - 1) / C::BN;
+    return tn * ((g.M - g.m_off + C::BM - 1) / C::BM);
+  };
+  if (2 * tiles(Big{}) > cus) return f(Big{});
+  if (tiles(Small{}) >= 2 * cus) return f(Small{});
+  if (tiles(Tiny{}) > tiles(Split{}) && tiles(Tiny{}) <= cus) return f(Tiny{});
+  return f(Split{});
 }
 
 template <int OPT>
 hipError_t wgrad_fused_bf16_opt(int sf, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
   return g_pick<WgradBig, WgradSmall, WgradSplit, WgradBand, WgradTiny>(
       g, [&](auto c, const GArgs& gc) { return g_launch_opt<decltype(c), OPT>(sf, sr, gc, a, st); });
+}
+
+// The fused step of the layers of a group (bf16 operands): one launch over all their tiles.
+template <int OPT>
+hipError_t wgrad_fused_bf16_group_opt(int sf, int sr, const GArgs& g, const OptArgs& a, const GroupArgs& gr,
+                                      hipStream_t st) {
+  return g_pick_group<WgradBig, WgradSmall, WgradSplit, WgradTiny>(
+      g, gr, [&](auto c) { return g_launch_opt<decltype(c), OPT>(sf, sr, g, a, st, &gr); });
 }
 
 // FP8 operands, dY in format FB (0 = E4M3, 1 = E5M2): the fused step of one
@@ -1119,10 +1220,13 @@ hipError_t wgrad_store_f8(const GArgs& g, hipStream_t st) {
       g, [&](auto c, const GArgs& gc) { return g_launch<decltype(c), G_EPI_STORE, FORGE_SGD, ST_F32, false>(gc, a, st); });
 }
 
-#define FORGE_EXTERN_BF16(OPT) \
-  extern template hipError_t wgrad_fused_bf16_opt<OPT>(int, int, const GArgs&, const OptArgs&, hipStream_t);
-#define FORGE_INST_BF16(OPT) \
-  template hipError_t wgrad_fused_bf16_opt<OPT>(int, int, const GArgs&, const OptArgs&, hipStream_t);
+#define FORGE_EXTERN_BF16(OPT)                                                                          \
+  extern template hipError_t wgrad_fused_bf16_opt<OPT>(int, int, const GArgs&, const OptArgs&, hipStream_t); \
+  extern template hipError_t wgrad_fused_bf16_group_opt<OPT>(int, int, const GArgs&, const OptArgs&,         \
+                                                             const GroupArgs&, hipStream_t);
+#define FORGE_INST_BF16(OPT)                                                                     \
+  template hipError_t wgrad_fused_bf16_opt<OPT>(int, int, const GArgs&, const OptArgs&, hipStream_t); \
+  template hipError_t wgrad_fused_bf16_group_opt<OPT>(int, int, const GArgs&, const OptArgs&, const GroupArgs&, hipStream_t);
 #define FORGE_EXTERN_F8(OPT, FB) \
   extern template hipError_t wgrad_fused_f8_opt<OPT, FB>(int, int, const GArgs&, const OptArgs&, hipStream_t);
 #define FORGE_INST_F8(OPT, FB) \

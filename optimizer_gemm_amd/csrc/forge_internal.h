@@ -413,5 +413,15 @@ hipError_t launch_wgrad_store_f8(int dy_e5m2, const void* X, const float* x_scal
                                  const float* dy_scale, const GemmDims& d, float* dW, int64_t ld_dw, hipStream_t st);
 hipError_t launch_dgrad_bf16(const void* dY, int64_t lddy, const void* W, int64_t ldw, void* dX, int64_t lddx,
                              int32_t T, int32_t out, int32_t in, hipStream_t stream);
+// One member of a grouped fused step (layers sharing X): its dY and epilogue arguments.
+struct GroupLayer {
+  const void* dY;
+  int64_t lddy;
+  OptArgs a;
+};
+// The fused step of n (1..FORGE_MAX_GROUP) layers that share X (bf16 operands), one launch;
+// d holds T, in and X's pitch; a's scalars are common to the layers.
+hipError_t launch_wgrad_fused_bf16_group(int state_fmt, int opt, int sr, const void* X, const GemmDims& d,
+                                         const GroupLayer* layers, int n, hipStream_t stream);
 
 }  // namespace forge

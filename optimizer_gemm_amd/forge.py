@@ -62,6 +62,9 @@ def _load() -> ctypes.CDLL:
     sigs = {
         "forge_linear_wgrad_step": ([P(ForgeTensor)] * 5 + [ctypes.c_int32, P(ForgeHyper), ctypes.c_int64,
                                                              ctypes.c_uint64, ctypes.c_void_p], ctypes.c_int),
+        "forge_linear_wgrad_step_group": ([P(ForgeTensor), ctypes.c_int32] + [P(ForgeTensor)] * 4 +
+                                          [ctypes.c_int32, P(ForgeHyper), ctypes.c_int64, P(ctypes.c_uint64),
+                                           ctypes.c_void_p], ctypes.c_int),
         "forge_linear_dgrad": ([P(ForgeTensor)] * 3 + [ctypes.c_void_p], ctypes.c_int),
         "forge_linear_wgrad": ([P(ForgeTensor), P(ForgeTensor), ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p],
                                ctypes.c_int),
@@ -265,6 +268,36 @@ def wgrad_step(X: torch.Tensor, dY: torch.Tensor, W: torch.Tensor, m: Optional[t
                                       ctypes.byref(h), int(step), seed & (2 ** 64 - 1), _stream(stream))
     if st:
         raise ForgeError(st, "forge_linear_wgrad_step")
+
+
+MAX_GROUP = 4
+
+
+def wgrad_step_group(X: torch.Tensor, dYs, Ws, ms, vs, opt: str = "adamw", hyper=None, step: int = 1, seeds=(0,),
+                     m_scales=None, v_scales=None, stream=None, code: str = "linear") -> None:
+    """Fused steps of the layers that share the input X, in one launch (forge_linear_wgrad_step_group):
+    layer l has gradient dYs[l], weights Ws[l], moments ms[l] / vs[l] (lists; None entries, or
+    None for the whole list, where the optimizer keeps no such slot) and seed seeds[l]."""
+    n = len(Ws)
+    if not (len(dYs) == n and len(seeds) == n) or n < 1 or n > MAX_GROUP:
+        raise ValueError(f"a group holds 1..{MAX_GROUP} layers, each with its dY, W and seed")
+
+    def arr(ts, scales=None):
+        if ts is None or all(t is None for t in ts):
+            return None
+        if any(t is None for t in ts):
+            raise ValueError("a moment slot is given for some layers of the group and not others")
+        sc = scales if scales is not None else [None] * n
+        return (ForgeTensor * n)(*[describe(t, s, code=code) for t, s in zip(ts, sc)])
+
+    h = _hyper(opt, hyper)
+    dy_a, w_a = arr(dYs), arr(Ws)
+    m_a, v_a = arr(ms, m_scales), arr(vs, v_scales)
+    seeds_a = (ctypes.c_uint64 * n)(*[s & (2 ** 64 - 1) for s in seeds])
+    st = _lib.forge_linear_wgrad_step_group(_ref(describe(X)), n, dy_a, w_a, m_a, v_a, OPT_ID[opt], ctypes.byref(h),
+                                            int(step), seeds_a, _stream(stream))
+    if st:
+        raise ForgeError(st, "forge_linear_wgrad_step_group")
 
 
 def dgrad(dY: torch.Tensor, W: torch.Tensor, dX: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:

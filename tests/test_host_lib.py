@@ -459,3 +459,60 @@ def test_bench_training_workload_rejects_empty_model():
                         "--blocks", "0"], capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "--blocks" in r.stderr
+
+
+def _call_group(f, X, dYs, Ws, ms, vs, n=None, opt="adamw", seeds=True):
+    h = f.make_hyper(opt)
+    k = len(Ws)
+    T = f.forge.ForgeTensor
+    arr = lambda ts: None if ts is None else (T * k)(*ts)  # noqa: E731
+    sd = (ctypes.c_uint64 * k)(*range(k)) if seeds else None
+    return f.lib().forge_linear_wgrad_step_group(ctypes.byref(X), k if n is None else n, arr(dYs), arr(Ws), arr(ms),
+                                                 arr(vs), f.forge.OPT_ID[opt], ctypes.byref(h), 1, sd, None)
+
+
+@cpu_only
+def test_group_validation(f):
+    """The grouped step checks every layer as the single-layer step does, plus the group's own
+    rules (1..FORGE_MAX_GROUP layers, one moment format, bfloat16 only, no overlap between
+    layers), all before a launch."""
+    F32, BF16, I8, U8, E4M3 = 0, 1, 2, 3, 4
+    A, B0, B1, C0, C1 = 0x10000000, 0x20000000, 0x21000000, 0x30000000, 0x31000000
+    M0, V0, M1, V1, S = 0x40000000, 0x41000000, 0x50000000, 0x51000000, 0x60000000
+    X = _t(f, A, BF16, 64, 256)
+    dYs = [_t(f, B0, BF16, 64, 128), _t(f, B1, BF16, 64, 64)]
+    Ws = [_t(f, C0, BF16, 128, 256), _t(f, C1, BF16, 64, 256)]
+    ms = [_t(f, M0, F32, 128, 256), _t(f, M1, F32, 64, 256)]
+    vs = [_t(f, V0, F32, 128, 256), _t(f, V1, F32, 64, 256)]
+    assert _call_group(f, X, dYs, Ws, ms, vs, n=0) == -2                      # no layer
+    assert _call_group(f, X, dYs, Ws, ms, vs, n=f.MAX_GROUP + 1) == -2        # more than the maximum
+    assert _call_group(f, X, dYs, Ws, ms, vs, seeds=False) == -1              # no seeds
+    assert _call_group(f, X, dYs, [Ws[0], _t(f, C1, BF16, 64, 128)], ms, vs) == -2      # in differs from X's
+    assert _call_group(f, X, dYs, Ws, None, vs) == -1                         # AdamW needs m
+    assert _call_group(f, X, dYs, [Ws[0], _t(f, C0 + 512, BF16, 64, 256)], ms, vs) == -8  # W of one layer in another's
+    assert _call_group(f, X, dYs, Ws, [ms[0], _t(f, V0, F32, 64, 256)], vs) == -8          # m of one layer on v of another
+    assert _call_group(f, X, dYs, Ws, [ms[0], _t(f, B1, F32, 64, 256)], vs) == -8          # an output on another layer's dY
+    q8 = [_t(f, M1, I8, 64, 256, scale=S), _t(f, V1, U8, 64, 256, scale=S + 4096)]
+    assert _call_group(f, X, dYs, Ws, [ms[0], q8[0]], [vs[0], q8[1]]) == -3   # moment formats differ
+    Xf = _t(f, A, F32, 64, 256)
+    assert _call_group(f, Xf, [_t(f, B0, F32, 64, 128), _t(f, B1, F32, 64, 64)],
+                       [_t(f, C0, F32, 128, 256), _t(f, C1, F32, 64, 256)], ms, vs) == -5  # fp32 layers
+    Xq = _t(f, A, E4M3, 64, 256, scale=S + 8192)
+    assert _call_group(f, Xq, [_t(f, B0, E4M3, 64, 128, scale=S + 8196), _t(f, B1, E4M3, 64, 64, scale=S + 8200)],
+                       Ws, ms, vs) == -5                                      # FP8 inputs
+
+
+@cpu_only
+def test_empty_layer_needs_no_pointers(f):
+    # a layer with no weights is a valid no-op: its W and moments may have NULL data (nothing
+    # is read, written or launched), alone or as a member of a group
+    BF16, F32 = 1, 0
+    X = _t(f, 0x10000000, BF16, 64, 256)
+    dY = _t(f, 0x20000000, BF16, 64, 0)
+    W = _t(f, None, BF16, 0, 256)
+    m, v = _t(f, None, F32, 0, 256), _t(f, None, F32, 0, 256)
+    assert _call_step(f, X, dY, W, m, v) == 0
+    assert _call_group(f, X, [dY], [W], [m], [v]) == 0
+    # a layer with weights still needs its moments
+    assert _call_step(f, X, _t(f, 0x20000000, BF16, 64, 128), _t(f, 0x30000000, BF16, 128, 256),
+                      _t(f, None, F32, 128, 256), v) == -1
