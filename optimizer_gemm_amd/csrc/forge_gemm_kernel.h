@@ -1170,33 +1170,62 @@ static hipError_t g_launch_opt(int sf, int sr, const GArgs& g, const OptArgs& a,
 // rules as g_pick without the band of a last round: large tiles for more than half a round,
 // 128x128 tiles for at least two per compute unit, else the split-K tiles that fill more of
 // the compute units in one round.
-template <class Big, class Small, class Split, class Tiny, class F>
+// Tile configuration(s) of a grouped launch, chosen as g_pick chooses for one layer from
+// the members' total tile count. The last-round band works at member boundaries: when the
+// large tiles' last round would be at most half full and a subset of the members fills
+// whole rounds of large tiles while the others fit in one round of band tiles, the two
+// subsets run as two launches on the stream (a band round counted as half a large one).
+// f(C{}, members) launches configuration C over a group of members.
+template <class Big, class Small, class Split, class Band, class Tiny, class F>
 static hipError_t g_pick_group(const GArgs& g, const GroupArgs& gr, F&& f) {
   const int cus = g_num_cus();
-  auto tiles = [&](auto c) {
+  const unsigned all = (1u << gr.count) - 1u;
+  auto tiles = [&](auto c, unsigned mask) {
     using C = decltype(c);
     int tn = 0;
-    for (int j = 0; j < gr.count; ++j) tn += (gr.mb[j].N + C::BN - 1) / C::BN;
+    for (int j = 0; j < gr.count; ++j)
+      if (mask >> j & 1u) tn += (gr.mb[j].N + C::BN - 1) / C::BN;
     return tn * ((g.M - g.m_off + C::BM - 1) / C::BM);
   };
-  if (2 * tiles(Big{}) > cus) return f(Big{});
-  if (tiles(Small{}) >= 2 * cus) return f(Small{});
-  if (tiles(Tiny{}) > tiles(Split{}) && tiles(Tiny{}) <= cus) return f(Tiny{});
-  return f(Split{});
+  auto subset = [&](unsigned mask) {
+    GroupArgs s{};
+    for (int j = 0; j < gr.count; ++j)
+      if (mask >> j & 1u) s.mb[s.count++] = gr.mb[j];
+    return s;
+  };
+  const int tb = tiles(Big{}, all);
+  if (tb >= cus) {
+    const int rounds = (tb + cus - 1) / cus, rem = tb % cus;
+    if (rem > 0 && 2 * rem <= cus) {
+      for (unsigned s = 1; s < all; ++s) {
+        const int ts = tiles(Big{}, s);
+        if (ts % cus == 0 && 2 * (ts / cus) + 1 < 2 * rounds && tiles(Band{}, all & ~s) <= cus) {
+          hipError_t e = f(Big{}, subset(s));
+          return e != hipSuccess ? e : f(Band{}, subset(all & ~s));
+        }
+      }
+    }
+    return f(Big{}, gr);
+  }
+  if (2 * tb > cus) return f(Big{}, gr);
+  if (tiles(Small{}, all) >= 2 * cus) return f(Small{}, gr);
+  if (tiles(Tiny{}, all) > tiles(Split{}, all) && tiles(Tiny{}, all) <= cus) return f(Tiny{}, gr);
+  return f(Split{}, gr);
+}
+
+// The fused step of the layers of a group (bf16 operands): one launch over all their
+// tiles (two when the last round is filled with band tiles).
+template <int OPT>
+hipError_t wgrad_fused_bf16_group_opt(int sf, int sr, const GArgs& g, const OptArgs& a, const GroupArgs& gr,
+                                      hipStream_t st) {
+  return g_pick_group<WgradBig, WgradSmall, WgradSplit, WgradBand, WgradTiny>(
+      g, gr, [&](auto c, const GroupArgs& sub) { return g_launch_opt<decltype(c), OPT>(sf, sr, g, a, st, &sub); });
 }
 
 template <int OPT>
 hipError_t wgrad_fused_bf16_opt(int sf, int sr, const GArgs& g, const OptArgs& a, hipStream_t st) {
   return g_pick<WgradBig, WgradSmall, WgradSplit, WgradBand, WgradTiny>(
       g, [&](auto c, const GArgs& gc) { return g_launch_opt<decltype(c), OPT>(sf, sr, gc, a, st); });
-}
-
-// The fused step of the layers of a group (bf16 operands): one launch over all their tiles.
-template <int OPT>
-hipError_t wgrad_fused_bf16_group_opt(int sf, int sr, const GArgs& g, const OptArgs& a, const GroupArgs& gr,
-                                      hipStream_t st) {
-  return g_pick_group<WgradBig, WgradSmall, WgradSplit, WgradTiny>(
-      g, gr, [&](auto c) { return g_launch_opt<decltype(c), OPT>(sf, sr, g, a, st, &gr); });
 }
 
 // FP8 operands, dY in format FB (0 = E4M3, 1 = E5M2): the fused step of one
