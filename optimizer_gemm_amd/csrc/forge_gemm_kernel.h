@@ -66,9 +66,14 @@ enum { G_EPI_STORE = 0, G_EPI_OPT = 1, G_EPI_DX = 2 };
 
 
 // 4-element vectors whose W / m / v loads the optimizer epilogue issues before consuming
-// any of them, and whether the compiler may move work across those batches
+// any of them (KB1: configurations with one wave per SIMD, whose accumulators sit in
+// AGPRs and leave room for a deeper batch; with half the waves of the others they need
+// more loads in flight per wave), and whether the compiler may move work across batches
 #ifndef FORGE_EPI_KB
 #define FORGE_EPI_KB 2
+#endif
+#ifndef FORGE_EPI_KB1
+#define FORGE_EPI_KB1 4
 #endif
 #ifndef FORGE_EPI_SCHED_BARRIER
 #define FORGE_EPI_SCHED_BARRIER 1
@@ -847,7 +852,7 @@ void gemm_kernel(GArgs g, OptArgs a, GroupArgs gr) {
         const EpiRes R = epi_res<OPT, SF>(at);
         // loads of KB vectors are issued before any of them is consumed; KB bounds the
         // registers a batch holds next to the accumulators still to be written out
-        constexpr int KB_MAX = Q8 && C::OCC >= 2 ? 1 : FORGE_EPI_KB;
+        constexpr int KB_MAX = Q8 && C::OCC >= 2 ? 1 : (C::OCC == 1 ? FORGE_EPI_KB1 : FORGE_EPI_KB);
         constexpr int KB = NVc > KB_MAX ? KB_MAX : NVc;
         // at most 8 batches unrolled (the one-wave FP8 tiles have 32 vectors per thread and
         // chunk: unrolling all of them exhausts the scalar registers)
