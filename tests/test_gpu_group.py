@@ -102,9 +102,10 @@ def test_group_of_one_equals_single_layer_call():
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
-def test_group_band_split_attention_projections():
+@pytest.mark.parametrize("state", ["f32", "q8"])
+def test_group_band_split_attention_projections(state):
     # q, k, v of a Llama-3.1-8B layer: 384 large tiles, a half-full last round on 256 CUs;
     # there q runs as one round of large tiles and k, v as one round of band tiles
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     print(f"[case] {cus} compute units", flush=True)
-    _run_group((4096, 1024, 1024), 4096, 300, "adamw", "f32", cfg=165, steps=1, n_rows=48)
+    _run_group((4096, 1024, 1024), 4096, 300, "adamw", state, cfg=165, steps=1, n_rows=48)
