@@ -403,8 +403,8 @@ def main() -> int:
     # input (q, k, v and gate, up, in the order q, k, v, o, gate, up, down) as one grouped step
     units = [[k] for k in range(len(per_layer))]
     if args.group:
-        if args.workload not in ("llama8b_layer_8192", "llama8b_tp8_8192", "stack") or fp8:
-            print("--group needs a decoder-layer workload with bf16 inputs", file=sys.stderr)
+        if args.workload not in ("llama8b_layer_8192", "llama8b_tp8_8192", "stack"):
+            print("--group needs a decoder-layer workload", file=sys.stderr)
             return 2
         units = []
         for b in range(0, len(per_layer), 7):
@@ -430,7 +430,8 @@ def main() -> int:
                 bufs = [shape_bufs[(L[0].out, L[0].inn, L[0].T)] for L in mem]
                 forge.wgrad_step_group(bufs[0][0], [b[5] for b in bufs], [L[1] for L in mem], [L[2] for L in mem],
                                        [L[3] for L in mem], opt, hyper, t, [L[6] for L in mem],
-                                       [L[4] for L in mem], [L[5] for L in mem], code=code)
+                                       [L[4] for L in mem], [L[5] for L in mem], code=code,
+                                       x_scale=bufs[0][3], dy_scales=[b[4] for b in bufs])
             if fused_events is not None:
                 fused_events[k0][1].record()
                 for k in unit[1:]:  # the group's time is the first member's

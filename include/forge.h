@@ -185,8 +185,10 @@ int forge_linear_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge
  * its own seed seeds[l]; opt, hyper and step are common. Each layer is updated exactly
  * as forge_linear_wgrad_step would update it (same element indices and random streams),
  * except that the tile shape, and so the order of the FP32 summation over tokens, is
- * chosen for the group as a whole. bfloat16 X, dY and W only (FP8 inputs and fp32 layers:
- * FORGE_ERR_UNSUPPORTED); every layer's moments in the same format.
+ * chosen for the group as a whole. bfloat16 W; X and dY bfloat16, or FP8 codes as in
+ * forge_linear_wgrad_step (X E4M3 with its scale; every dY in one format, E4M3 or E5M2,
+ * each with its own scale), else FORGE_ERR_DTYPE; fp32 layers: FORGE_ERR_UNSUPPORTED.
+ * Every layer's moments in the same format (FORGE_ERR_DTYPE).
  * 1 <= n_layers <= FORGE_MAX_GROUP, else FORGE_ERR_SHAPE. Every argument check of
  * forge_linear_wgrad_step applies to each layer; in addition no layer's W, m, v or block
  * scales may overlap any other layer's tensors (FORGE_ERR_ALIAS). Nothing is enqueued

@@ -454,8 +454,9 @@ int forge_linear_wgrad_step_group(const forge_tensor* X, int32_t n_layers, const
     int r = plan_step(X, &dY[l], &W[l], m ? &m[l] : nullptr, v ? &v[l] : nullptr, opt, hyper, step, seeds[l],
                       nullptr, 0, &p[l]);
     if (r) return r;
-    if (p[l].f8 || p[l].io != FORGE_BF16) return FORGE_ERR_UNSUPPORTED;
-    if (p[l].fmt != p[0].fmt) return FORGE_ERR_DTYPE;
+    if (p[l].io != FORGE_BF16) return FORGE_ERR_UNSUPPORTED;
+    // one operand format and one moment format for the whole group
+    if (p[l].f8 != p[0].f8 || (p[l].f8 && dY[l].dtype != dY[0].dtype) || p[l].fmt != p[0].fmt) return FORGE_ERR_DTYPE;
   }
   // a layer's outputs overlap no other layer's tensors (each plan checked its own)
   const int sl = opt_slots(opt);
@@ -475,11 +476,13 @@ int forge_linear_wgrad_step_group(const forge_tensor* X, int32_t n_layers, const
   int n = 0;
   for (int l = 0; l < n_layers; ++l) {
     if (p[l].empty) continue;  // no weights: nothing to update
-    layers[n++] = GroupLayer{dY[l].data, dY[l].ld, p[l].a};
+    layers[n++] = GroupLayer{dY[l].data, dY[l].ld, dY[l].scale, p[l].a};
   }
   if (n == 0) return FORGE_OK;
   const StepPlan& p0 = p[0];
-  hipError_t e = launch_wgrad_fused_bf16_group(p0.fmt, opt, p0.sr, X->data, p0.d, layers, n, (hipStream_t)stream);
+  hipError_t e = p0.f8 ? launch_wgrad_fused_f8_group(dY[0].dtype == FORGE_E5M2, p0.fmt, opt, p0.sr, X->data, X->scale,
+                                                     p0.d, layers, n, (hipStream_t)stream)
+                       : launch_wgrad_fused_bf16_group(p0.fmt, opt, p0.sr, X->data, p0.d, layers, n, (hipStream_t)stream);
   return e == hipSuccess ? FORGE_OK : FORGE_ERR_HIP;
 }
 

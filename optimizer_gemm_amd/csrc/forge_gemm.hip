@@ -43,17 +43,19 @@ hipError_t launch_wgrad_fused_bf16(int state_fmt, int opt, int sr, const void* X
   }
 }
 
-hipError_t launch_wgrad_fused_bf16_group(int state_fmt, int opt, int sr, const void* X, const GemmDims& d,
-                                         const GroupLayer* layers, int n, hipStream_t st) {
-  if (n < 1 || n > kMaxGroup) return hipErrorInvalidValue;
+// The member table of a grouped launch (eb: bytes per operand element) and the launch's
+// common arguments: the A operand and the sizes the members share; B and N come from each
+// member.
+static GroupArgs group_args(const GroupLayer* layers, int n, const GemmDims& d, int eb) {
   GroupArgs gr{};
   gr.count = n;
   for (int j = 0; j < n; ++j) {
     const OptArgs& a = layers[j].a;
     GroupMember& M = gr.mb[j];
     M.B = layers[j].dY;
+    M.b_scale = layers[j].dy_scale;
     M.ldb = layers[j].lddy;
-    M.b_bytes = extent(d.T, a.out, layers[j].lddy, 2);
+    M.b_bytes = extent(d.T, a.out, layers[j].lddy, eb);
     M.N = a.out;
     M.W = a.W;
     M.m = a.m;
@@ -65,7 +67,13 @@ hipError_t launch_wgrad_fused_bf16_group(int state_fmt, int opt, int sr, const v
     M.ldv = a.ldv;
     M.rng_base = a.rng_base;
   }
-  // the A operand and the sizes common to the members; B and N come from each member
+  return gr;
+}
+
+hipError_t launch_wgrad_fused_bf16_group(int state_fmt, int opt, int sr, const void* X, const GemmDims& d,
+                                         const GroupLayer* layers, int n, hipStream_t st) {
+  if (n < 1 || n > kMaxGroup) return hipErrorInvalidValue;
+  const GroupArgs gr = group_args(layers, n, d, 2);
   GArgs g{X, layers[0].dY, d.ldx, layers[0].lddy, d.in, layers[0].a.out, d.T, nullptr, 0,
           extent(d.T, d.in, d.ldx, 2), gr.mb[0].b_bytes, 0};
   const OptArgs& a = layers[0].a;
@@ -80,6 +88,34 @@ hipError_t launch_wgrad_fused_bf16_group(int state_fmt, int opt, int sr, const v
     case FORGE_RADAM: return wgrad_fused_bf16_group_opt<FORGE_RADAM>(state_fmt, sr, g, a, gr, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int FB>
+static hipError_t wgrad_fused_f8_group(int sf, int opt, int sr, const GArgs& g, const OptArgs& a, const GroupArgs& gr,
+                                       hipStream_t st) {
+  switch (opt) {
+    case FORGE_ADAMW: return wgrad_fused_f8_group_opt<FORGE_ADAMW, FB>(sf, sr, g, a, gr, st);
+    case FORGE_SGD: return wgrad_fused_f8_group_opt<FORGE_SGD, FB>(sf, sr, g, a, gr, st);
+    case FORGE_SGD_MOMENTUM: return wgrad_fused_f8_group_opt<FORGE_SGD_MOMENTUM, FB>(sf, sr, g, a, gr, st);
+    case FORGE_LION: return wgrad_fused_f8_group_opt<FORGE_LION, FB>(sf, sr, g, a, gr, st);
+    case FORGE_RMSPROP: return wgrad_fused_f8_group_opt<FORGE_RMSPROP, FB>(sf, sr, g, a, gr, st);
+    case FORGE_ADAGRAD: return wgrad_fused_f8_group_opt<FORGE_ADAGRAD, FB>(sf, sr, g, a, gr, st);
+    case FORGE_NADAM: return wgrad_fused_f8_group_opt<FORGE_NADAM, FB>(sf, sr, g, a, gr, st);
+    case FORGE_RADAM: return wgrad_fused_f8_group_opt<FORGE_RADAM, FB>(sf, sr, g, a, gr, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_wgrad_fused_f8_group(int dy_e5m2, int state_fmt, int opt, int sr, const void* X,
+                                       const float* x_scale, const GemmDims& d, const GroupLayer* layers, int n,
+                                       hipStream_t st) {
+  if (n < 1 || n > kMaxGroup) return hipErrorInvalidValue;
+  const GroupArgs gr = group_args(layers, n, d, 1);
+  GArgs g{X, layers[0].dY, d.ldx, layers[0].lddy, d.in, layers[0].a.out, d.T, nullptr, 0,
+          extent(d.T, d.in, d.ldx, 1), gr.mb[0].b_bytes, 0, x_scale, layers[0].dy_scale};
+  const OptArgs& a = layers[0].a;
+  return dy_e5m2 ? wgrad_fused_f8_group<1>(state_fmt, opt, sr, g, a, gr, st)
+                 : wgrad_fused_f8_group<0>(state_fmt, opt, sr, g, a, gr, st);
 }
 
 hipError_t launch_wgrad_store_bf16(const void* X, const void* dY, const GemmDims& d, float* dW, int64_t ld_dw,

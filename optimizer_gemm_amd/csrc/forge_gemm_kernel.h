@@ -194,6 +194,7 @@ struct GArgs {
 constexpr int kMaxGroup = FORGE_MAX_GROUP;
 struct GroupMember {
   const void* B;
+  const float* b_scale;  // FP8 B: its dequantisation scale
   int64_t ldb;
   uint32_t b_bytes;
   int32_t N;    // the member's rows of C (its out)
@@ -367,8 +368,8 @@ void gemm_kernel(GArgs g, OptArgs a, GroupArgs gr) {
 
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A, g.a_bytes);
   // FP8 operands: the gradient is the product of the two dequantisation scales times
-  // the sum of code products
-  const float gscale = C::F8 ? g.a_scale[0] * g.b_scale[0] : 1.f;
+  // the sum of code products (B's scale is the tile's layer's, in a grouped launch)
+  const float a_sc = C::F8 ? g.a_scale[0] : 1.f;
 
   const int ntm = g_ntm<C>(g), ntn = g_ntn<C>(g);
   const int ntiles = ntm * ntn;
@@ -393,6 +394,7 @@ void gemm_kernel(GArgs g, OptArgs a, GroupArgs gr) {
     // the tile's layer (a grouped launch): its B operand, rows and pitch, and the
     // epilogue's tensors and random stream; chosen with uniform selects
     const void* t_B = g.B;
+    const float* t_bsc = g.b_scale;
     uint32_t t_b_bytes = g.b_bytes;
     int64_t gt_ldb = g.ldb;
     int gt_N = g.N;
@@ -406,6 +408,7 @@ void gemm_kernel(GArgs g, OptArgs a, GroupArgs gr) {
           const GroupMember& M = gr.mb[j];
           tn0 = start;
           t_B = M.B;
+          t_bsc = M.b_scale;
           t_b_bytes = M.b_bytes;
           gt_ldb = M.ldb;
           gt_N = M.N;
@@ -423,6 +426,7 @@ void gemm_kernel(GArgs g, OptArgs a, GroupArgs gr) {
       }
       tn -= tn0;
     }
+    const float gscale = C::F8 ? a_sc * t_bsc[0] : 1.f;
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(t_B, t_b_bytes);
     const uint32_t b_rowb = (uint32_t)(B_RSTEP * gt_ldb * C::EB);
     const uint32_t b_stageb = C::B_TR ? (uint32_t)(C::BK * gt_ldb * C::EB) : (uint32_t)(C::BK * C::EB);
@@ -1253,6 +1257,14 @@ hipError_t wgrad_fused_f8_opt(int sf, int sr, const GArgs& g, const OptArgs& a, 
       g, [&](auto c, const GArgs& gc) { return g_launch_opt_f8<decltype(c), OPT>(sf, sr, gc, a, st); });
 }
 
+// The fused step of the layers of a group, FP8 operands (dY of every layer in format FB).
+template <int OPT, int FB>
+hipError_t wgrad_fused_f8_group_opt(int sf, int sr, const GArgs& g, const OptArgs& a, const GroupArgs& gr,
+                                    hipStream_t st) {
+  return g_pick_group<WgradF8Big<FB>, WgradF8Small<FB>, WgradF8Small<FB>, WgradF8Small<FB>, WgradF8Small<FB>>(
+      g, gr, [&](auto c, const GroupArgs& sub) { return g_launch_opt<decltype(c), OPT>(sf, sr, g, a, st, &sub); });
+}
+
 template <int FB>
 hipError_t wgrad_store_f8(const GArgs& g, hipStream_t st) {
   OptArgs a{};
@@ -1267,9 +1279,12 @@ hipError_t wgrad_store_f8(const GArgs& g, hipStream_t st) {
 #define FORGE_INST_BF16(OPT)                                                                     \
   template hipError_t wgrad_fused_bf16_opt<OPT>(int, int, const GArgs&, const OptArgs&, hipStream_t); \
   template hipError_t wgrad_fused_bf16_group_opt<OPT>(int, int, const GArgs&, const OptArgs&, const GroupArgs&, hipStream_t);
-#define FORGE_EXTERN_F8(OPT, FB) \
-  extern template hipError_t wgrad_fused_f8_opt<OPT, FB>(int, int, const GArgs&, const OptArgs&, hipStream_t);
-#define FORGE_INST_F8(OPT, FB) \
-  template hipError_t wgrad_fused_f8_opt<OPT, FB>(int, int, const GArgs&, const OptArgs&, hipStream_t);
+#define FORGE_EXTERN_F8(OPT, FB)                                                                          \
+  extern template hipError_t wgrad_fused_f8_opt<OPT, FB>(int, int, const GArgs&, const OptArgs&, hipStream_t); \
+  extern template hipError_t wgrad_fused_f8_group_opt<OPT, FB>(int, int, const GArgs&, const OptArgs&,         \
+                                                               const GroupArgs&, hipStream_t);
+#define FORGE_INST_F8(OPT, FB)                                                                       \
+  template hipError_t wgrad_fused_f8_opt<OPT, FB>(int, int, const GArgs&, const OptArgs&, hipStream_t); \
+  template hipError_t wgrad_fused_f8_group_opt<OPT, FB>(int, int, const GArgs&, const OptArgs&, const GroupArgs&, hipStream_t);
 
 }  // namespace forge

@@ -417,11 +417,16 @@ hipError_t launch_dgrad_bf16(const void* dY, int64_t lddy, const void* W, int64_
 struct GroupLayer {
   const void* dY;
   int64_t lddy;
+  const float* dy_scale;  // FP8 dY: its dequantisation scale (else unused)
   OptArgs a;
 };
-// The fused step of n (1..FORGE_MAX_GROUP) layers that share X (bf16 operands), one launch;
-// d holds T, in and X's pitch; a's scalars are common to the layers.
+// The fused step of n (1..FORGE_MAX_GROUP) layers that share X, one launch; d holds T, in
+// and X's pitch; a's scalars are common to the layers. bf16 operands, or FP8 codes (X in
+// E4M3 with scale x_scale, every dY in E4M3 or, dy_e5m2, E5M2, each with its own scale).
 hipError_t launch_wgrad_fused_bf16_group(int state_fmt, int opt, int sr, const void* X, const GemmDims& d,
                                          const GroupLayer* layers, int n, hipStream_t stream);
+hipError_t launch_wgrad_fused_f8_group(int dy_e5m2, int state_fmt, int opt, int sr, const void* X,
+                                       const float* x_scale, const GemmDims& d, const GroupLayer* layers, int n,
+                                       hipStream_t stream);
 
 }  // namespace forge

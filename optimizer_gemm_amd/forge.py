@@ -274,10 +274,12 @@ MAX_GROUP = 4
 
 
 def wgrad_step_group(X: torch.Tensor, dYs, Ws, ms, vs, opt: str = "adamw", hyper=None, step: int = 1, seeds=(0,),
-                     m_scales=None, v_scales=None, stream=None, code: str = "linear") -> None:
+                     m_scales=None, v_scales=None, stream=None, code: str = "linear",
+                     x_scale: Optional[torch.Tensor] = None, dy_scales=None) -> None:
     """Fused steps of the layers that share the input X, in one launch (forge_linear_wgrad_step_group):
     layer l has gradient dYs[l], weights Ws[l], moments ms[l] / vs[l] (lists; None entries, or
-    None for the whole list, where the optimizer keeps no such slot) and seed seeds[l]."""
+    None for the whole list, where the optimizer keeps no such slot) and seed seeds[l]. FP8
+    inputs as in wgrad_step: x_scale for X, dy_scales[l] for dYs[l]."""
     n = len(Ws)
     if not (len(dYs) == n and len(seeds) == n) or n < 1 or n > MAX_GROUP:
         raise ValueError(f"a group holds 1..{MAX_GROUP} layers, each with its dY, W and seed")
@@ -291,10 +293,11 @@ def wgrad_step_group(X: torch.Tensor, dYs, Ws, ms, vs, opt: str = "adamw", hyper
         return (ForgeTensor * n)(*[describe(t, s, code=code) for t, s in zip(ts, sc)])
 
     h = _hyper(opt, hyper)
-    dy_a, w_a = arr(dYs), arr(Ws)
+    dy_a, w_a = arr(dYs, dy_scales), arr(Ws)
     m_a, v_a = arr(ms, m_scales), arr(vs, v_scales)
     seeds_a = (ctypes.c_uint64 * n)(*[s & (2 ** 64 - 1) for s in seeds])
-    st = _lib.forge_linear_wgrad_step_group(_ref(describe(X)), n, dy_a, w_a, m_a, v_a, OPT_ID[opt], ctypes.byref(h),
+    st = _lib.forge_linear_wgrad_step_group(_ref(describe(X, x_scale)), n, dy_a, w_a, m_a, v_a, OPT_ID[opt],
+                                            ctypes.byref(h),
                                             int(step), seeds_a, _stream(stream))
     if st:
         raise ForgeError(st, "forge_linear_wgrad_step_group")

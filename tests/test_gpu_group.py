@@ -11,8 +11,9 @@ import pytest
 import torch
 
 from oracle import optim
-from synth import LayerSpec, draw_layer_batch, draw_layer_init, sample_rows
+from synth import LayerSpec, draw_layer_batch, draw_layer_batch_fp8, draw_layer_init, sample_rows
 from tests import _parity as P
+from tests.test_gpu_fp8 import dev_fp8, dev_scale
 
 pytestmark = pytest.mark.gpu
 
@@ -109,3 +110,66 @@ def test_group_band_split_attention_projections(state):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     print(f"[case] {cus} compute units", flush=True)
     _run_group((4096, 1024, 1024), 4096, 300, "adamw", state, cfg=165, steps=1, n_rows=48)
+
+
+def _run_group_fp8(outs, inn, T, opt, state, cfg, dy_fmt="e5m2", steps=2, n_rows=None):
+    """As _run_group with FP8 inputs: X (E4M3, layer 0's draw) shared, each layer's dY in
+    dy_fmt with its own scale; each layer checked with the FP8 gradient bound."""
+    f = _forge()
+    hp = optim.hyper(opt)
+    specs = [LayerSpec(f"g{k}", out, inn, T) for k, out in enumerate(outs)]
+    seeds = [(0x6B0000 + cfg) ^ k for k in range(len(outs))]
+    Ws = [P.dev_bf16(draw_layer_init(cfg, k, s)) for k, s in enumerate(specs)]
+    st = [f.new_states(W, opt, state) for W in Ws]
+    rows = [np.arange(s.out) if n_rows is None or s.out <= n_rows else sample_rows(cfg, k, s.out, n_rows)
+            for k, s in enumerate(specs)]
+    print(f"[case] fp8 group {outs} x {inn}, T={T}, dY {dy_fmt}, {opt}, {state} moments", flush=True)
+    for t in range(1, steps + 1):
+        draws = [draw_layer_batch_fp8(cfg, k, t, s, "e4m3", dy_fmt) for k, s in enumerate(specs)]
+        Xq, sx = draws[0][0], draws[0][2]
+        before = [P.snapshot((W, *s), r) for W, s, r in zip(Ws, st, rows)]
+        f.wgrad_step_group(dev_fp8(Xq, "e4m3"), [dev_fp8(d[1], dy_fmt) for d in draws], Ws, [s[0] for s in st],
+                           [s[1] for s in st], opt, _gh(hp), t, seeds, [s[2] for s in st], [s[3] for s in st],
+                           code=P.state_code(state), x_scale=dev_scale(sx), dy_scales=[dev_scale(d[3]) for d in draws])
+        torch.cuda.synchronize()
+        for k in range(len(specs)):
+            after = P.snapshot((Ws[k], *st[k]), rows[k])
+            P.verify_step(opt, Xq, draws[k][1], before[k], after, hp, t, seeds[k], "bf16", state, True, rows[k],
+                          fp8=("e4m3", dy_fmt, sx, draws[k][3]))
+        print(f"[ok] step {t}: every layer of the FP8 group", flush=True)
+
+
+@pytest.mark.parametrize("state", ["f32", "q8"])
+def test_group_fp8_ragged_layers(state):
+    # FP8 rows are multiples of 16 bytes: 144 = 128 + 16 output rows, 520 = 8 * 64 + 8 tokens
+    _run_group_fp8((384, 144, 128), 1024, 520, "adamw", state, cfg=170)
+
+
+def test_group_fp8_large_tiles_e4m3_gradients():
+    # 160 tiles of 256x256 over four layers: more than half a round, so the large FP8 tiles
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    outs = (1024, 512, 512, 512)
+    assert 2 * 16 * sum(o // 256 for o in outs) > cus
+    _run_group_fp8(outs, 4096, 300, "adamw", "f32", cfg=171, dy_fmt="e4m3", steps=1, n_rows=48)
+
+
+def test_group_fp8_of_one_equals_single_layer_call():
+    f = _forge()
+    spec = LayerSpec("g", 512, 768, 256)
+    hp = _gh(optim.hyper("adamw"))
+    Xq, dYq, sx, sd = draw_layer_batch_fp8(172, 0, 1, spec, "e4m3", "e5m2")
+    Xd, dYd, xs, ds = dev_fp8(Xq, "e4m3"), dev_fp8(dYq, "e5m2"), dev_scale(sx), dev_scale(sd)
+    W0 = draw_layer_init(172, 0, spec)
+    outs = []
+    for grouped in (False, True):
+        W = P.dev_bf16(W0)
+        m, v, _, _ = f.new_states(W, "adamw", "f32")
+        for t in (1, 2):
+            if grouped:
+                f.wgrad_step_group(Xd, [dYd], [W], [m], [v], "adamw", hp, t, [99], x_scale=xs, dy_scales=[ds])
+            else:
+                f.wgrad_step(Xd, dYd, W, m, v, "adamw", hp, t, 99, x_scale=xs, dy_scale=ds)
+        torch.cuda.synchronize()
+        outs.append([P.host(x).copy() for x in (W, m, v)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))

@@ -474,9 +474,9 @@ def _call_group(f, X, dYs, Ws, ms, vs, n=None, opt="adamw", seeds=True):
 @cpu_only
 def test_group_validation(f):
     """The grouped step checks every layer as the single-layer step does, plus the group's own
-    rules (1..FORGE_MAX_GROUP layers, one moment format, bfloat16 only, no overlap between
-    layers), all before a launch."""
-    F32, BF16, I8, U8, E4M3 = 0, 1, 2, 3, 4
+    rules (1..FORGE_MAX_GROUP layers, one operand format and one moment format, no fp32
+    layers, no overlap between layers), all before a launch."""
+    F32, BF16, I8, U8, E4M3, E5M2 = 0, 1, 2, 3, 4, 5
     A, B0, B1, C0, C1 = 0x10000000, 0x20000000, 0x21000000, 0x30000000, 0x31000000
     M0, V0, M1, V1, S = 0x40000000, 0x41000000, 0x50000000, 0x51000000, 0x60000000
     X = _t(f, A, BF16, 64, 256)
@@ -498,8 +498,12 @@ def test_group_validation(f):
     assert _call_group(f, Xf, [_t(f, B0, F32, 64, 128), _t(f, B1, F32, 64, 64)],
                        [_t(f, C0, F32, 128, 256), _t(f, C1, F32, 64, 256)], ms, vs) == -5  # fp32 layers
     Xq = _t(f, A, E4M3, 64, 256, scale=S + 8192)
-    assert _call_group(f, Xq, [_t(f, B0, E4M3, 64, 128, scale=S + 8196), _t(f, B1, E4M3, 64, 64, scale=S + 8200)],
-                       Ws, ms, vs) == -5                                      # FP8 inputs
+    assert _call_group(f, Xq, [_t(f, B0, E4M3, 64, 128, scale=S + 8196), _t(f, B1, E5M2, 64, 64, scale=S + 8200)],
+                       Ws, ms, vs) == -3                                      # FP8 dY in two formats
+    assert _call_group(f, Xq, [_t(f, B0, E4M3, 64, 128, scale=S + 8196), _t(f, B1, BF16, 64, 64)],
+                       Ws, ms, vs) == -3                                      # FP8 and bf16 gradients
+    assert _call_group(f, Xq, [_t(f, B0, E4M3, 64, 128, scale=S + 8196), _t(f, B1, E4M3, 64, 64)],
+                       Ws, ms, vs) == -1                                      # an FP8 dY without its scale
 
 
 @cpu_only
