@@ -85,6 +85,10 @@ enum { G_EPI_STORE = 0, G_EPI_OPT = 1, G_EPI_DX = 2 };
 #endif
 
 // issue priority of a ping-pong wave over its compute phase
+// ping-pong mainloop: read the next stage's first k-step during the compute phase
+#ifndef FORGE_PP_SPLIT
+#define FORGE_PP_SPLIT 1
+#endif
 #ifndef FORGE_PP_PRIO
 #define FORGE_PP_PRIO 1
 #endif
@@ -623,9 +627,57 @@ void gemm_kernel(GArgs g, OptArgs a, GroupArgs gr) {
     // for in M_{s-1}; the barrier that ends that phase publishes them before either
     // group reads stage s.
     const bool grp_b = wave_u >= C::NW / 2;
-    Frag F[C::KPW];
+    // Split reads: a group reads k-step 0 of stage i + 1 during C_i, between its MFMAs,
+    // so M_i reads only k-step 1 of stage i and the memory phase fits under the other
+    // group's MFMAs. Each wave then waits for its own loads of stage i + 2 at the end of
+    // C_i, so both groups' shares of stage i + 1 have landed by the barrier before either
+    // C_i (group A's C_i runs beside group B's M_i). A stage's buffer is refilled two
+    // phases after its last read. Not for the dynamic 8-bit code, whose epilogue leaves no
+    // registers for the third fragment set.
+    constexpr bool SPLIT = FORGE_PP_SPLIT && C::KPW == 2 && C::NSTAGE % 2 == 0 && C::NSTAGE >= 4 && !Q8D;
     __syncthreads();  // the previous tile's epilogue is done with LDS
     static_for<0, C::NSTAGE>([&](auto b_c) { dma(b_c, decltype(b_c)::value); });
+    if constexpr (SPLIT) {
+    Frag F0[2], F1;  // k-step 0 of this stage and of the next (alternating), k-step 1
+    vm_wait_barrier<(C::NSTAGE - 2) * LPS>();  // stages 0 and 1 published
+    static_for<0, NR>([&](auto r_c) {
+      read_one(F0[0], std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, r_c);
+    });
+    if (grp_b) wg_barrier();  // group B starts one phase later
+    auto pp_stage = [&](auto R_c, int i) {
+      constexpr int R = decltype(R_c)::value;  // i % NSTAGE
+      constexpr int cur = R % 2, nxt = 1 - cur;
+      // memory phase M_i: this wave's loads of stage i - 1 + NSTAGE (past the last stage
+      // too: the vmcnt waits count a fixed number of loads per phase), k-step 1 of stage i
+      if (i >= 1) dma(std::integral_constant<int, (R + C::NSTAGE - 1) % C::NSTAGE>{}, i - 1 + C::NSTAGE);
+      static_for<0, NR>([&](auto r_c) { read_one(F1, R_c, std::integral_constant<int, 1>{}, r_c); });
+      vm_wait_barrier<(C::NSTAGE - 2) * LPS>();  // fragments landed (the loads are waited in C)
+      // compute phase C_i, reading k-step 0 of stage i + 1 over the first MFMAs
+      settle(F0[cur]);
+      settle(F1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_prio<FORGE_PP_PRIO>();
+      mma_reading(F0[cur], F0[nxt], std::integral_constant<int, (R + 1) % C::NSTAGE>{},
+                  std::integral_constant<int, 0>{}, [] {});
+      static_for<0, C::FM * C::FN>([&](auto i_c) { mfma_one(F1, i_c); });
+      issue_prio<0>();
+      __builtin_amdgcn_sched_barrier(0);
+      // own loads of stage i + 2 landed (stage i + 3's may still be in flight)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"i"((C::NSTAGE - 3) * LPS) : "memory");
+      wg_barrier();
+    };
+    for (int i0 = 0; i0 < nst; i0 += C::NSTAGE)
+      static_for<0, C::NSTAGE>([&](auto r_c) {
+        const int i = i0 + decltype(r_c)::value;
+        if (i < nst) pp_stage(r_c, i);
+      });
+    // the last compute phase read k-step 0 of a stage past the end: those registers stay
+    // pinned until the reads have landed
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    settle(F0[0]);
+    settle(F0[1]);
+    } else {
+    Frag F[C::KPW];
     vm_wait_barrier<(C::NSTAGE - 1) * LPS>();  // stage 0 published
     if (grp_b) wg_barrier();                     // group B starts one phase later
     auto pp_stage = [&](auto R_c, int i) {
@@ -656,6 +708,7 @@ void gemm_kernel(GArgs g, OptArgs a, GroupArgs gr) {
         const int i = i0 + decltype(r_c)::value;
         if (i < nst) pp_stage(r_c, i);
       });
+    }
     if (!grp_b) wg_barrier();  // both groups pass the same number of barriers
     // the loads of the stages past the last one still write LDS: let them land
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
