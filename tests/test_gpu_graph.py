@@ -122,3 +122,42 @@ def test_captured_noalloc_baseline_replays_equal_eager():
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"replay {r}: {name} differs"
     assert torch.cuda.memory_allocated() == base
     del g
+
+
+def test_captured_grouped_step_replays_equal_eager():
+    """The grouped fused step (three layers on one X) captured once and replayed, against
+    the same call made eagerly, bit for bit after each replay."""
+    f = _forge()
+    specs = [LayerSpec("gq", 512, 768, 256), LayerSpec("gk", 128, 768, 256), LayerSpec("gv", 128, 768, 256)]
+    opt, t = "adamw", 4
+    hp = _gh(optim.hyper(opt))
+    X, _ = draw_layer_batch(152, 0, 1, specs[0])
+    Xd = P.dev_bf16(X)
+    dYs = [P.dev_bf16(draw_layer_batch(152, k, 1, s)[1]) for k, s in enumerate(specs)]
+    W0 = [draw_layer_init(152, k, s) for k, s in enumerate(specs)]
+    seeds = [0xBEEF ^ k for k in range(len(specs))]
+
+    def step(st):
+        f.wgrad_step_group(Xd, dYs, [s[0] for s in st], [s[1] for s in st], [s[2] for s in st], opt, hp, t, seeds)
+
+    eager = [_state(f, w, opt, "f32") for w in W0]
+    ref = []
+    for _ in range(REPLAYS):
+        step(eager)
+        torch.cuda.synchronize()
+        ref.append([_snap(st[:3]) for st in eager])
+    cap = [_state(f, w, opt, "f32") for w in W0]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(cap)
+    torch.cuda.synchronize()
+    print("[case] graph of one grouped launch over 3 layers", flush=True)
+    for r in range(REPLAYS):
+        g.replay()
+        torch.cuda.synchronize()
+        for k, st in enumerate(cap):
+            for name, a, b in zip(("W", "m", "v"), _snap(st[:3]), ref[r][k]):
+                assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"replay {r}, layer {k}: {name} differs"
+        print(f"[ok] replay {r}", flush=True)
+    del g
