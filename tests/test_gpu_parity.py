@@ -185,6 +185,31 @@ def test_each_tile_configuration_dgrad(cfg):
     assert bad == 0, f"{bad} dX elements beyond one bf16 ulp (worst {worst:.3g})"
 
 
+@pytest.mark.parametrize("T", [0, 17, 40])
+def test_large_tiles_few_token_stages(T):
+    # the 256x256 tiles' mainloop with 0, 1 and 2 stages of 32 tokens: the ring's prologue,
+    # the reads ahead into stages past the last one and the closing waits
+    n_in, n_out = _shape("big")
+    rows = np.unique(np.concatenate([np.arange(0, n_out, max(1, n_out // 64)), [n_out - 1]]))
+    run_case(LayerSpec("c", n_out, n_in, T), "adamw", 2, config=89, rows=rows, label=f"256x256 tiles, T={T}")
+
+
+@pytest.mark.parametrize("n_out", [16, 40])
+def test_large_tiles_dgrad_few_stages(n_out):
+    # dgrad on 256x256 tiles whose reduction (out) spans one or two 32-row stages
+    f = _forge()
+    n_in, T = _shape("big")
+    spec = LayerSpec("d", n_out, n_in, T)
+    print(f"[case] dgrad 256x256 tiles: T={T} out={n_out} in={n_in}", flush=True)
+    W = draw_layer_init(86, 0, spec)
+    X, dY = draw_layer_batch(86, 0, 1, spec)
+    dX = f.dgrad(P.dev_bf16(dY), P.dev_bf16(W))
+    torch.cuda.synchronize()
+    ref = gemm.dgrad(f32_from_bf16_bits(dY), f32_from_bf16_bits(W))
+    bad, worst = P.dgrad_bf16_ok(P.host_bits(dX), ref)
+    assert bad == 0, f"{bad} dX elements beyond one bf16 ulp (worst {worst:.3g})"
+
+
 # ---------------------------------------------------------------- dgrad
 @pytest.mark.parametrize("shape,io", [((130, 200, 328), "bf16"), ((512, 384, 256), "bf16"),
                                       ((512, 256, 256), "f32"), ((70, 72, 100), "f32")])
