@@ -128,6 +128,82 @@ class ForgeLinear(torch.nn.Module):
         self.grad32 = None
 
 
+class _ForgeGroupFn(torch.autograd.Function):
+    """Several ForgeLinear layers applied to the same input: forward Y_l = X W_l^T for each;
+    backward dX = sum_l dY_l W_l (each on the old W_l) and then one grouped fused step of
+    all the layers (forge_linear_wgrad_step_group), where the layers' tiles share the
+    launch."""
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, layers, *weights: torch.Tensor):
+        ctx.layers = layers
+        ctx.save_for_backward(x)
+        return tuple(torch.matmul(x, w.t()) for w in weights)
+
+    @staticmethod
+    def backward(ctx, *dys):
+        (x,) = ctx.saved_tensors
+        layers = ctx.layers
+        ws = [L.weight.detach() for L in layers]
+        x2 = x.reshape(-1, ws[0].shape[1])
+        if not x2.is_contiguous():
+            x2 = x2.contiguous()
+        dy2s = []
+        for w, dy in zip(ws, dys):
+            if dy is None:  # an output that reached no loss: a zero gradient, the layer still steps
+                dy2s.append(torch.zeros((x2.shape[0], w.shape[0]), dtype=w.dtype, device=w.device))
+                continue
+            dy2 = dy.reshape(-1, w.shape[0])
+            dy2s.append(dy2 if dy2.is_contiguous() and dy2.dtype == w.dtype else dy2.to(w.dtype).contiguous())
+        dx = None
+        if ctx.needs_input_grad[0]:
+            dx = forge.dgrad(dy2s[0], ws[0])  # old W, before the update below
+            for w, dy2 in zip(ws[1:], dy2s[1:]):
+                dx.add_(forge.dgrad(dy2, w))
+            dx = dx.reshape(x.shape)
+        L0 = layers[0]
+        if not L0.fused:
+            for L, dy2 in zip(layers, dy2s):
+                g = forge.wgrad(x2, dy2)
+                if L.grad32 is None:
+                    L.grad32 = g
+                else:
+                    L.grad32.add_(g)
+            return (dx, None) + (None,) * len(layers)
+        for L in layers:
+            L._step_count += 1
+        ev = L0.timing
+        if ev is not None:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        forge.wgrad_step_group(x2, dy2s, ws, [L.m for L in layers], [L.v for L in layers], L0.opt, L0.hyper,
+                               L0._step_count, [L.seed for L in layers], [L.m_scale for L in layers],
+                               [L.v_scale for L in layers], code=L0.code)
+        if ev is not None:
+            e1.record()
+            ev.append((e0, e1))
+        return (dx, None) + (None,) * len(layers)
+
+
+def grouped_linear(layers, x: torch.Tensor):
+    """Y_l = X W_l^T for ForgeLinear layers that read the same input x, as one autograd node
+    whose backward steps all of them in one grouped launch (the layers' outputs as a tuple).
+    The layers must agree in optimizer, hyper-parameters, moment format, schedule and step
+    count; the group's time is recorded on the first layer's `timing` list."""
+    layers = list(layers)
+    L0 = layers[0]
+    if not 1 <= len(layers) <= forge.MAX_GROUP:
+        raise ValueError(f"a group holds 1..{forge.MAX_GROUP} layers")
+    for L in layers[1:]:
+        if (L.opt, L.code, L.fused, L._step_count, L.weight.dtype) != (L0.opt, L0.code, L0.fused, L0._step_count,
+                                                                         L0.weight.dtype) or \
+                (L.m is None) != (L0.m is None) or (L.v is None) != (L0.v is None) or \
+                (L.m is not None and L.m.dtype != L0.m.dtype) or \
+                any(getattr(L.hyper, n) != getattr(L0.hyper, n) for n, _ in L0.hyper._fields_):
+            raise ValueError("grouped layers must share optimizer, hyper-parameters, states, schedule and step")
+    return _ForgeGroupFn.apply(x, layers, *[L.weight for L in layers])
+
+
 def step_all(model: torch.nn.Module) -> None:
     """The optimizer phase of the two-phase schedule for every ForgeLinear in `model`."""
     for mod in model.modules():
@@ -146,18 +222,24 @@ class SwiGLUBlock(torch.nn.Module):
     gate / up: [hidden, d] weights, down: [d, hidden]. With checkpoint=True the block
     keeps only its input for backward and recomputes the rest (activation
     checkpointing); the recomputation runs before any of the block's layers steps,
-    so it sees the same weights as the forward pass."""
+    so it sees the same weights as the forward pass. With grouped=True gate and up, which
+    read the same n(x), take their fused steps in one grouped launch."""
 
-    def __init__(self, d: int, hidden: int, checkpoint: bool = False, seed: int = 0, **kw):
+    def __init__(self, d: int, hidden: int, checkpoint: bool = False, seed: int = 0, grouped: bool = False, **kw):
         super().__init__()
         self.gate = ForgeLinear(d, hidden, seed=3 * seed, **kw)
         self.up = ForgeLinear(d, hidden, seed=3 * seed + 1, **kw)
         self.down = ForgeLinear(hidden, d, seed=3 * seed + 2, **kw)
         self.checkpoint = checkpoint
+        self.grouped = grouped
 
     def _body(self, x: torch.Tensor) -> torch.Tensor:
         h = _rms_norm(x)
-        return x + self.down(torch.nn.functional.silu(self.gate(h)) * self.up(h))
+        if self.grouped:
+            g, u = grouped_linear((self.gate, self.up), h)
+        else:
+            g, u = self.gate(h), self.up(h)
+        return x + self.down(torch.nn.functional.silu(g) * u)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         if self.checkpoint and torch.is_grad_enabled():

@@ -156,6 +156,35 @@ def test_checkpointed_block_equals_plain_block():
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("ckpt", [False, True])
+def test_grouped_gate_up_equals_separate_layers(ckpt):
+    # gate and up (same input) as one grouped launch: dX is the sum of the two dgrads on
+    # the old weights, as autograd sums the separate layers' contributions, and on these
+    # shapes the grouped and the single-layer launchers pick the same 64x128 tiles, so
+    # weights, moments and input gradients equal the ungrouped block's bit for bit
+    from optimizer_gemm_amd.nn import SwiGLUBlock
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(9)
+    T, d, hidden = 256, 256, 512
+    print(f"[case] SwiGLU blocks, gate/up grouped vs separate, checkpoint={ckpt}", flush=True)
+    x = torch.randn(T, d, device=dev, generator=g).to(torch.bfloat16)
+    G = (torch.randn(T, d, device=dev, generator=g) * 1e-3).to(torch.bfloat16)
+    runs = []
+    for grouped in (False, True):
+        torch.manual_seed(21)
+        model = torch.nn.Sequential(*[SwiGLUBlock(d, hidden, checkpoint=ckpt, seed=b, grouped=grouped, device=dev)
+                                      for b in range(2)])
+        grads = _train(model, x, G, 3, True)
+        runs.append((_lin_state(model), grads, [m.step_count for m in model.modules() if hasattr(m, "step_count")]))
+    (s0, g0, c0), (s1, g1, c1) = runs
+    assert c0 == c1 == [3] * len(c0)
+    for (w0, m0, v0), (w1, m1, v1) in zip(s0, s1):
+        assert torch.equal(w0.view(torch.int16), w1.view(torch.int16))
+        assert torch.equal(m0, m1) and torch.equal(v0, v1)
+    for a, b in zip(g0, g1):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 def test_two_phase_schedule_matches_fused():
     # the two-phase schedule (float32 dW stored in backward, optimizer pass afterwards)
     # and the fused one apply the same update: at step 1 bit for bit up to the SR flips the
