@@ -66,9 +66,10 @@ enum { G_EPI_STORE = 0, G_EPI_OPT = 1, G_EPI_DX = 2 };
 
 
 // 4-element vectors whose W / m / v loads the optimizer epilogue issues before consuming
-// any of them (KB1: configurations with one wave per SIMD, whose accumulators sit in
-// AGPRs and leave room for a deeper batch; with half the waves of the others they need
-// more loads in flight per wave), and whether the compiler may move work across batches
+// any of them (KB1: configurations with one wave per SIMD, none of the default ones, whose
+// accumulators sit in AGPRs and leave room for a deeper batch; with half the waves of the
+// others they need more loads in flight per wave), and whether the compiler may move work
+// across batches
 #ifndef FORGE_EPI_KB
 #define FORGE_EPI_KB 2
 #endif
@@ -144,8 +145,8 @@ struct GCfg {
   static_assert(NT % A_CPR == 0 && NT % B_CPR == 0, "a thread's chunks share a column");
   static_assert(TM % 32 == 0 && TN % 32 == 0 && BK % KSTEP == 0 && KSTEPS % KS == 0 && KPW >= 1, "tile shape");
   static_assert(F8 || PP || KPW % 2 == 0, "bf16 stages hold an even number of k-steps per wave");
-  static_assert(!PP || (KS == 1 && WM * WN == 8 && OCC == 2 && !F8 && NSTAGE >= 3),
-                "ping-pong: 8 waves (two per SIMD), no k-split, bf16, a ring of three or more stages");
+  static_assert(!PP || (KS == 1 && WM * WN == 8 && OCC == 2 && NSTAGE >= 3),
+                "ping-pong: 8 waves (two per SIMD), no k-split, a ring of three or more stages");
   // Chunk swizzles (XOR of the 16-byte chunk index of a row):
   //  * rows read with the 16-bit transpose read: 4 * (row % 4), so the four rows one read
   //    touches land in four different 64-byte bank groups (16 or more chunks per row);
@@ -1102,16 +1103,20 @@ void gemm_kernel(GArgs g, OptArgs a, GroupArgs gr) {
 #define FORGE_DGRAD_SPLIT_CFG 128, 128, 64, 2, 2, false, 2, 4, 2
 #endif
 // FP8 operands (X in E4M3, dY in format FB): 64-token stages, one MFMA k-step each. The
-// large tile runs 4 waves of 128x128 (one per SIMD, 512 registers each): two sets of
-// 8-register FP8 fragments would not fit next to 128 accumulators at two waves per SIMD.
+// large tile runs 8 waves of 128x64 (two per SIMD) with the ping-pong mainloop: one
+// fragment set of a k-step per group fits next to the 128 accumulators, and the
+// epilogue has twice the waves of a one-wave-per-SIMD layout.
 #ifndef FORGE_WGRAD_F8_BIG_CFG
-#define FORGE_WGRAD_F8_BIG_CFG 256, 256, 64, 2, 2, true, 1, 4, 1
+#define FORGE_WGRAD_F8_BIG_CFG 256, 256, 64, 2, 4, true, 2, 4, 1
 #endif
 #ifndef FORGE_WGRAD_F8_SMALL_CFG
 #define FORGE_WGRAD_F8_SMALL_CFG 128, 128, 64, 2, 2, true, 2, 4, 1
 #endif
 template <int FB>
-using WgradF8Big = GCfg<FORGE_WGRAD_F8_BIG_CFG, G_FP8, 0, FB>;
+#ifndef FORGE_F8_BIG_PP
+#define FORGE_F8_BIG_PP 1
+#endif
+using WgradF8Big = GCfg<FORGE_WGRAD_F8_BIG_CFG, G_FP8, 0, FB, FORGE_F8_BIG_PP>;
 template <int FB>
 using WgradF8Small = GCfg<FORGE_WGRAD_F8_SMALL_CFG, G_FP8, 0, FB>;
 using WgradBig = GCfg<FORGE_WGRAD_BIG_CFG>;
