@@ -173,3 +173,38 @@ def test_group_fp8_of_one_equals_single_layer_call():
         outs.append([P.host(x).copy() for x in (W, m, v)])
     for a, b in zip(*outs):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_group_members_with_row_pitch():
+    # members whose dY, W and moments are views into wider buffers (row pitch > columns):
+    # each member's pitches travel in its own table entry
+    f = _forge()
+    hp = optim.hyper("adamw")
+    outs, inn, T, cfg = (256, 136), 512, 200, 173
+    specs = [LayerSpec(f"p{k}", out, inn, T) for k, out in enumerate(outs)]
+    seeds = [0x7100 ^ k for k in range(2)]
+    X, _ = draw_layer_batch(cfg, 0, 1, specs[0])
+    dYs = [draw_layer_batch(cfg, k, 1, s)[1] for k, s in enumerate(specs)]
+    W0 = [draw_layer_init(cfg, k, s) for k, s in enumerate(specs)]
+    pad = (64, 128)
+
+    def pitched(a, p, dtype):
+        base = torch.zeros((a.shape[0], a.shape[1] + p), dtype=dtype, device="cuda")
+        v = base[:, :a.shape[1]]
+        v.copy_(a)
+        return v
+
+    dY_d = [pitched(P.dev_bf16(d), p, torch.bfloat16) for d, p in zip(dYs, pad)]
+    Ws = [pitched(P.dev_bf16(w), p, torch.bfloat16) for w, p in zip(W0, pad)]
+    ms = [pitched(torch.zeros(w.shape, device="cuda"), p, torch.float32) for w, p in zip(W0, pad)]
+    vs = [pitched(torch.zeros(w.shape, device="cuda"), p, torch.float32) for w, p in zip(W0, pad)]
+    assert all(w.stride(0) != w.shape[1] for w in Ws)
+    print("[case] group of 2 with pitched dY, W, m, v", flush=True)
+    rows = [np.arange(s.out) for s in specs]
+    before = [P.snapshot((W, m, v, None, None), r) for W, m, v, r in zip(Ws, ms, vs, rows)]
+    f.wgrad_step_group(P.dev_bf16(X), dY_d, Ws, ms, vs, "adamw", _gh(hp), 1, seeds)
+    torch.cuda.synchronize()
+    for k in range(2):
+        after = P.snapshot((Ws[k], ms[k], vs[k], None, None), rows[k])
+        P.verify_step("adamw", X, dYs[k], before[k], after, hp, 1, seeds[k], "bf16", "f32", True, rows[k])
+    print("[ok] both members", flush=True)
