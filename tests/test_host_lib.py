@@ -520,3 +520,25 @@ def test_empty_layer_needs_no_pointers(f):
     # a layer with weights still needs its moments
     assert _call_step(f, X, _t(f, 0x20000000, BF16, 64, 128), _t(f, 0x30000000, BF16, 128, 256),
                       _t(f, None, F32, 128, 256), v) == -1
+
+
+def test_grouped_linear_rejects_layers_that_cannot_share_a_launch(f):
+    # the check runs on the host before any kernel: layers of a group must agree in
+    # optimizer, hyper-parameters, moment format, schedule and step count
+    import torch
+
+    from optimizer_gemm_amd.nn import ForgeLinear, grouped_linear
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    a = ForgeLinear(64, 32, device="cpu", seed=1)
+    for other in (ForgeLinear(64, 32, device="cpu", seed=2, opt="lion"),
+                  ForgeLinear(64, 16, device="cpu", seed=3, hyper={"lr": 5e-4}),
+                  ForgeLinear(64, 16, device="cpu", seed=4, states="bf16"),
+                  ForgeLinear(64, 16, device="cpu", seed=5, fused=False)):
+        with pytest.raises(ValueError):
+            grouped_linear([a, other], x)
+    b = ForgeLinear(64, 16, device="cpu", seed=6)
+    b._step_count = 1
+    with pytest.raises(ValueError):
+        grouped_linear([a, b], x)
+    with pytest.raises(ValueError):
+        grouped_linear([a] * (f.MAX_GROUP + 1), x)
