@@ -193,6 +193,10 @@ int forge_linear_wgrad_step(const forge_tensor* X, const forge_tensor* dY, forge
  * forge_linear_wgrad_step applies to each layer; in addition no layer's W, m, v or block
  * scales may overlap any other layer's tensors (FORGE_ERR_ALIAS). Nothing is enqueued
  * on an error. Must be enqueued after each layer's forge_linear_dgrad.
+ * The operation is the pages' fused step (§2 Method, "Core mechanism") for each layer; sharing one
+ * launch is this library's arrangement, not part of the method. The descriptor arrays
+ * and seeds are host memory read during the call; the tensors' data is caller-owned
+ * device memory, as for forge_linear_wgrad_step.
  */
 #define FORGE_MAX_GROUP 4
 int forge_linear_wgrad_step_group(const forge_tensor* X, int32_t n_layers, const forge_tensor* dY,
